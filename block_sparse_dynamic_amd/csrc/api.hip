@@ -1,0 +1,143 @@
+// C ABI of libdma.so: argument validation and dispatch to the gfx950 kernels.
+// Declarations, layouts and error behaviour are documented in include/dma.h.
+#include "../../include/dma.h"
+
+#include "common.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_or_null(const void* p) { return p == nullptr || aligned16(p); }
+
+// Element counts must stay below 2^62 so that every offset fits in int64.
+bool sizes_ok(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv) {
+  if (b < 1 || lq < 1 || lk < 1 || hq < 1 || hkv < 1) return false;
+  const double plane = (double)b * (double)hkv * (double)lq * (double)lk;
+  return plane < 4.0e18;
+}
+
+int check_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
+               const uint8_t* state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+               int is_causal) {
+  if (!q || !k || !v || !state) return DMA_ERR_INVALID_ARGUMENT;
+  if (!sizes_ok(b, lq, lk, hq, hkv) || d < 1) return DMA_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return DMA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned_or_null(mask) || !aligned_or_null(bias))
+    return DMA_ERR_INVALID_ARGUMENT;
+  if ((mask || bias) && lk % 8 != 0) return DMA_ERR_INVALID_ARGUMENT;
+  if (hq % hkv != 0) return DMA_ERR_INVALID_ARGUMENT;
+  const int64_t G = hq / hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return DMA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return DMA_ERR_UNSUPPORTED;
+  const int64_t nqb = (lq + 63) / 64, nkb = (lk + 63) / 64;
+  if (b * hkv * nqb * (G >= 4 ? G / 4 : 1) > 0x7FFFFFFF || b * hkv * nkb > 0x7FFFFFFF) return DMA_ERR_UNSUPPORTED;
+  return DMA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DMA_OK : DMA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int dma_block_size(void) { return dma::kBlock; }
+
+const char* dma_status_string(int status) {
+  switch (status) {
+    case DMA_OK:
+      return "ok";
+    case DMA_ERR_INVALID_ARGUMENT:
+      return "invalid argument";
+    case DMA_ERR_UNSUPPORTED:
+      return "unsupported configuration (d must be 64 or 128, hq/hkv in {1,2,4,8,16})";
+    case DMA_ERR_WORKSPACE_TOO_SMALL:
+      return "workspace too small";
+    case DMA_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int is_causal,
+                       uint8_t* block_state, void* stream) {
+  if (!block_state || !sizes_ok(b, lq, lk, 1, hkv)) return DMA_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return DMA_ERR_INVALID_ARGUMENT;
+  if (mask && (lk % 8 != 0 || !aligned16(mask))) return DMA_ERR_INVALID_ARGUMENT;
+  if (b * hkv > 65535 || (lq + 63) / 64 > 65535) return DMA_ERR_UNSUPPORTED;
+  return hip_status(dma::launch_classify(mask, b, hkv, lq, lk, is_causal, block_state, (hipStream_t)stream));
+}
+
+int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
+                 const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                 float scale, int is_causal, uint16_t* o, float* lse, void* stream) {
+  int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
+  if (st != DMA_OK) return st;
+  if (!o || !lse || !aligned16(o) || !aligned16(lse)) return DMA_ERR_INVALID_ARGUMENT;
+  dma::AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.mask = mask;
+  a.bias = bias;
+  a.state = block_state;
+  a.o_out = o;
+  a.lse_out = lse;
+  a.b = b;
+  a.lq = lq;
+  a.lk = lk;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.scale = scale;
+  a.causal = is_causal;
+  return hip_status(dma::launch_fwd(a, (hipStream_t)stream));
+}
+
+size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t hq, int64_t d) {
+  if (b < 1 || lq < 1 || hq < 1 || d < 1) return 0;
+  const size_t acc = (size_t)b * (size_t)lq * (size_t)hq * (size_t)d * sizeof(float);
+  const size_t rows = (size_t)b * (size_t)hq * (size_t)lq * sizeof(float);
+  return acc + ((rows + 255) / 256) * 256;
+}
+
+int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
+                 const uint8_t* block_state, const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b,
+                 int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq,
+                 uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
+  if (st != DMA_OK) return st;
+  if (!o || !dout || !lse || !dq || !dk || !dv || !workspace) return DMA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned_or_null(dbias) || !aligned16(workspace))
+    return DMA_ERR_INVALID_ARGUMENT;
+  if (dbias && lk % 8 != 0) return DMA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < dma_attn_bwd_workspace_size(b, lq, hq, d)) return DMA_ERR_WORKSPACE_TOO_SMALL;
+  dma::AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.mask = mask;
+  a.bias = bias;
+  a.state = block_state;
+  a.o = o;
+  a.dout = dout;
+  a.lse_in = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dbias = dbias;
+  a.dq_acc = static_cast<float*>(workspace);
+  a.drow = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)b * lq * hq * d * sizeof(float));
+  a.b = b;
+  a.lq = lq;
+  a.lk = lk;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.scale = scale;
+  a.causal = is_causal;
+  return hip_status(dma::launch_bwd(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Device-side helpers shared by the gfx950 kernels of libdma.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dma {
+
+constexpr int kBlock = 64;  // classification block: 64 query rows x 64 key columns
+constexpr uint8_t kSkip = 0, kPartial = 1, kFull = 2;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ bool attends_lo(uint32_t w) { return (w & 0x7FFFu) != 0; }
+__device__ __forceinline__ bool attends_hi(uint32_t w) { return (w & 0x7FFF0000u) != 0; }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// x of the partner lane l ^ 32 combined with x by max / sum (v_permlane32_swap).
+__device__ __forceinline__ float max_with_half_swap(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_half_swap(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive 16-bit elements in[s][0..3];
+// lane j receives out[j][e] = in[4e + j/4][j%4].  With lane s pointing at row
+// r0 + s/4, columns c0 + 4(s%4) .. +3 of a row-major tile, lane j gets rows
+// r0 .. r0+3 of column c0 + j: a column read of 4 elements.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, const_cast<void*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(i16x4 a, i16x4 b) {
+  bf16x8 r;
+  u32x4 u;
+  u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  u[0] = ua[0];
+  u[1] = ua[1];
+  u[2] = ub[0];
+  u[3] = ub[1];
+  r = __builtin_bit_cast(bf16x8, u);
+  return r;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace dma
+
+// Host-side launchers (one per kernel file).
+namespace dma {
+hipError_t launch_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int causal,
+                           uint8_t* state, hipStream_t stream);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* mask;
+  const uint16_t* bias;
+  const uint8_t* state;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse_in;
+  uint16_t* o_out;
+  float* lse_out;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  uint16_t* dbias;
+  float* dq_acc;  // fp32 [b, lq, hq, d]
+  float* drow;    // fp32 [b, hq, lq]: rowsum(dO * O)
+  int64_t b, lq, lk, hq, hkv, d;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
+}  // namespace dma

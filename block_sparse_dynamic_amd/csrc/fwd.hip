@@ -1,0 +1,292 @@
+// Forward kernel of dynamic-mask attention for gfx950.
+//
+// Computes O = softmax(scale * Q K^T + B, invalid positions -> -inf) V and the
+// row log-sum-exp (Flash-DMA issue "Project Progress"; FlashMask README,
+// Formulation), visiting only the key blocks the classification marked
+// non-SKIP (Flash-DMA README, key design: K/V are loaded only for blocks whose
+// mask OR-reduces to true).
+//
+// Work decomposition.  One workgroup owns one (batch, kv head g, 64-row query
+// block, chunk of HC query heads of g's group).  All HC heads read one staged
+// copy of the block's K, V, mask and bias, so the dense mask/bias planes are
+// streamed from HBM once per group instead of once per query head.  Each
+// wavefront owns 32 query rows of one head.
+//
+// Per key block (64 keys):
+//   1. the workgroup copies K and V (row-major, [key][d]) and the *effective*
+//      bias into LDS.  The effective bias is bias where the position is valid
+//      and -inf elsewhere: mask, causality and the ragged matrix edge are
+//      folded in once here (PARTIAL blocks only), so the score epilogue is one
+//      fma per element for every head.  FULL blocks copy the bias alone.
+//   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
+//      wave's Q rows held in registers for the whole kernel.  The result's
+//      lane l holds query l%32 and 16 keys of each 32-key half, so a row's
+//      64 scores live in lanes l and l^32.
+//   3. online softmax in fp32: row max over the lane pair (v_permlane32_swap),
+//      exp2 with log2(e) folded in, a lazy rescale of the running output that
+//      only fires when a row maximum grows by more than 8 nats.
+//   4. O^T += V^T P^T: P^T goes from the accumulator registers straight into
+//      the B operand (the key order inside a k-step only has to agree between
+//      A and B); V^T comes out of the row-major V tile by ds_read_b64_tr_b16.
+#include <math.h>
+
+#include "common.h"
+
+namespace dma {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* mask;
+  const uint16_t* bias;
+  const uint8_t* state;
+  uint16_t* o;
+  float* lse;
+  int64_t lq, lk, hq, hkv;
+  int G, chunks, nqb, nkb, total_wg;
+  float scale;
+  int causal;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleNats = 8.0f;
+constexpr uint16_t kBf16NegInf = 0xFF80u;
+
+template <int D>
+struct FwdSmem {
+  static constexpr int kRow = D + 8;  // padded row (elements) of the K and V tiles
+  static constexpr int kBRow = kBlock + 8;
+  uint16_t k[kBlock * kRow];
+  uint16_t v[kBlock * kRow];
+  uint16_t b[kBlock * kBRow];  // effective bias, bf16 bits
+};
+
+template <int D, int HC>
+__global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
+  constexpr int NT = HC * 128;
+  constexpr int KR = FwdSmem<D>::kRow, BR = FwdSmem<D>::kBRow;
+  __shared__ FwdSmem<D> sm;
+
+  // XCD-aware order: workgroup w runs on XCD w % 8; give each XCD a contiguous
+  // range of (unit, query block) so the units of one (b, g) share an L2, and run
+  // query blocks from the last (longest under causality) to the first.
+  const int w = blockIdx.x;
+  const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
+  const int unit = t / p.nqb;
+  const int qb = p.nqb - 1 - (t % p.nqb);
+  const int plane = unit / p.chunks, chunk = unit % p.chunks;
+  const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int head = (int)g * p.G + chunk * HC + (wave >> 1);
+  const int rloc = (wave & 1) * 32 + (lane & 31);  // query row inside the block
+  const int64_t row = (int64_t)qb * kBlock + rloc;
+  const int64_t shift = p.lk - p.lq;
+  const int hi = lane >> 5;  // which half of the key quartets this lane holds
+
+  // Q rows in registers: B operand of S^T = K Q^T, d = s*16 + hi*8 .. +7.
+  bf16x8 qreg[D / 16];
+  {
+    const uint16_t* qp = p.q + ((bidx * p.lq + row) * p.hq + head) * D + hi * 8;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 w4 = {0u, 0u, 0u, 0u};
+      if (row < p.lq) w4 = *reinterpret_cast<const u32x4*>(qp + s * 16);
+      qreg[s] = __builtin_bit_cast(bf16x8, w4);
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+  float m_ref = -INFINITY, l_part = 0.f;
+
+  const uint8_t* st_row = p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
+  const uint16_t* kbase = p.k + (bidx * p.lk * p.hkv + g) * D;
+  const uint16_t* vbase = p.v + (bidx * p.lk * p.hkv + g) * D;
+  const int64_t plane_off = (int64_t)plane * p.lq * p.lk;
+  const bool has_bias = p.bias != nullptr, has_mask = p.mask != nullptr;
+
+  for (int kb = 0; kb < p.nkb; ++kb) {
+    const uint8_t st = st_row[kb];
+    if (st == kSkip) continue;
+    const bool full = (st == kFull);
+    __syncthreads();  // the previous block's LDS reads are done
+    // ---- stage K, V (row-major) and the effective bias -------------------
+    for (int task = tid; task < kBlock * (D / 8); task += NT) {
+      const int r = task / (D / 8), c = task % (D / 8);
+      const int64_t key = (int64_t)kb * kBlock + r;
+      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+      if (key < p.lk) {
+        kw = *reinterpret_cast<const u32x4*>(kbase + key * p.hkv * D + c * 8);
+        vw = *reinterpret_cast<const u32x4*>(vbase + key * p.hkv * D + c * 8);
+      }
+      *reinterpret_cast<u32x4*>(&sm.k[r * KR + c * 8]) = kw;
+      *reinterpret_cast<u32x4*>(&sm.v[r * KR + c * 8]) = vw;
+    }
+    if (has_bias || !full) {
+      for (int task = tid; task < kBlock * 8; task += NT) {
+        const int r = task >> 3, c = task & 7;
+        const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
+        u32x4 bw = {0u, 0u, 0u, 0u};
+        const bool inside = i < p.lq && j0 < p.lk;
+        if (has_bias && inside) bw = *reinterpret_cast<const u32x4*>(p.bias + plane_off + i * p.lk + j0);
+        if (!full) {
+          u32x4 mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+          if (has_mask && inside) mw = *reinterpret_cast<const u32x4*>(p.mask + plane_off + i * p.lk + j0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t j = j0 + 2 * e;
+            const bool v0 = inside && attends_lo(mw[e]) && (!p.causal || j <= i + shift);
+            const bool v1 = inside && attends_hi(mw[e]) && (!p.causal || j + 1 <= i + shift);
+            const uint32_t lo = v0 ? (bw[e] & 0xFFFFu) : kBf16NegInf;
+            const uint32_t hi16 = v1 ? (bw[e] >> 16) : kBf16NegInf;
+            bw[e] = lo | (hi16 << 16);
+          }
+        }
+        *reinterpret_cast<u32x4*>(&sm.b[r * BR + c * 8]) = bw;
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T --------------------------------------------------------
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[(kt * 32 + (lane & 31)) * KR + s * 16 + hi * 8]);
+        sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
+      }
+    }
+    // ---- scores: x = scale * s + effective bias ---------------------------
+    float mx = -INFINITY;
+    if (has_bias || !full) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const u32x2 bw = *reinterpret_cast<const u32x2*>(&sm.b[rloc * BR + kt * 32 + gi * 8 + hi * 4]);
+          const float bb[4] = {bf16_lo(bw[0]), bf16_hi(bw[0]), bf16_lo(bw[1]), bf16_hi(bw[1])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = fmaf(sacc[kt][gi * 4 + e], p.scale, bb[e]);
+            sacc[kt][gi * 4 + e] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = sacc[kt][i] * p.scale;
+          sacc[kt][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+    }
+    mx = max_with_half_swap(mx);
+    // ---- online softmax with lazy rescaling ---------------------------------
+    if (__any(mx > m_ref + kRescaleNats)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_ref - m_new) * kLog2e);
+      m_ref = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * kLog2e;
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], kLog2e, -mb));
+        sacc[kt][i] = pv;
+        rs += pv;
+      }
+    l_part += rs;
+    // ---- O^T += V^T P^T -------------------------------------------------------
+    const int trow = (lane & 15) >> 2;                           // row offset inside a 4-row tr group
+    const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;    // column inside a 32-wide tile
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 pw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(sacc[kt][hh * 8 + 2 * e], sacc[kt][hh * 8 + 2 * e + 1]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        const int key0 = kt * 32 + hh * 16 + hi * 4 + trow;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const i16x4 a0 = lds_read_tr16(&sm.v[key0 * KR + dt * 32 + tcol]);
+          const i16x4 a1 = lds_read_tr16(&sm.v[(key0 + 8) * KR + dt * 32 + tcol]);
+          oacc[dt] = mfma32(join_bf16x8(a0, a1), pb, oacc[dt]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue -----------------------------------------------------------------
+  const float l_tot = sum_with_half_swap(l_part);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row < p.lq) {
+    uint16_t* op = p.o + ((bidx * p.lq + row) * p.hq + head) * D + hi * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2 w2;
+        w2[0] = pack_bf16x2(oacc[dt][gi * 4 + 0] * inv, oacc[dt][gi * 4 + 1] * inv);
+        w2[1] = pack_bf16x2(oacc[dt][gi * 4 + 2] * inv, oacc[dt][gi * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + dt * 32 + gi * 8) = w2;
+      }
+    if (hi == 0) p.lse[(bidx * p.hq + head) * p.lq + row] = l_tot > 0.f ? m_ref + logf(l_tot) : INFINITY;
+  }
+}
+
+template <int D, int HC>
+static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_kernel<D, HC>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
+  FwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.mask = a.mask;
+  p.bias = a.bias;
+  p.state = a.state;
+  p.o = a.o_out;
+  p.lse = a.lse_out;
+  p.lq = a.lq;
+  p.lk = a.lk;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.G = (int)(a.hq / a.hkv);
+  const int HC = p.G >= 4 ? 4 : p.G;
+  p.chunks = p.G / HC;
+  p.nqb = (int)((a.lq + kBlock - 1) / kBlock);
+  p.nkb = (int)((a.lk + kBlock - 1) / kBlock);
+  p.total_wg = (int)(a.b * a.hkv * p.chunks * p.nqb);
+  p.scale = a.scale;
+  p.causal = a.causal;
+  if (a.d == 64) {
+    if (HC == 1) return launch_fwd_t<64, 1>(p, stream);
+    if (HC == 2) return launch_fwd_t<64, 2>(p, stream);
+    return launch_fwd_t<64, 4>(p, stream);
+  }
+  if (HC == 1) return launch_fwd_t<128, 1>(p, stream);
+  if (HC == 2) return launch_fwd_t<128, 2>(p, stream);
+  return launch_fwd_t<128, 4>(p, stream);
+}
+
+}  // namespace dma

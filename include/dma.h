@@ -1,0 +1,139 @@
+/*
+ * dma.h -- C ABI of the dynamic-mask attention library (libdma.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (Flash-DMA README, features and usage example; Flash-DMA issue
+ * "Project Progress"; FlashMask README, Formulation):
+ *
+ *   valid(b,g,i,j) = mask[b,g,i,j] != 0  AND  (not is_causal OR j <= i + lk - lq)
+ *   S[b,h,i,j]     = scale * <q[b,i,h,:], k[b,j,g,:]> + bias[b,g,i,j]   on valid (i,j)
+ *                    -inf                                               elsewhere
+ *   o[b,i,h,:]     = sum_j softmax_j(S[b,h,i,:]) * v[b,j,g,:]
+ *
+ * with g = h / (hq / hkv) (grouped-query attention: consecutive query heads
+ * share one key/value head).  A mask element attends iff its bf16 value is
+ * non-zero (bits & 0x7FFF != 0).  The bias is added after scaling and is not
+ * scaled.  A query row with no valid key gets o = 0 and lse = +inf, and
+ * contributes nothing to any gradient.
+ *
+ * Block skipping (Flash-DMA README, key design; FlashMask README, Key
+ * Features): the [lq, lk] plane of every (b, g) is cut into 64 x 64 blocks
+ * (query rows x key columns).  dma_block_classify() labels each block
+ * SKIP (no valid element), FULL (all 4096 positions exist and are valid) or
+ * PARTIAL, and forward and backward both read that one bitmap: SKIP blocks
+ * load no K/V/mask/bias and do no arithmetic; FULL blocks read the bias only.
+ *
+ * Conventions shared by every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *     row-major in the layouts written below, and 16-byte aligned.
+ *   - lk must be a multiple of 8 when a mask or bias is given (16-byte rows).
+ *   - Sizes are 64-bit; element offsets are computed in 64 bits (a mask plane
+ *     of lq = lk = 65536 holds 2^32 elements).
+ *   - stream is a hipStream_t (NULL = the default stream).  Work is enqueued on
+ *     it asynchronously; the library never allocates, frees or synchronises
+ *     and keeps no mutable global state, so calls on different streams may
+ *     run concurrently.
+ *   - Every argument is validated before anything is enqueued.  A non-zero
+ *     status means nothing was enqueued and the outputs are untouched.  A
+ *     launch error reported by the runtime after enqueueing returns DMA_ERR_HIP.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef DMA_H_
+#define DMA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DMA_OK = 0,
+  DMA_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, bad size, misalignment */
+  DMA_ERR_UNSUPPORTED = 2,      /* valid but not implemented: d, group size */
+  DMA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DMA_ERR_HIP = 4 /* the HIP runtime refused a launch */
+};
+
+enum { DMA_BLOCK_SKIP = 0, DMA_BLOCK_PARTIAL = 1, DMA_BLOCK_FULL = 2 };
+
+/* Side of the square classification block: 64 (query rows = key columns). */
+int dma_block_size(void);
+
+/* Static text for a status code (never NULL). */
+const char* dma_status_string(int status);
+
+/*
+ * Block classification (Flash-DMA README, key design: OR-reduction of the mask
+ * block, one decision shared by forward and backward; FlashMask README, Key
+ * Features: fully masked / partially masked / unmasked blocks).
+ *
+ *   mask        bf16 [b, hkv, lq, lk], or NULL for "every key attends"
+ *   is_causal   0 or 1; blocks wholly above the causal diagonal are SKIP and
+ *               their mask bytes are not read
+ *   block_state out, uint8 [b, hkv, ceil(lq/64), ceil(lk/64)]:
+ *               DMA_BLOCK_SKIP / DMA_BLOCK_PARTIAL / DMA_BLOCK_FULL.
+ *               A block that sticks out of the matrix (ragged edge) or
+ *               crosses the causal diagonal is never FULL.
+ * Errors: DMA_ERR_INVALID_ARGUMENT for sizes < 1, NULL block_state, lk % 8 != 0
+ * with a mask, or a misaligned mask pointer.
+ */
+int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int is_causal,
+                       uint8_t* block_state, void* stream);
+
+/*
+ * Forward pass (Flash-DMA issue "Project Progress": masked scores to -inf,
+ * valid scores scaled, bias added; softmax; times V).
+ *
+ *   q           bf16 [b, lq, hq, d]
+ *   k, v        bf16 [b, lk, hkv, d]
+ *   mask, bias  bf16 [b, hkv, lq, lk]; either may be NULL (no mask: every key
+ *               attends; no bias: zero).  bias entries at masked positions
+ *               are never read into the result (they may hold NaN or inf).
+ *   block_state from dma_block_classify with the same mask, sizes and is_causal
+ *   scale       multiplies q.k (callers usually pass 1/sqrt(d))
+ *   o           out, bf16 [b, lq, hq, d]
+ *   lse         out, fp32 [b, hq, lq]: natural log of the softmax denominator
+ *               including the row maximum, +inf for rows with no valid key
+ * Supported: d in {64, 128}; hq % hkv == 0 with hq / hkv in {1, 2, 4, 8, 16}.
+ * Errors: DMA_ERR_INVALID_ARGUMENT (NULL q/k/v/o/lse/block_state, sizes < 1,
+ * misalignment, lk % 8 != 0 with mask or bias), DMA_ERR_UNSUPPORTED (d, group).
+ */
+int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
+                 const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                 float scale, int is_causal, uint16_t* o, float* lse, void* stream);
+
+/* Bytes of device workspace dma_attn_bwd needs: fp32 dq accumulator [b, lq, hq, d]
+ * plus the fp32 row terms D = rowsum(dO * O) [b, hq, lq]. */
+size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t hq, int64_t d);
+
+/*
+ * Backward pass (Flash-DMA README: gradients for query, key, value and bias,
+ * the bias gradient computed inside the backward kernels).
+ *
+ * Inputs as for dma_attn_fwd plus
+ *   o, lse      the forward's outputs for the same inputs
+ *   dout        bf16 [b, lq, hq, d], gradient of the loss w.r.t. o
+ * Outputs (every element written):
+ *   dq          bf16 [b, lq, hq, d]
+ *   dk, dv      bf16 [b, lk, hkv, d]
+ *   dbias       bf16 [b, hkv, lq, lk] = dS summed over the query heads of each
+ *               group; exactly 0 on invalid entries and SKIP blocks.  May be
+ *               NULL: then the bias gradient is not produced.
+ *   workspace   device scratch of at least dma_attn_bwd_workspace_size() bytes,
+ *               16-byte aligned, owned by the caller, contents on entry ignored
+ * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL.
+ */
+int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
+                 const uint8_t* block_state, const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b,
+                 int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq,
+                 uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMA_H_ */

@@ -1,0 +1,136 @@
+"""The C ABI library loads, exports every symbol include/dma.h declares, and rejects
+bad arguments before enqueueing anything (no GPU needed: validation precedes every HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_sparse_dynamic_amd", "libdma.so")
+HEADER = os.path.join(ROOT, "include", "dma.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced by validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import block_sparse_dynamic_amd.build as b
+
+        b.build()
+    L = ctypes.CDLL(LIB)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.dma_block_classify.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp]
+    L.dma_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp]
+    L.dma_attn_bwd_workspace_size.restype = sz
+    L.dma_attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+    L.dma_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp,
+                               vp, vp, sz, vp]
+    L.dma_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dma_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("dma_block_classify", "dma_attn_fwd", "dma_attn_bwd", "dma_attn_bwd_workspace_size",
+                 "dma_block_size", "dma_status_string"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {LIB}").read()
+    for name in declared_symbols():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_block_size_and_status_strings(lib):
+    assert lib.dma_block_size() == 64
+    for s in range(5):
+        assert lib.dma_status_string(s)
+    assert lib.dma_status_string(99) == b"unknown status"
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, mask=P, bias=P, st=P, b=1, lq=128, lk=128, hq=4, hkv=2, d=128, scale=0.1, causal=1,
+             o=P, lse=P, stream=None)
+    a.update(kw)
+    return lib.dma_attn_fwd(a["q"], a["k"], a["v"], a["mask"], a["bias"], a["st"], a["b"], a["lq"], a["lk"], a["hq"],
+                            a["hkv"], a["d"], a["scale"], a["causal"], a["o"], a["lse"], a["stream"])
+
+
+def bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, mask=P, bias=P, st=P, o=P, do=P, lse=P, b=1, lq=128, lk=128, hq=4, hkv=2, d=128,
+             scale=0.1, causal=1, dq=P, dk=P, dv=P, db=P, ws=P, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.dma_attn_bwd(a["q"], a["k"], a["v"], a["mask"], a["bias"], a["st"], a["o"], a["do"], a["lse"], a["b"],
+                            a["lq"], a["lk"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["dq"], a["dk"],
+                            a["dv"], a["db"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(st=None), INVALID),
+    (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(b=0), INVALID), (dict(lq=0), INVALID), (dict(lk=-1), INVALID), (dict(hkv=0), INVALID),
+    (dict(q=P + 2), INVALID), (dict(mask=P + 8), INVALID), (dict(o=P + 4), INVALID),
+    (dict(lk=100), INVALID),  # rows of mask/bias must be 16-byte multiples
+    (dict(hq=6, hkv=4), INVALID), (dict(causal=2), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(hq=6, hkv=2), UNSUPPORTED),
+    (dict(hq=64, hkv=2), UNSUPPORTED),
+])
+def test_fwd_rejects(lib, kw, want):
+    assert fwd(lib, **kw) == want
+
+
+def test_fwd_ragged_lk_allowed_without_mask_and_bias(lib):
+    # lk % 8 != 0 is fine when neither mask nor bias is given; check only that validation
+    # does not reject it (d unsupported short-circuits before any launch)
+    assert fwd(lib, lk=100, mask=None, bias=None, d=96) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID), (dict(dv=None), INVALID),
+    (dict(ws=None), INVALID), (dict(lse=P + 4), INVALID), (dict(db=P + 2), INVALID),
+    (dict(wsb=1000), WS_SMALL), (dict(d=80), UNSUPPORTED),
+])
+def test_bwd_rejects(lib, kw, want):
+    assert bwd(lib, **kw) == want
+
+
+def test_workspace_size(lib):
+    n = lib.dma_attn_bwd_workspace_size(2, 100, 8, 128)
+    assert n >= 2 * 100 * 8 * 128 * 4 + 2 * 8 * 100 * 4
+    assert lib.dma_attn_bwd_workspace_size(0, 1, 1, 1) == 0
+
+
+def test_classify_rejects(lib):
+    c = lib.dma_block_classify
+    assert c(P, 1, 1, 128, 128, 1, None, None) == INVALID
+    assert c(P, 0, 1, 128, 128, 1, P, None) == INVALID
+    assert c(P, 1, 1, 128, 100, 1, P, None) == INVALID
+    assert c(P + 8, 1, 1, 128, 128, 1, P, None) == INVALID
+    assert c(P, 1, 1, 128, 128, 3, P, None) == INVALID
+    assert c(P, 70000, 1, 128, 128, 1, P, None) == UNSUPPORTED
+
+
+def test_package_fails_loudly_without_library(tmp_path):
+    """The binding has no fallback: importing it without libdma.so raises."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = tmp_path / "block_sparse_dynamic_amd"
+    shutil.copytree(os.path.join(ROOT, "block_sparse_dynamic_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import block_sparse_dynamic_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "libdma.so is missing" in r.stderr

@@ -1,0 +1,127 @@
+"""GPU parity of classify / forward / backward against the fp64 oracle, whole tensors.
+
+Cases span several 64x64 tiles with ragged tails, all three block classes, NULL
+mask and bias, lq != lk (bottom-right causal alignment, rows with no valid key),
+group sizes 1..16, head dims 64 and 128, and NaN stored in masked bias entries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import Case
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    synth.CASES["tiny"],
+    Case("ragged_blocks", 10, 2, 200, 200, 8, 2, 128, True, "blocks"),
+    Case("ragged_blocks_noncausal", 11, 1, 264, 264, 4, 4, 64, False, "blocks"),
+    Case("lq_lt_lk", 12, 1, 130, 264, 8, 2, 64, True, "blocks"),
+    Case("lq_gt_lk_empty_rows", 13, 1, 200, 136, 4, 1, 128, True, "blocks"),
+    Case("no_mask_no_bias", 14, 1, 320, 320, 8, 2, 128, True, "none", bias=False),
+    Case("mask_only", 15, 1, 192, 192, 4, 2, 128, True, "topk", 64, bias=False),
+    Case("bias_only_noncausal", 16, 2, 128, 256, 2, 2, 64, False, "none"),
+    Case("g1_topk", 17, 1, 256, 256, 2, 2, 128, True, "topk", 100),
+    Case("g8_topk", 18, 1, 256, 256, 16, 2, 128, True, "topk", 96),
+    Case("g16_blocks", 19, 1, 128, 128, 16, 1, 64, True, "blocks"),
+    Case("nan_in_masked_bias", 20, 1, 256, 256, 8, 2, 128, True, "blocks", fill="nan"),
+    Case("doc_small", 21, 1, 1000, 1000, 4, 1, 128, True, "doc", doc_min=64, doc_max=300, bias_std=0.5,
+         fill="lowest"),
+    Case("all_ones_mask", 22, 1, 192, 192, 4, 1, 128, False, "ones"),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    synth.build()
+
+
+@pytest.mark.parametrize("c", SMALL, ids=[c.name for c in SMALL])
+def test_small_case_parity(c):
+    import gpu_harness as H
+
+    print(f"case {c}", flush=True)
+    H.check_small_case(c)
+
+
+def test_page_example_loss_sum():
+    """Flash-DMA README usage example: loss = output.sum(), so dO = 1 everywhere."""
+    import gpu_harness as H
+
+    c = synth.CASES["tiny"]
+    ones = np.full((c.b, c.lq, c.hq, c.d), 0x3F80, dtype=np.uint16)
+    H.check_small_case(c, do_bits=ones)
+
+
+def test_autograd_wrapper_matches_oracle():
+    """dma_attention as a torch.autograd.Function: output and grads of q, k, v, bias."""
+    import block_sparse_dynamic_amd as dma
+    import gpu_harness as H
+
+    c = Case("autograd", 23, 1, 192, 192, 4, 2, 64, True, "topk", 80)
+    q, k, v, do = synth.q(c), synth.k(c), synth.v(c), synth.do(c)
+    m, b = synth.mask_bias(c)
+    tq, tk, tv, tb = (H.to_dev(x).requires_grad_(True) for x in (q, k, v, b))
+    out = dma.dma_attention(tq, tk, tv, attn_mask=H.to_dev(m), attn_bias=tb, is_causal=True, scale=c.scale_f32)
+    out.backward(H.to_dev(do))
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.forward(q, k, v, m, b, c.scale_f32, True)
+    dq, dk, dv, db = oracle.backward(q, k, v, m, b, c.scale_f32, True, do)
+    H.check_o(H.f64(out.detach()), o_ref)
+    H.check_grad(H.f64(tq.grad), dq, "dQ")
+    H.check_grad(H.f64(tk.grad), dk, "dK")
+    H.check_grad(H.f64(tv.grad), dv, "dV")
+    H.check_grad(H.f64(tb.grad), db, "dBias")
+
+
+def test_repeatable():
+    """Two runs: O, LSE, dK, dV, dBias bit-identical (one writer per element); dQ within 1e-6 (fp32 atomics)."""
+    import gpu_harness as H
+
+    c = Case("repeat", 24, 1, 512, 512, 8, 2, 128, True, "topk", 200)
+    dc = H.DeviceCase(c)
+    outs = []
+    for _ in range(2):
+        dc.classify()
+        dc.forward()
+        dc.backward()
+        torch.cuda.synchronize()
+        outs.append([H.bits(t) for t in (dc.o, dc.dk, dc.dv, dc.dbias)] + [dc.lse.cpu().numpy(), H.f64(dc.dq)])
+    for a, b in zip(outs[0][:5], outs[1][:5]):
+        assert np.array_equal(a, b)
+    assert H.rel_l2(outs[0][5], outs[1][5]) < 1e-6
+
+
+def test_skipped_tiles_do_not_leak():
+    """K/V rows and bias of SKIP blocks set to NaN change nothing (they are never loaded)."""
+    import gpu_harness as H
+
+    c = Case("skip_nan", 25, 1, 256, 256, 4, 2, 128, False, "blocks")
+    dc = H.DeviceCase(c)
+    dc.classify()
+    dc.forward()
+    torch.cuda.synchronize()
+    o1 = H.bits(dc.o)
+    st = dc.state.cpu().numpy()
+    bias2 = dc.bias_h.copy()
+    for bb in range(c.b):
+        for g in range(c.hkv):
+            for qb in range(st.shape[2]):
+                for kb in range(st.shape[3]):
+                    if st[bb, g, qb, kb] == oracle.SKIP:
+                        bias2[bb, g, qb * 64:(qb + 1) * 64, kb * 64:(kb + 1) * 64] = 0x7FC0
+    # a key block that is SKIP for every query block of a plane: poison its K and V rows
+    k2, v2 = dc.k_h.copy(), dc.v_h.copy()
+    for kb in range(st.shape[3]):
+        for g in range(c.hkv):
+            if np.all(st[0, g, :, kb] == oracle.SKIP):
+                k2[0, kb * 64:(kb + 1) * 64, g] = 0x7FC0
+                v2[0, kb * 64:(kb + 1) * 64, g] = 0x7FC0
+    dc.bias, dc.k, dc.v = H.to_dev(bias2), H.to_dev(k2), H.to_dev(v2)
+    dc.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(H.bits(dc.o), o1)
