@@ -1,0 +1,215 @@
+"""Throughput of the dynamic-mask attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input already
+resident in HBM: block classification, forward (O, LSE) and backward (dQ, dK, dV,
+dBias), each through the C ABI on the current stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config headline]
+
+Prints one JSON line.  ``value`` is the effective fwd+bwd TFLOP/s of the step:
+MMA FLOPs over the non-SKIP 64x64 blocks (4*d per block element per query head
+forward, 10*d backward; FlashMask README, Performance: theoretical FLOPs count
+only the core matrix multiplies) divided by the time of the whole step,
+classification included.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=16, help="query-row blocks the oracle times")
+    return ap.parse_args()
+
+
+def block_counts(state):
+    import torch
+
+    n_skip = int((state == 0).sum())
+    n_p = int((state == 1).sum())
+    n_f = int((state == 2).sum())
+    return n_skip, n_p, n_f
+
+
+def cpu_baseline(c, blocks: int, f_total: float):
+    """Oracle (fp64 numpy) on a bounded sample: `blocks` 64-row query blocks of the workload,
+    forward and backward, extrapolated to the whole workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+
+    sample = synth.sample_row_blocks(c, blocks)
+    k = oracle.bf16_to_f64(synth.k(c))
+    v = oracle.bf16_to_f64(synth.v(c))
+    t_total = 0.0
+    for (bb, r0) in sample:
+        rows = np.arange(r0, min(r0 + 64, c.lq))
+        qr = oracle.bf16_to_f64(synth.rows_of(c, synth.TAG_Q, c.hq, bb, rows))
+        dor = oracle.bf16_to_f64(synth.rows_of(c, synth.TAG_DO, c.hq, bb, rows))
+        ms, bs = [], []
+        for g in range(c.hkv):
+            m, b = synth.mask_bias_rows(c, bb, g, int(rows[0]), len(rows))
+            ms.append(m)
+            bs.append(b)
+        mask = None if ms[0] is None else np.stack(ms)
+        bias = None if bs[0] is None else oracle.bf16_to_f64(np.stack(bs))
+        t0 = time.perf_counter()
+        oracle.forward_rows(qr, k[bb], v[bb], mask, bias, c.scale_f32, c.causal, rows, c.lq)
+        oracle.backward_rows(qr, k[bb], v[bb], mask, bias, c.scale_f32, c.causal, rows, c.lq, dor)
+        t_total += time.perf_counter() - t0
+    n_blocks_all = c.b * ((c.lq + 63) // 64)
+    t_whole = t_total / len(sample) * n_blocks_all
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": round(f_total / t_whole / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(sample)} seeded 64-row query blocks (all {c.hq} heads, fwd+bwd) of {n_blocks_all}, "
+                  f"{t_total:.1f} s, extrapolated to the whole workload ({t_whole:.0f} s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (each (batch, kv head) plane "
+              "is independent, so several GPUs would each run this one-GPU kernel on their share).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_dynamic_amd as dma
+    import synth
+    from synth.device import upload_dense, upload_mask_bias
+
+    c = synth.CASES[args.config]
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    q, k, v, do = upload_dense(c)
+    mask, bias = upload_mask_bias(c)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {c.name}: inputs generated and uploaded in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    state = torch.empty(dma.block_state_shape(c.b, c.hkv, c.lq, c.lk), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = torch.empty((c.b, c.hkv, c.lq, c.lk), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.hq, c.d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(timed=None):
+        if timed is not None:
+            timed[0].record(stream)
+        dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, state, stream)
+        if timed is not None:
+            timed[1].record(stream)
+        dma.dma_attn_fwd(q, k, v, mask, bias, state, c.scale_f32, c.causal, o, lse, stream)
+        if timed is not None:
+            timed[2].record(stream)
+        dma.dma_attn_bwd(q, k, v, mask, bias, state, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws,
+                         stream)
+        if timed is not None:
+            timed[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per = np.zeros((args.steps, 3))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in range(args.steps):
+        e = evs[s]
+        per[s] = [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+    t_cls, t_fwd, t_bwd = per.mean(axis=0)  # ms
+    ms_step = wall / args.steps * 1e3
+
+    n_skip, n_p, n_f = block_counts(state)
+    n_ns = n_p + n_f
+    G, d = c.hq // c.hkv, c.d
+    f_fwd = 4.0 * d * 64 * 64 * G * n_ns
+    f_bwd = 10.0 * d * 64 * 64 * G * n_ns
+    # blocks wholly excluded by causality are never read by classification
+    nqb, nkb = (c.lq + 63) // 64, (c.lk + 63) // 64
+    qb = np.arange(nqb)[:, None]
+    kb = np.arange(nkb)[None, :]
+    live = (kb * 64 <= np.minimum(qb * 64 + 63, c.lq - 1) + (c.lk - c.lq)) if c.causal else np.ones((nqb, nkb), bool)
+    n_live = int(live.sum()) * c.b * c.hkv
+    has_mask = mask is not None
+    b_cls = 2.0 * 64 * 64 * n_live if has_mask else 0.0
+    b_fwd = 2.0 * 64 * 64 * (2 * n_p + n_f)
+    b_bwd = b_fwd + 2.0 * c.b * c.hkv * c.lq * c.lk
+    tflops = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    gbs = (b_cls + b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9
+
+    # dominant launch: the one with the largest share of the step
+    phases = {"bwd": (t_bwd, f_bwd, "dma_attn_bwd (bwd_pre + bwd_main + dq_convert)"),
+              "fwd": (t_fwd, f_fwd, "dma_attn_fwd (fwd_kernel)")}
+    dom = max(phases, key=lambda k: phases[k][0])
+    t_dom, f_dom, dom_name = phases[dom]
+    achieved = f_dom / (t_dom * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom_name,
+                "ms_per_launch": round(t_dom, 4)}
+
+    line = {
+        "metric": "fwd+bwd effective TFLOP/s (unmasked tiles) + HBM GB/s, L=16K GQA top-k",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1) q/k/v/dO/bias, top-k mask from the bias)",
+        "config": {"workload": f"{c.name}: b={c.b} L={c.lq} Hq={c.hq} Hkv={c.hkv} d={c.d} "
+                               f"{'top-k ' + str(c.topk) if c.mask == 'topk' else c.mask} mask, "
+                               f"{'causal' if c.causal else 'non-causal'}",
+                   "b": c.b, "seq_len": c.lq, "hq": c.hq, "hkv": c.hkv, "d": c.d,
+                   "blocks_nonskip": n_ns, "blocks_partial": n_p, "blocks_full": n_f, "blocks_skip": n_skip},
+        "hbm_gbs_mandatory": round(gbs, 1),
+        "phases_ms": {"classify": round(t_cls, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
+        "phases_tflops": {"fwd": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
+                          "bwd": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2)},
+        "phases_gbs_mandatory": {"classify": round(b_cls / (t_cls * 1e-3) / 1e9, 1),
+                                 "fwd": round(b_fwd / (t_fwd * 1e-3) / 1e9, 1),
+                                 "bwd": round(b_bwd / (t_bwd * 1e-3) / 1e9, 1)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, args.cpu_blocks, f_fwd + f_bwd)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
