@@ -10,25 +10,31 @@
 //
 // Kernels:
 //   bwd_pre_kernel    D = rowsum(dO * O) and a zeroed fp32 dQ accumulator.
-//   bwd_main_kernel   one workgroup per (batch, kv head g, 64-key block); four
-//                     wavefronts own 16 keys each.  K and V of the block sit in
-//                     registers for the whole kernel and dK/dV accumulate in
-//                     registers over every non-SKIP query block and every head
-//                     of the group, so they are written once, without atomics.
-//                     Per query block the effective bias (bias where valid,
-//                     -inf elsewhere) is staged once and serves all G heads;
-//                     dBias for the block is summed over the heads in
-//                     registers and stored once.  SKIP blocks get zeros.
-//                     dQ: dS^T goes to LDS and each wave multiplies 16 query
-//                     rows by the block's K, adding into the fp32 accumulator
-//                     with atomics (query rows are shared by all key blocks).
+//   bwd_main_kernel   one workgroup per (batch, kv head g, 128 keys = two
+//                     classification blocks); four wavefronts own 32 keys each.
+//                     Work items are (query block, 32-row half, head), heads
+//                     innermost.
+//                     K and V of the keys sit in registers for the whole kernel
+//                     and dK/dV accumulate in registers over every non-SKIP query
+//                     block and every head of the group, so they are written
+//                     once, without atomics.  Per query block the effective bias
+//                     (bias where valid, -inf elsewhere) is staged once and
+//                     serves all G heads; dBias of the block is summed over the
+//                     heads in registers and stored once.  SKIP blocks get zeros
+//                     and no loads.  The Q/dO tiles (and the bias/mask of a new
+//                     query block) of the next item are loaded into registers
+//                     while the current item computes.  dQ: dS^T goes to LDS and
+//                     each wave multiplies it by 32 columns of K, adding into the
+//                     fp32 accumulator with atomics (query rows are shared by
+//                     all key blocks).
 //   dq_convert_kernel fp32 accumulator -> bf16 dQ.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16.  S = Q K^T puts one key per lane (lane l%16)
-// and 4 query rows per lane group, which is the A-operand layout of the
-// key-major products dV = P^T dO and dK = dS^T Q; their B operands (dO, Q with
-// the query index as the contraction) come from the row-major tiles through
-// ds_read_b64_tr_b16.
+// MFMA: v_mfma_f32_32x32x16_bf16 for all five products.  S = Q K^T puts one key
+// per lane (lane l%32) and 16 query rows per lane, which is the A-operand layout
+// of the key-major products dV = P^T dO and dK = dS^T Q (the query order inside
+// a k-step only has to agree between A and B); their B operands (dO, Q with the
+// query index as the contraction) come from the row-major tiles through
+// ds_read_b64_tr_b16, as do both operands of dQ = dS K.
 #include <math.h>
 
 #include "common.h"
@@ -81,102 +87,198 @@ struct BwdParams {
   uint16_t* dv;
   uint16_t* dbias;
   int64_t lq, lk, hq, hkv;
-  int G, nqb, nkb, total_wg;
+  int G, nqb, nkb, nkb2, total_wg;
   float scale;
   int causal;
 };
 
+constexpr int kKeys = 128;  // keys per workgroup: two classification blocks
+constexpr int kRows = 32;   // query rows per item (half a classification block)
+
 template <int D>
 struct BwdSmem {
-  static constexpr int kRow = D + 8;
-  static constexpr int kSRow = kBlock + 8;
-  uint16_t k[kBlock * kRow];   // K tile [key][d]
-  uint16_t q[kBlock * kRow];   // Q tile of one head [query][d]
-  uint16_t g[kBlock * kRow];   // dO tile of one head [query][d]
-  uint16_t s[kBlock * kSRow];  // dS^T [key][query] (bf16)
-  uint16_t b[kBlock * kSRow];  // effective bias [query][key] (bf16)
-  float lse2[kBlock];          // lse * log2(e), +inf outside the matrix
-  float dr[kBlock];            // D = rowsum(dO * O)
+  static constexpr int kRow = D + 8;        // K, Q, dO tiles [row][d]
+  static constexpr int kSRow = kRows + 8;   // dS^T [key][query]
+  static constexpr int kBRow = kKeys + 8;   // effective bias [query][key]
+  uint16_t q[kRows * kRow];
+  uint16_t g[kRows * kRow];
+  uint16_t s[kKeys * kSRow];
+  uint16_t b[kRows * kBRow];
+  float lse2[kRows];  // lse * log2(e); +inf outside the matrix
+  float dr[kRows];    // D = rowsum(dO * O)
+  uint16_t k[kKeys * kRow];
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
-  constexpr int KR = BwdSmem<D>::kRow, SR = BwdSmem<D>::kSRow;
+  constexpr int KR = BwdSmem<D>::kRow, SR = BwdSmem<D>::kSRow, BR = BwdSmem<D>::kBRow;
+  constexpr int QN = kRows * (D / 8) / 256;      // 16-byte chunks of a Q (or dO) item per thread
+  constexpr int BN = kRows * (kKeys / 8) / 256;  // 16-byte chunks of the bias (or mask) rows per thread
   __shared__ BwdSmem<D> sm;
 
   const int w = blockIdx.x;
   const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
-  const int plane = t / p.nkb, kb = t % p.nkb;  // low kb (most query blocks under causality) first
+  const int plane = t / p.nkb2, KB = t % p.nkb2;  // low key blocks (most query blocks under causality) first
+  const int kb0 = 2 * KB;
+  const bool has_kb1 = kb0 + 1 < p.nkb;
   const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int kl = lane & 15, qg = lane >> 4;
-  const int key_loc = wave * 16 + kl;
-  const int64_t key_abs = (int64_t)kb * kBlock + key_loc;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int half = wave >> 1;           // which 64-key classification block this wave is in
+  const int key_loc = wave * 32 + l32;  // key of this lane inside the 128
+  const int64_t key_abs = (int64_t)kb0 * kBlock + key_loc;
   const int64_t shift = p.lk - p.lq;
   const int64_t plane_off = (int64_t)plane * p.lq * p.lk;
   const bool has_bias = p.bias != nullptr, has_mask = p.mask != nullptr;
   const float scale2 = p.scale * kLog2eB;
+  const uint8_t* st_col = p.state + (int64_t)plane * p.nqb * p.nkb + kb0;  // + qb * nkb (+1)
 
-  // K, V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kreg[D / 32], vreg[D / 32];
+  // this lane's key row of V: B operand of dP = dO V^T (d = s*16 + hi*8 ..); the K operand of
+  // S = Q K^T is read from the staged K tile
+  bf16x8 vreg[D / 16];
   {
-    const int64_t off = ((bidx * p.lk + key_abs) * p.hkv + g) * D + qg * 8;
+    const int64_t off = ((bidx * p.lk + key_abs) * p.hkv + g) * D + hi * 8;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (key_abs < p.lk) {
-        kw = *reinterpret_cast<const u32x4*>(p.k + off + s * 32);
-        vw = *reinterpret_cast<const u32x4*>(p.v + off + s * 32);
-      }
-      kreg[s] = __builtin_bit_cast(bf16x8, kw);
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 vw = {0u, 0u, 0u, 0u};
+      if (key_abs < p.lk) vw = *reinterpret_cast<const u32x4*>(p.v + off + s * 16);
       vreg[s] = __builtin_bit_cast(bf16x8, vw);
     }
   }
-  // K tile for dQ.
-  for (int task = tid; task < kBlock * (D / 8); task += 256) {
+  for (int task = tid; task < kKeys * (D / 8); task += 256) {
     const int r = task / (D / 8), c = task % (D / 8);
-    const int64_t key = (int64_t)kb * kBlock + r;
+    const int64_t key = (int64_t)kb0 * kBlock + r;
     u32x4 kw = {0u, 0u, 0u, 0u};
     if (key < p.lk) kw = *reinterpret_cast<const u32x4*>(p.k + ((bidx * p.lk + key) * p.hkv + g) * D + c * 8);
     *reinterpret_cast<u32x4*>(&sm.k[r * KR + c * 8]) = kw;
   }
 
-  f32x4 dk[D / 16], dv[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    dk[dt] = f32x4{};
-    dv[dt] = f32x4{};
-  }
-
-  const int trow = kl >> 2, tcol = (kl & 3) * 4;  // ds_read_b64_tr_b16 addressing inside a lane group
-
-  for (int qb = 0; qb < p.nqb; ++qb) {
-    const uint8_t st = p.state[((int64_t)plane * p.nqb + qb) * p.nkb + kb];
-    const int64_t i0 = (int64_t)qb * kBlock;
-    if (st == kSkip) {
-      if (p.dbias != nullptr) {  // dense contract: zeros on skipped blocks
-        for (int task = tid; task < kBlock * 8; task += 256) {
-          const int r = task >> 3, c = task & 7;
-          const int64_t i = i0 + r, j = (int64_t)kb * kBlock + c * 8;
+  // next query block with a non-SKIP half at or after `from`; rows of blocks that are SKIP in
+  // both halves get their zeros here
+  auto next_qb = [&](int from, uint8_t& s0, uint8_t& s1) -> int {
+    for (int qb = from; qb < p.nqb; ++qb) {
+      const uint8_t* sp = st_col + (int64_t)qb * p.nkb;
+      s0 = sp[0];
+      s1 = has_kb1 ? sp[1] : kSkip;
+      if (s0 != kSkip || s1 != kSkip) return qb;
+      if (p.dbias != nullptr) {
+        for (int task = tid; task < kBlock * (kKeys / 8); task += 256) {
+          const int r = task / (kKeys / 8), c = task % (kKeys / 8);
+          const int64_t i = (int64_t)qb * kBlock + r, j = (int64_t)kb0 * kBlock + c * 8;
           if (i < p.lq && j < p.lk)
             *reinterpret_cast<u32x4*>(p.dbias + plane_off + i * p.lk + j) = u32x4{0u, 0u, 0u, 0u};
         }
       }
-      continue;
     }
-    const bool full = (st == kFull);
-    const bool use_b = has_bias || !full;
-    __syncthreads();  // previous block's readers of the staged tiles are done
-    if (use_b) {
-      for (int task = tid; task < kBlock * 8; task += 256) {
-        const int r = task >> 3, c = task & 7;
-        const int64_t i = i0 + r, j0 = (int64_t)kb * kBlock + c * 8;
-        const bool inside = i < p.lq && j0 < p.lk;
-        u32x4 bw = {0u, 0u, 0u, 0u};
-        if (has_bias && inside) bw = *reinterpret_cast<const u32x4*>(p.bias + plane_off + i * p.lk + j0);
-        if (!full) {
-          u32x4 mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-          if (has_mask && inside) mw = *reinterpret_cast<const u32x4*>(p.mask + plane_off + i * p.lk + j0);
+    return p.nqb;
+  };
+
+  // Per-lane 32-bit offsets inside an item; the item's base pointers are uniform (scalar
+  // registers), so no 64-bit per-lane address stays live across items.
+  uint32_t qoff[QN], boff[BN];
+#pragma unroll
+  for (int n = 0; n < QN; ++n) {
+    const int task = tid + n * 256;
+    qoff[n] = (uint32_t)(task / (D / 8)) * (uint32_t)(p.hq * D) + (uint32_t)(task % (D / 8)) * 8u;
+  }
+#pragma unroll
+  for (int n = 0; n < BN; ++n) {
+    const int task = tid + n * 256;
+    boff[n] = (uint32_t)(task / (kKeys / 8)) * (uint32_t)p.lk + (uint32_t)(task % (kKeys / 8)) * 8u;
+  }
+
+  // registers that carry the next item while the current one computes
+  u32x4 pq[QN], pg[QN], pb[BN], pm[BN];
+  float prow;
+  auto prefetch = [&](int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
+    const int64_t h = g * p.G + hh;
+    const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
+    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
+    const int64_t item = ((bidx * p.lq + i0) * p.hq + h) * D;
+#pragma unroll
+    for (int n = 0; n < QN; ++n) {
+      const int r = (tid + n * 256) / (D / 8);
+      u32x4 qw = {0u, 0u, 0u, 0u}, gw = {0u, 0u, 0u, 0u};
+      if (r < rows_left) {
+        qw = *reinterpret_cast<const u32x4*>(p.q + item + qoff[n]);
+        gw = *reinterpret_cast<const u32x4*>(p.dout + item + qoff[n]);
+      }
+      pq[n] = qw;
+      pg[n] = gw;
+    }
+    if (hh == 0) {
+      const int64_t boff0 = plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;
+#pragma unroll
+      for (int n = 0; n < BN; ++n) {
+        const int task = tid + n * 256;
+        const int r = task / (kKeys / 8), c = task % (kKeys / 8);
+        const uint8_t st = (c < 8) ? s0 : s1;
+        const bool in = st != kSkip && r < rows_left && (int64_t)kb0 * kBlock + c * 8 < p.lk;
+        u32x4 bw = {0u, 0u, 0u, 0u}, mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        if (in) {
+          if (has_bias) bw = *reinterpret_cast<const u32x4*>(p.bias + boff0 + boff[n]);
+          if (has_mask && st == kPartial) mw = *reinterpret_cast<const u32x4*>(p.mask + boff0 + boff[n]);
+        }
+        pb[n] = bw;
+        pm[n] = mw;
+      }
+    }
+    float rv = 0.f;
+    if (tid < 2 * kRows) {
+      const int r = tid & (kRows - 1);
+      const int64_t rowbase = (bidx * p.hq + h) * p.lq + i0;
+      if (tid < kRows) {
+        rv = INFINITY;
+        if (r < rows_left) rv = p.lse[rowbase + r] * kLog2eB;
+      } else if (r < rows_left) {
+        rv = p.drow[rowbase + r];
+      }
+    }
+    prow = rv;
+  };
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+  f32x16 dbacc = f32x16{};
+  uint32_t beff[4][2];  // effective bias of this lane's (query, key) pairs, bf16 pairs
+
+  // tr-read addressing: inside a 16-lane group, lane s points at row +s/4, column +4(s%4)
+  const int trow = (lane & 15) >> 2;
+  const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  uint8_t cs0, cs1;  // states of the current item's two key blocks
+  int qb = next_qb(0, cs0, cs1);
+  int rh = 0, hh = 0;
+  if (qb < p.nqb) prefetch(qb, 0, 0, cs0, cs1);
+  lds_barrier();  // K tile staged
+
+  while (qb < p.nqb) {
+    const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
+    const int64_t h = g * p.G + hh;
+    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
+    // ---- write the prefetched item into LDS ----------------------------------------
+#pragma unroll
+    for (int n = 0; n < QN; ++n) {
+      const int task = tid + n * 256;
+      const int r = task / (D / 8), c = task % (D / 8);
+      *reinterpret_cast<u32x4*>(&sm.q[r * KR + c * 8]) = pq[n];
+      *reinterpret_cast<u32x4*>(&sm.g[r * KR + c * 8]) = pg[n];
+    }
+    if (hh == 0) {
+#pragma unroll
+      for (int n = 0; n < BN; ++n) {
+        const int task = tid + n * 256;
+        const int r = task / (kKeys / 8), c = task % (kKeys / 8);
+        const uint8_t st = (c < 8) ? cs0 : cs1;
+        const int64_t i = i0 + r, j0 = (int64_t)kb0 * kBlock + c * 8;
+        const bool inside = i < p.lq && j0 < p.lk && st != kSkip;
+        u32x4 bw = pb[n];
+        if (st != kFull) {
+          const u32x4 mw = pm[n];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t j = j0 + 2 * e;
@@ -187,160 +289,162 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
             bw[e] = lo | (hi16 << 16);
           }
         }
-        *reinterpret_cast<u32x4*>(&sm.b[r * SR + c * 8]) = bw;
+        *reinterpret_cast<u32x4*>(&sm.b[r * BR + c * 8]) = bw;
       }
     }
-    __syncthreads();
-    // effective bias of this lane's 16 (query, key) pairs, in log2 units
-    f32x4 beff[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float bv = 0.f;
-        if (use_b) bv = __uint_as_float((uint32_t)sm.b[(tt * 16 + qg * 4 + i) * SR + key_loc] << 16) * kLog2eB;
-        beff[tt][i] = bv;
-      }
-    f32x4 dbacc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+    if (tid < kRows) sm.lse2[tid] = prow;
+    else if (tid < 2 * kRows) sm.dr[tid - kRows] = prow;
+    const uint8_t my_st = half ? cs1 : cs0;
+    const uint8_t s0_now = cs0, s1_now = cs1;
+    lds_barrier();
 
-    for (int hh = 0; hh < p.G; ++hh) {
-      const int64_t h = g * p.G + hh;
-      // ---- stage Q, dO, lse, D of head h -------------------------------------
-      for (int task = tid; task < kBlock * (D / 8); task += 256) {
-        const int r = task / (D / 8), c = task % (D / 8);
-        const int64_t i = i0 + r;
-        u32x4 qw = {0u, 0u, 0u, 0u}, gw = {0u, 0u, 0u, 0u};
-        if (i < p.lq) {
-          const int64_t off = ((bidx * p.lq + i) * p.hq + h) * D + c * 8;
-          qw = *reinterpret_cast<const u32x4*>(p.q + off);
-          gw = *reinterpret_cast<const u32x4*>(p.dout + off);
-        }
-        *reinterpret_cast<u32x4*>(&sm.q[r * KR + c * 8]) = qw;
-        *reinterpret_cast<u32x4*>(&sm.g[r * KR + c * 8]) = gw;
+    // ---- start loading the next item ------------------------------------------------
+    int nqb = qb, nrh = rh, nhh = hh + 1;
+    uint8_t ns0 = cs0, ns1 = cs1;
+    if (nhh == p.G) {
+      nhh = 0;
+      nrh = rh + 1;
+      if (nrh == 2 || i0 + kRows >= p.lq) {
+        nrh = 0;
+        nqb = next_qb(qb + 1, ns0, ns1);
       }
-      if (tid < kBlock) {
-        const int64_t i = i0 + tid;
-        float l2 = INFINITY, dd = 0.f;
-        if (i < p.lq) {
-          l2 = p.lse[(bidx * p.hq + h) * p.lq + i] * kLog2eB;
-          dd = p.drow[(bidx * p.hq + h) * p.lq + i];
-        }
-        sm.lse2[tid] = l2;
-        sm.dr[tid] = dd;
+    }
+    if (nqb < p.nqb) prefetch(nqb, nrh, nhh, ns0, ns1);
+
+    if (hh == 0) {
+      // effective bias in the S layout: row group gi -> rows gi*8 + hi*4 .. +3 of the item
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const i16x4 x = lds_read_tr16(&sm.b[(gi * 8 + hi * 4 + trow) * BR + wave * 32 + tcol]);
+        const u32x2 u = __builtin_bit_cast(u32x2, x);
+        beff[gi][0] = u[0];
+        beff[gi][1] = u[1];
       }
-      __syncthreads();
-      // ---- S = Q K^T and dP = dO V^T (query tiles tt, key = this lane) -------
-      f32x4 sacc[4], pacc[4];
+      dbacc = f32x16{};
+    }
+
+    // A SKIP half runs the same straight-line code: its effective bias is -inf everywhere,
+    // so P = dS = 0 exactly and it adds nothing (a branch here would make the compiler
+    // shuttle the dK/dV accumulators between register files on every item).
+    // ---- S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys ------------------
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        sacc[tt] = f32x4{};
-        pacc[tt] = f32x4{};
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[key_loc * KR + s * 16 + hi * 8]);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[l32 * KR + s * 16 + hi * 8]);
+      sacc = mfma32(aq, kbs, sacc);
+      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[l32 * KR + s * 16 + hi * 8]);
+      pacc = mfma32(ag, vreg[s], pacc);
+    }
+    // ---- P = exp(S - lse) on valid entries, dS = P (dP - D) -----------------------------
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[(tt * 16 + kl) * KR + s * 32 + qg * 8]);
-          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[(tt * 16 + kl) * KR + s * 32 + qg * 8]);
-          sacc[tt] = mfma16(aq, kreg[s], sacc[tt]);
-          pacc[tt] = mfma16(ag, vreg[s], pacc[tt]);
-        }
+    for (int gi = 0; gi < 4; ++gi) {
+      const int q0 = gi * 8 + hi * 4;
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[q0]);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dr[q0]);
+      const float bb[4] = {bf16_lo(beff[gi][0]), bf16_hi(beff[gi][0]), bf16_lo(beff[gi][1]), bf16_hi(beff[gi][1])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = gi * 4 + e;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale2, fmaf(bb[e], kLog2eB, -l2[e])));
+        const float ds = pv * (pacc[i] - dd[e]);
+        sacc[i] = pv;
+        pacc[i] = ds;
+        dbacc[i] += ds;
       }
-      // ---- P, dS -------------------------------------------------------------
+    }
+    // ---- dV += P^T dO, dK += dS^T Q: two k-steps of 16 queries ----------------------------
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[tt * 16 + qg * 4]);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dr[tt * 16 + qg * 4]);
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 pw, sw;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[tt][i], scale2, beff[tt][i] - l2[i]));
-          const float ds = pv * (pacc[tt][i] - dd[i]);
-          sacc[tt][i] = pv;
-          pacc[tt][i] = ds;
-          dbacc[tt][i] += ds;
-        }
+      for (int e = 0; e < 4; ++e) {
+        pw[e] = pack_bf16x2(sacc[ks * 8 + 2 * e], sacc[ks * 8 + 2 * e + 1]);
+        sw[e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
       }
-      // ---- dV += P^T dO, dK += dS^T Q ------------------------------------------
+      const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw);
+      const int r0 = ks * 16 + hi * 4 + trow;
 #pragma unroll
-      for (int t0 = 0; t0 < 4; t0 += 2) {
-        u32x4 pw, sw;
-        pw[0] = pack_bf16x2(sacc[t0][0], sacc[t0][1]);
-        pw[1] = pack_bf16x2(sacc[t0][2], sacc[t0][3]);
-        pw[2] = pack_bf16x2(sacc[t0 + 1][0], sacc[t0 + 1][1]);
-        pw[3] = pack_bf16x2(sacc[t0 + 1][2], sacc[t0 + 1][3]);
-        sw[0] = pack_bf16x2(pacc[t0][0], pacc[t0][1]);
-        sw[1] = pack_bf16x2(pacc[t0][2], pacc[t0][3]);
-        sw[2] = pack_bf16x2(pacc[t0 + 1][0], pacc[t0 + 1][1]);
-        sw[3] = pack_bf16x2(pacc[t0 + 1][2], pacc[t0 + 1][3]);
-        const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw);
-        const int r0 = t0 * 16 + qg * 4 + trow;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const i16x4 g0 = lds_read_tr16(&sm.g[r0 * KR + dt * 16 + tcol]);
-          const i16x4 g1 = lds_read_tr16(&sm.g[(r0 + 16) * KR + dt * 16 + tcol]);
-          dv[dt] = mfma16(ap, join_bf16x8(g0, g1), dv[dt]);
-          const i16x4 q0 = lds_read_tr16(&sm.q[r0 * KR + dt * 16 + tcol]);
-          const i16x4 q1 = lds_read_tr16(&sm.q[(r0 + 16) * KR + dt * 16 + tcol]);
-          dk[dt] = mfma16(as, join_bf16x8(q0, q1), dk[dt]);
-        }
-        // dS^T rows of this lane's key: 4 consecutive queries per tile
-#pragma unroll
-        for (int tt = t0; tt < t0 + 2; ++tt) {
-          u32x2 w2;
-          w2[0] = pack_bf16x2(pacc[tt][0], pacc[tt][1]);
-          w2[1] = pack_bf16x2(pacc[tt][2], pacc[tt][3]);
-          *reinterpret_cast<u32x2*>(&sm.s[key_loc * SR + tt * 16 + qg * 4]) = w2;
-        }
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const i16x4 g0 = lds_read_tr16(&sm.g[r0 * KR + dt * 32 + tcol]);
+        const i16x4 g1 = lds_read_tr16(&sm.g[(r0 + 8) * KR + dt * 32 + tcol]);
+        dv[dt] = mfma32(ap, join_bf16x8(g0, g1), dv[dt]);
+        const i16x4 q0 = lds_read_tr16(&sm.q[r0 * KR + dt * 32 + tcol]);
+        const i16x4 q1 = lds_read_tr16(&sm.q[(r0 + 8) * KR + dt * 32 + tcol]);
+        dk[dt] = mfma32(as, join_bf16x8(q0, q1), dk[dt]);
       }
-      __syncthreads();
-      // ---- dQ rows wave*16 .. +15 += scale * dS K  (fp32 atomics) -----------
-      {
-        bf16x8 aS[2];
+    }
+    // ---- dS^T row of this lane's key: 4 consecutive queries per row group -----------------
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int r0 = ks * 32 + qg * 8 + trow;
-          const i16x4 s0 = lds_read_tr16(&sm.s[r0 * SR + wave * 16 + tcol]);
-          const i16x4 s1 = lds_read_tr16(&sm.s[(r0 + 4) * SR + wave * 16 + tcol]);
-          aS[ks] = join_bf16x8(s0, s1);
-        }
-        const int64_t qrow0 = i0 + wave * 16 + qg * 4;
+    for (int gi = 0; gi < 4; ++gi) {
+      u32x2 w2;
+      w2[0] = pack_bf16x2(pacc[gi * 4 + 0], pacc[gi * 4 + 1]);
+      w2[1] = pack_bf16x2(pacc[gi * 4 + 2], pacc[gi * 4 + 3]);
+      *reinterpret_cast<u32x2*>(&sm.s[key_loc * SR + gi * 8 + hi * 4]) = w2;
+    }
+    lds_barrier();
+
+    // ---- dQ[:, dtile*32 .. +31] += scale * dS K over the non-SKIP key halves ------------------
+    // D/32 column tiles of dQ; with d = 64 two waves share a tile and split the keys.
+    {
+      constexpr int DT = D / 32, WPT = 4 / DT, KCH = 8 / WPT;
+      const int dtile = wave % DT, kpart = wave / DT;
+      const int ks_lo = max((s0_now != kSkip) ? 0 : 4, kpart * KCH);
+      const int ks_hi = min((s1_now != kSkip) ? 8 : 4, (kpart + 1) * KCH);
+      f32x16 c = f32x16{};
+      for (int ks = ks_lo; ks < ks_hi; ++ks) {
+        const int r0 = ks * 16 + hi * 8 + trow;
+        const i16x4 k0 = lds_read_tr16(&sm.k[r0 * KR + dtile * 32 + tcol]);
+        const i16x4 k1 = lds_read_tr16(&sm.k[(r0 + 4) * KR + dtile * 32 + tcol]);
+        const i16x4 a0 = lds_read_tr16(&sm.s[r0 * SR + tcol]);
+        const i16x4 a1 = lds_read_tr16(&sm.s[(r0 + 4) * SR + tcol]);
+        c = mfma32(join_bf16x8(a0, a1), join_bf16x8(k0, k1), c);
+      }
+      if (ks_lo < ks_hi) {
+        float* dqbase = p.dq_acc + ((bidx * p.lq + i0) * p.hq + h) * D + dtile * 32;
+        uint32_t rstride = (uint32_t)(p.hq * D);
+        asm volatile("" : "+s"(rstride));  // keep the row offsets below inside the loop (not hoisted)
+        const uint32_t lane_off = (uint32_t)(hi * 4) * rstride + (uint32_t)l32;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          f32x4 c = f32x4{};
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int r0 = ks * 32 + qg * 8 + trow;
-            const i16x4 k0 = lds_read_tr16(&sm.k[r0 * KR + dt * 16 + tcol]);
-            const i16x4 k1 = lds_read_tr16(&sm.k[(r0 + 4) * KR + dt * 16 + tcol]);
-            c = mfma16(aS[ks], join_bf16x8(k0, k1), c);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t qi = qrow0 + i;
-            if (qi < p.lq) atomicAdd(p.dq_acc + ((bidx * p.lq + qi) * p.hq + h) * D + dt * 16 + kl, c[i] * p.scale);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int rc = (i >> 2) * 8 + (i & 3);  // row minus this lane's hi*4
+          float* rowp = dqbase + (uint32_t)rc * rstride;
+          if (rc + hi * 4 < rows_left) atomicAdd(rowp + lane_off, c[i] * p.scale);
         }
       }
     }
-    // ---- dBias of the block, summed over the group, from registers ----------
-    if (p.dbias != nullptr && key_abs < p.lk) {
+
+    // ---- dBias of the item's rows, summed over the group: store after the last head -------------
+    if (hh == p.G - 1 && p.dbias != nullptr && key_abs < p.lk) {
+      uint16_t* dbbase = p.dbias + plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;
+      uint32_t lk32 = (uint32_t)p.lk;
+      asm volatile("" : "+s"(lk32));  // keep the row offsets below inside the loop (not hoisted)
+      const uint32_t lane_off = (uint32_t)(hi * 4) * lk32 + (uint32_t)key_loc;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t qi = i0 + tt * 16 + qg * 4 + i;
-          if (qi < p.lq) p.dbias[plane_off + qi * p.lk + key_abs] = f32_to_bf16(dbacc[tt][i]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int rc = (i >> 2) * 8 + (i & 3);
+        uint16_t* rowp = dbbase + (uint32_t)rc * lk32;
+        if (rc + hi * 4 < rows_left) rowp[lane_off] = f32_to_bf16(my_st != kSkip ? dbacc[i] : 0.f);
+      }
     }
+    lds_barrier();  // every reader of this item's tiles is done before the next item overwrites them
+    qb = nqb;
+    rh = nrh;
+    hh = nhh;
+    cs0 = ns0;
+    cs1 = ns1;
   }
 
-  // ---- dK, dV -----------------------------------------------------------------------
+  // ---- dK, dV: lane holds d = dt*32 + l32 for keys (i/4)*8 + hi*4 + i%4 of this wave -------------
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t key = (int64_t)kb * kBlock + wave * 16 + qg * 4 + i;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t key = (int64_t)kb0 * kBlock + wave * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
     if (key < p.lk) {
-      const int64_t off = ((bidx * p.lk + key) * p.hkv + g) * D + kl;
+      const int64_t off = ((bidx * p.lk + key) * p.hkv + g) * D + l32;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        p.dk[off + dt * 16] = f32_to_bf16(dk[dt][i] * p.scale);
-        p.dv[off + dt * 16] = f32_to_bf16(dv[dt][i]);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        p.dk[off + dt * 32] = f32_to_bf16(dk[dt][i] * p.scale);
+        p.dv[off + dt * 32] = f32_to_bf16(dv[dt][i]);
       }
     }
   }
@@ -392,7 +496,8 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.G = (int)(a.hq / a.hkv);
   p.nqb = (int)((a.lq + kBlock - 1) / kBlock);
   p.nkb = (int)((a.lk + kBlock - 1) / kBlock);
-  p.total_wg = (int)(a.b * a.hkv * p.nkb);
+  p.nkb2 = (p.nkb + 1) / 2;
+  p.total_wg = (int)(a.b * a.hkv * p.nkb2);
   p.scale = a.scale;
   p.causal = a.causal;
   if (a.d == 64)

@@ -33,6 +33,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits for
+// every outstanding global load, store and atomic of the wave (vmcnt(0)), which
+// would stall on the loads a kernel issues early to overlap them with compute.
+// Global results loaded into registers are still waited for by the compiler
+// before their first use.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // x of the partner lane l ^ 32 combined with x by max / sum (v_permlane32_swap).
 __device__ __forceinline__ float max_with_half_swap(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
