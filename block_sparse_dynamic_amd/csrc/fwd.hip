@@ -23,11 +23,14 @@
 //      lane l holds query l%32 and 16 keys of each 32-key half, so a row's
 //      64 scores live in lanes l and l^32.
 //   3. online softmax in fp32: row max over the lane pair (v_permlane32_swap),
-//      exp2 with log2(e) folded in, a lazy rescale of the running output that
-//      only fires when a row maximum grows by more than 8 nats.
+//      exp2 with log2(e) folded in; the running output is rescaled whenever a
+//      row maximum grows (the wave skips the rescale when none does), so the
+//      largest weight of a row always enters the PV product as exactly 1.0 and
+//      the bf16 rounding of P stays off the dominant term.
 //   4. O^T += V^T P^T: P^T goes from the accumulator registers straight into
 //      the B operand (the key order inside a k-step only has to agree between
-//      A and B); V^T comes out of the row-major V tile by ds_read_b64_tr_b16.
+//      A and B), as a bf16 hi part plus a bf16 lo part; V^T comes out of the
+//      row-major V tile by ds_read_b64_tr_b16.
 #include <math.h>
 
 #include "common.h"
@@ -50,7 +53,6 @@ struct FwdParams {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleNats = 8.0f;
 constexpr uint16_t kBf16NegInf = 0xFF80u;
 
 template <int D>
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       }
     }
     mx = max_with_half_swap(mx);
-    // ---- online softmax with lazy rescaling ---------------------------------
-    if (__any(mx > m_ref + kRescaleNats)) {
+    // ---- online softmax ----------------------------------------------------------
+    if (__any(mx > m_ref)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_ref - m_new) * kLog2e);
       m_ref = m_new;
@@ -212,22 +214,32 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       }
     l_part += rs;
     // ---- O^T += V^T P^T -------------------------------------------------------
+    // P goes in as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), so the weights
+    // carry ~16 significant bits: with a bf16 P alone its rounding (2^-9 relative) can
+    // move O by more than the 1e-2 the output tolerance leaves after bf16 storage.
+    // Both MFMAs read the same V^T operand.
     const int trow = (lane & 15) >> 2;                           // row offset inside a 4-row tr group
     const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;    // column inside a 32-wide tile
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        u32x4 pw;
+        u32x4 pw, lw;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(sacc[kt][hh * 8 + 2 * e], sacc[kt][hh * 8 + 2 * e + 1]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = sacc[kt][hh * 8 + 2 * e], p1 = sacc[kt][hh * 8 + 2 * e + 1];
+          pw[e] = pack_bf16x2(p0, p1);
+          lw[e] = pack_bf16x2(p0 - bf16_lo(pw[e]), p1 - bf16_hi(pw[e]));
+        }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw), pl = __builtin_bit_cast(bf16x8, lw);
         const int key0 = kt * 32 + hh * 16 + hi * 4 + trow;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const i16x4 a0 = lds_read_tr16(&sm.v[key0 * KR + dt * 32 + tcol]);
           const i16x4 a1 = lds_read_tr16(&sm.v[(key0 + 8) * KR + dt * 32 + tcol]);
-          oacc[dt] = mfma32(join_bf16x8(a0, a1), pb, oacc[dt]);
+          const bf16x8 av = join_bf16x8(a0, a1);
+          oacc[dt] = mfma32(av, pb, oacc[dt]);
+          oacc[dt] = mfma32(av, pl, oacc[dt]);
         }
       }
     }

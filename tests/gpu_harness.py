@@ -37,9 +37,18 @@ def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
 
 
+def worst_elements(o: np.ndarray, ref: np.ndarray, n: int = 5) -> str:
+    err = np.abs(o - ref).ravel()
+    idx = np.argsort(err)[::-1][:n]
+    return "; ".join(f"at {np.unravel_index(i, o.shape)} gpu {o.ravel()[i]:.6g} ref {ref.ravel()[i]:.6g} "
+                     f"err {err[i]:.3g}" for i in idx)
+
+
 def check_o(o: np.ndarray, ref: np.ndarray, what: str = "O"):
     err = np.abs(o - ref)
     bad = err > O_TOL
+    if err.size:
+        print(f"{what}: worst elements: {worst_elements(o, ref)}", flush=True)
     if bad.any():
         r = np.abs(ref[bad])
         ulp_half = np.ldexp(1.0, np.floor(np.log2(np.maximum(r, 1e-30))).astype(int) - 8)
@@ -136,3 +145,106 @@ def check_small_case(c: synth.Case, do_bits=None, verbose=True):
     if verbose:
         print(c.name, {k: f"{v:.2e}" for k, v in errs.items()})
     return dc, errs
+
+
+def _oracle_block(c, k_b, v_b, bb, r0):
+    """fp64 oracle on one sampled 64-row query block (all heads): forward and backward terms."""
+    rows = np.arange(r0, min(r0 + 64, c.lq))
+    qr = oracle.bf16_to_f64(synth.rows_of(c, synth.TAG_Q, c.hq, bb, rows))
+    dor = oracle.bf16_to_f64(synth.rows_of(c, synth.TAG_DO, c.hq, bb, rows))
+    ms, bs = [], []
+    for g in range(c.hkv):
+        m, b = synth.mask_bias_rows(c, bb, g, int(rows[0]), len(rows))
+        ms.append(m)
+        bs.append(b)
+    mask = None if ms[0] is None else np.stack(ms)
+    bias = None if bs[0] is None else oracle.bf16_to_f64(np.stack(bs))
+    o, lse = oracle.forward_rows(qr, k_b, v_b, mask, bias, c.scale_f32, c.causal, rows, c.lq)
+    bias_for_grad = bias if bias is not None else np.zeros((c.hkv, len(rows), c.lk))
+    dq, dk, dv, db = oracle.backward_rows(qr, k_b, v_b, mask, bias_for_grad, c.scale_f32, c.causal, rows, c.lq, dor)
+    valid = np.stack([oracle.valid_rows(None if mask is None else mask[g], rows, c.lq, c.lk, c.causal)
+                      for g in range(c.hkv)])
+    return dict(rows=rows, o=o, lse=lse, dq=dq, dk=dk, dv=dv, db=db, valid=valid)
+
+
+def check_full_case(c: synth.Case, n_blocks: int = 64, log=print):
+    """Parity at the workload's full size, in the launch configuration the benchmark times.
+
+    Whole block bitmap bit-exact; O, LSE, dQ, dBias on `n_blocks` seeded 64-row query
+    blocks (all heads); dK, dV from a second backward whose dO is zero outside the
+    sampled rows, which makes them exactly the sampled rows' contributions.
+    """
+    import concurrent.futures
+    import os
+
+    from threadpoolctl import threadpool_limits
+
+    import block_sparse_dynamic_amd as dma
+    from synth.device import upload_dense, upload_mask_bias
+
+    nqb, nkb = (c.lq + 63) // 64, (c.lk + 63) // 64
+    ref_state = np.empty((c.b, c.hkv, nqb, nkb), dtype=np.uint8)
+
+    def on_chunk(bb, g, r0, m, b):  # classify each uploaded chunk of rows on the CPU
+        n = min(1024, c.lq - r0)
+        blk = oracle.classify_plane_rows(None if m is None else m[:n], r0, c.lq, c.lk, c.causal)
+        nb = (n + 63) // 64
+        ref_state[bb, g, r0 // 64: r0 // 64 + nb] = blk[:nb]
+
+    log(f"[{c.name}] generating and uploading inputs", flush=True)
+    q, k, v, do = upload_dense(c)
+    mask, bias = upload_mask_bias(c, chunk_rows=1024, on_chunk=on_chunk)
+    state = torch.empty((c.b, c.hkv, nqb, nkb), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = torch.full((c.b, c.hkv, c.lq, c.lk), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.hq, c.d), dtype=torch.uint8, device="cuda")
+    log(f"[{c.name}] classify / fwd / bwd on the GPU", flush=True)
+    dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, state)
+    dma.dma_attn_fwd(q, k, v, mask, bias, state, c.scale_f32, c.causal, o, lse)
+    dma.dma_attn_bwd(q, k, v, mask, bias, state, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws)
+    torch.cuda.synchronize()
+    st = state.cpu().numpy()
+    assert np.array_equal(st, ref_state), f"{c.name}: block_state differs in {int((st != ref_state).sum())} blocks"
+    log(f"[{c.name}] block bitmap bit-exact ({int((st != 0).sum())} non-SKIP blocks)", flush=True)
+
+    sample = synth.sample_row_blocks(c, n_blocks)
+    got = []
+    for bb, r0 in sample:
+        r1 = min(r0 + 64, c.lq)
+        got.append(dict(o=f64(o[bb, r0:r1]), lse=lse[bb, :, r0:r1].cpu().numpy().astype(np.float64),
+                        dq=f64(dq[bb, r0:r1]), db=f64(dbias[bb, :, r0:r1])))
+    # second backward: dO restricted to the sampled rows
+    do_s = torch.zeros_like(do)
+    for bb, r0 in sample:
+        do_s[bb, r0:r0 + 64] = do[bb, r0:r0 + 64]
+    dma.dma_attn_bwd(q, k, v, mask, bias, state, o, do_s, lse, c.scale_f32, c.causal, dq, dk, dv, None, ws)
+    torch.cuda.synchronize()
+    dk_s, dv_s = f64(dk), f64(dv)
+    del q, k, v, do, mask, bias, dbias, do_s
+    torch.cuda.empty_cache()
+
+    log(f"[{c.name}] oracle on {len(sample)} sampled query blocks", flush=True)
+    kh, vh = oracle.bf16_to_f64(synth.k(c)), oracle.bf16_to_f64(synth.v(c))
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        refs = list(ex.map(lambda s: _oracle_block(c, kh[s[0]], vh[s[0]], s[0], s[1]), sample))
+    dk_ref = np.zeros((c.b, c.lk, c.hkv, c.d))
+    dv_ref = np.zeros((c.b, c.lk, c.hkv, c.d))
+    for (bb, _), r in zip(sample, refs):
+        dk_ref[bb] += r["dk"]
+        dv_ref[bb] += r["dv"]
+    o_err = check_o(np.concatenate([g_["o"] for g_ in got]), np.concatenate([r["o"] for r in refs]), f"{c.name} O")
+    check_lse(np.concatenate([g_["lse"] for g_ in got], axis=1), np.concatenate([r["lse"] for r in refs], axis=1))
+    errs = {"O_maxabs": o_err}
+    errs["dQ"] = check_grad(np.concatenate([g_["dq"] for g_ in got]), np.concatenate([r["dq"] for r in refs]),
+                            f"{c.name} dQ")
+    db_g = np.concatenate([g_["db"] for g_ in got], axis=1)
+    errs["dBias"] = check_grad(db_g, np.concatenate([r["db"] for r in refs], axis=1), f"{c.name} dBias")
+    valid = np.concatenate([r["valid"] for r in refs], axis=1)
+    assert np.all(db_g[~valid] == 0.0), f"{c.name}: dBias not exactly zero on invalid entries"
+    errs["dK"] = check_grad(dk_s, dk_ref, f"{c.name} dK (sampled rows)")
+    errs["dV"] = check_grad(dv_s, dv_ref, f"{c.name} dV (sampled rows)")
+    log(f"[{c.name}] parity ok {{" + ", ".join(f"{k_}: {v_:.2e}" for k_, v_ in errs.items()) + "}", flush=True)
+    return errs
