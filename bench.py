@@ -35,6 +35,11 @@ def parse():
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=16, help="query-row blocks the oracle times")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before the steps, so that a hardware counter "
+                         "pass can relate its FETCH_SIZE / WRITE_SIZE to known bytes")
+    ap.add_argument("--traffic-json", default=None,
+                    help="JSON with measured HBM bytes per launch of the dominant call (from counter passes)")
     return ap.parse_args()
 
 
@@ -134,6 +139,13 @@ def main():
         if timed is not None:
             timed[3].record(stream)
 
+    if args.calibrate_copy_mib > 0:  # one plain copy of known size, for counter calibration
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -175,8 +187,13 @@ def main():
     dom = max(phases, key=lambda k: phases[k][0])
     t_dom, f_dom, dom_name = phases[dom]
     achieved = f_dom / (t_dom * 1e-3) / 1e12
+    traffic = None
+    if args.traffic_json:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        traffic = tj.get(dom)  # bytes per launch, measured for these kernels
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom_name,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
                 "ms_per_launch": round(t_dom, 4)}
 
     line = {

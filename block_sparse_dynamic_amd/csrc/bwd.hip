@@ -94,6 +94,7 @@ struct BwdParams {
 
 constexpr int kKeys = 128;  // keys per workgroup: two classification blocks
 constexpr int kRows = 32;   // query rows per item (half a classification block)
+constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LDS at a time
 
 template <int D>
 struct BwdSmem {
@@ -106,6 +107,7 @@ struct BwdSmem {
   uint16_t b[kRows * kBRow];
   float lse2[kRows];  // lse * log2(e); +inf outside the matrix
   float dr[kRows];    // D = rowsum(dO * O)
+  uint8_t st[2][kStateChunk];  // block states of the two key blocks for a range of query blocks
   uint16_t k[kKeys * kRow];
 };
 
@@ -153,13 +155,30 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     *reinterpret_cast<u32x4*>(&sm.k[r * KR + c * 8]) = kw;
   }
 
-  // next query block with a non-SKIP half at or after `from`; rows of blocks that are SKIP in
-  // both halves get their zeros here
+  // Query blocks are walked from the last to the first: the workgroups of one XCD start
+  // together on the same rows, so their Q/dO reads share the XCD's L2.  The states of
+  // this workgroup's two key blocks are cached in LDS a chunk of query blocks at a time,
+  // so the item loop never waits on a global load of the bitmap.
+  int cache_lo = p.nqb;  // cached query blocks: [cache_lo, cache_lo + kStateChunk)
+  auto fill_cache = [&](int qb_hi) {
+    lds_barrier();  // every reader of the previous chunk is done
+    const int lo = max(0, qb_hi - kStateChunk + 1);
+    for (int t = tid; t < 2 * kStateChunk; t += 256) {
+      const int hf = t / kStateChunk, j = t % kStateChunk, qb = lo + j;
+      uint8_t v = kSkip;
+      if (qb <= qb_hi && (hf == 0 || has_kb1)) v = st_col[(int64_t)qb * p.nkb + hf];
+      sm.st[hf][j] = v;
+    }
+    lds_barrier();
+    cache_lo = lo;
+  };
+  // next query block with a non-SKIP half at or before `from`; rows of blocks that are SKIP
+  // in both halves get their zeros here
   auto next_qb = [&](int from, uint8_t& s0, uint8_t& s1) -> int {
-    for (int qb = from; qb < p.nqb; ++qb) {
-      const uint8_t* sp = st_col + (int64_t)qb * p.nkb;
-      s0 = sp[0];
-      s1 = has_kb1 ? sp[1] : kSkip;
+    for (int qb = from; qb >= 0; --qb) {
+      if (qb < cache_lo) fill_cache(qb);
+      s0 = sm.st[0][qb - cache_lo];
+      s1 = sm.st[1][qb - cache_lo];
       if (s0 != kSkip || s1 != kSkip) return qb;
       if (p.dbias != nullptr) {
         for (int task = tid; task < kBlock * (kKeys / 8); task += 256) {
@@ -170,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         }
       }
     }
-    return p.nqb;
+    return -1;
   };
 
   // Per-lane 32-bit offsets inside an item; the item's base pointers are uniform (scalar
@@ -187,54 +206,41 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     boff[n] = (uint32_t)(task / (kKeys / 8)) * (uint32_t)p.lk + (uint32_t)(task % (kKeys / 8)) * 8u;
   }
 
-  // registers that carry the next item while the current one computes
+  // Registers that carry the next item while the current one computes.  No branch
+  // surrounds a load (the compiler would wait for every outstanding memory operation,
+  // atomics included, where the paths join): lanes whose data is not needed load an
+  // in-bounds stand-in address and their value is discarded when the item is staged.
   u32x4 pq[QN], pg[QN], pb[BN], pm[BN];
-  float prow;
+  float prow_l, prow_d;
   auto prefetch = [&](int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
     const int64_t h = g * p.G + hh;
     const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
-    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
+    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);  // >= 1
     const int64_t item = ((bidx * p.lq + i0) * p.hq + h) * D;
 #pragma unroll
     for (int n = 0; n < QN; ++n) {
-      const int r = (tid + n * 256) / (D / 8);
-      u32x4 qw = {0u, 0u, 0u, 0u}, gw = {0u, 0u, 0u, 0u};
-      if (r < rows_left) {
-        qw = *reinterpret_cast<const u32x4*>(p.q + item + qoff[n]);
-        gw = *reinterpret_cast<const u32x4*>(p.dout + item + qoff[n]);
-      }
-      pq[n] = qw;
-      pg[n] = gw;
+      const int task = tid + n * 256;
+      const uint32_t off = (task / (D / 8) < rows_left) ? qoff[n] : (uint32_t)(task % (D / 8)) * 8u;  // row 0
+      pq[n] = *reinterpret_cast<const u32x4*>(p.q + item + off);
+      pg[n] = *reinterpret_cast<const u32x4*>(p.dout + item + off);
     }
     if (hh == 0) {
-      const int64_t boff0 = plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;
+      const int64_t boff0 = plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;  // (row i0, key kb0*64): in bounds
+      const uint16_t* bsrc = has_bias ? p.bias + boff0 : p.q;
+      const uint16_t* msrc = has_mask ? p.mask + boff0 : p.q;
 #pragma unroll
       for (int n = 0; n < BN; ++n) {
         const int task = tid + n * 256;
         const int r = task / (kKeys / 8), c = task % (kKeys / 8);
         const uint8_t st = (c < 8) ? s0 : s1;
         const bool in = st != kSkip && r < rows_left && (int64_t)kb0 * kBlock + c * 8 < p.lk;
-        u32x4 bw = {0u, 0u, 0u, 0u}, mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-        if (in) {
-          if (has_bias) bw = *reinterpret_cast<const u32x4*>(p.bias + boff0 + boff[n]);
-          if (has_mask && st == kPartial) mw = *reinterpret_cast<const u32x4*>(p.mask + boff0 + boff[n]);
-        }
-        pb[n] = bw;
-        pm[n] = mw;
+        pb[n] = *reinterpret_cast<const u32x4*>(bsrc + ((has_bias && in) ? boff[n] : 0u));
+        pm[n] = *reinterpret_cast<const u32x4*>(msrc + ((has_mask && in && st == kPartial) ? boff[n] : 0u));
       }
     }
-    float rv = 0.f;
-    if (tid < 2 * kRows) {
-      const int r = tid & (kRows - 1);
-      const int64_t rowbase = (bidx * p.hq + h) * p.lq + i0;
-      if (tid < kRows) {
-        rv = INFINITY;
-        if (r < rows_left) rv = p.lse[rowbase + r] * kLog2eB;
-      } else if (r < rows_left) {
-        rv = p.drow[rowbase + r];
-      }
-    }
-    prow = rv;
+    const int64_t ridx = (bidx * p.hq + h) * p.lq + i0 + min(tid & (kRows - 1), rows_left - 1);
+    prow_l = p.lse[ridx];
+    prow_d = p.drow[ridx];
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -251,12 +257,12 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
   uint8_t cs0, cs1;  // states of the current item's two key blocks
-  int qb = next_qb(0, cs0, cs1);
+  lds_barrier();        // K tile staged
+  int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
   int rh = 0, hh = 0;
-  if (qb < p.nqb) prefetch(qb, 0, 0, cs0, cs1);
-  lds_barrier();  // K tile staged
+  if (qb >= 0) prefetch(qb, 0, 0, cs0, cs1);
 
-  while (qb < p.nqb) {
+  while (qb >= 0) {
     const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
     const int64_t h = g * p.G + hh;
     const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
@@ -265,8 +271,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     for (int n = 0; n < QN; ++n) {
       const int task = tid + n * 256;
       const int r = task / (D / 8), c = task % (D / 8);
-      *reinterpret_cast<u32x4*>(&sm.q[r * KR + c * 8]) = pq[n];
-      *reinterpret_cast<u32x4*>(&sm.g[r * KR + c * 8]) = pg[n];
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&sm.q[r * KR + c * 8]) = (r < rows_left) ? pq[n] : z;
+      *reinterpret_cast<u32x4*>(&sm.g[r * KR + c * 8]) = (r < rows_left) ? pg[n] : z;
     }
     if (hh == 0) {
 #pragma unroll
@@ -276,9 +283,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         const uint8_t st = (c < 8) ? cs0 : cs1;
         const int64_t i = i0 + r, j0 = (int64_t)kb0 * kBlock + c * 8;
         const bool inside = i < p.lq && j0 < p.lk && st != kSkip;
-        u32x4 bw = pb[n];
+        u32x4 bw = has_bias ? pb[n] : u32x4{0u, 0u, 0u, 0u};
         if (st != kFull) {
-          const u32x4 mw = pm[n];
+          const u32x4 mw = has_mask ? pm[n] : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t j = j0 + 2 * e;
@@ -292,8 +299,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         *reinterpret_cast<u32x4*>(&sm.b[r * BR + c * 8]) = bw;
       }
     }
-    if (tid < kRows) sm.lse2[tid] = prow;
-    else if (tid < 2 * kRows) sm.dr[tid - kRows] = prow;
+    if (tid < kRows) sm.lse2[tid] = (tid < rows_left) ? prow_l * kLog2eB : INFINITY;
+    else if (tid < 2 * kRows) sm.dr[tid - kRows] = (tid - kRows < rows_left) ? prow_d : 0.f;
     const uint8_t my_st = half ? cs1 : cs0;
     const uint8_t s0_now = cs0, s1_now = cs1;
     lds_barrier();
@@ -306,10 +313,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       nrh = rh + 1;
       if (nrh == 2 || i0 + kRows >= p.lq) {
         nrh = 0;
-        nqb = next_qb(qb + 1, ns0, ns1);
+        nqb = next_qb(qb - 1, ns0, ns1);
       }
     }
-    if (nqb < p.nqb) prefetch(nqb, nrh, nhh, ns0, ns1);
+    if (nqb >= 0) prefetch(nqb, nrh, nhh, ns0, ns1);
 
     if (hh == 0) {
       // effective bias in the S layout: row group gi -> rows gi*8 + hi*4 .. +3 of the item
