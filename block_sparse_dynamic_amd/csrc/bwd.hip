@@ -98,8 +98,8 @@ constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LD
 
 template <int D>
 struct BwdSmem {
-  static constexpr int kRow = D + 8;        // K, Q, dO tiles [row][d]
-  static constexpr int kSRow = kRows + 8;   // dS^T [key][query]
+  static constexpr int kRow = tile_row<D>();  // K, Q, dO tiles [row][d] (tile_off layout)
+  static constexpr int kSRow = kRows;         // dS^T [key][query] (swz32 layout)
   static constexpr int kBRow = kKeys + 8;   // effective bias [query][key]
   uint16_t q[kRows * kRow];
   uint16_t g[kRows * kRow];
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     const int64_t key = (int64_t)kb0 * kBlock + r;
     u32x4 kw = {0u, 0u, 0u, 0u};
     if (key < p.lk) kw = *reinterpret_cast<const u32x4*>(p.k + ((bidx * p.lk + key) * p.hkv + g) * D + c * 8);
-    *reinterpret_cast<u32x4*>(&sm.k[r * KR + c * 8]) = kw;
+    *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = kw;
   }
 
   // Query blocks are walked from the last to the first: the workgroups of one XCD start
@@ -272,8 +272,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       const int task = tid + n * 256;
       const int r = task / (D / 8), c = task % (D / 8);
       const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.q[r * KR + c * 8]) = (r < rows_left) ? pq[n] : z;
-      *reinterpret_cast<u32x4*>(&sm.g[r * KR + c * 8]) = (r < rows_left) ? pg[n] : z;
+      *reinterpret_cast<u32x4*>(&sm.q[tile_off<D>(r, c * 8)]) = (r < rows_left) ? pq[n] : z;
+      *reinterpret_cast<u32x4*>(&sm.g[tile_off<D>(r, c * 8)]) = (r < rows_left) ? pg[n] : z;
     }
     if (hh == 0) {
 #pragma unroll
@@ -337,10 +337,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[key_loc * KR + s * 16 + hi * 8]);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[l32 * KR + s * 16 + hi * 8]);
+      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[tile_off<D>(key_loc, s * 16 + hi * 8)]);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[tile_off<D>(l32, s * 16 + hi * 8)]);
       sacc = mfma32(aq, kbs, sacc);
-      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[l32 * KR + s * 16 + hi * 8]);
+      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[tile_off<D>(l32, s * 16 + hi * 8)]);
       pacc = mfma32(ag, vreg[s], pacc);
     }
     // ---- P = exp(S - lse) on valid entries, dS = P (dP - D) -----------------------------
@@ -373,11 +373,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       const int r0 = ks * 16 + hi * 4 + trow;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const i16x4 g0 = lds_read_tr16(&sm.g[r0 * KR + dt * 32 + tcol]);
-        const i16x4 g1 = lds_read_tr16(&sm.g[(r0 + 8) * KR + dt * 32 + tcol]);
+        const i16x4 g0 = lds_read_tr16(&sm.g[tile_off<D>(r0, dt * 32 + tcol)]);
+        const i16x4 g1 = lds_read_tr16(&sm.g[tile_off<D>(r0 + 8, dt * 32 + tcol)]);
         dv[dt] = mfma32(ap, join_bf16x8(g0, g1), dv[dt]);
-        const i16x4 q0 = lds_read_tr16(&sm.q[r0 * KR + dt * 32 + tcol]);
-        const i16x4 q1 = lds_read_tr16(&sm.q[(r0 + 8) * KR + dt * 32 + tcol]);
+        const i16x4 q0 = lds_read_tr16(&sm.q[tile_off<D>(r0, dt * 32 + tcol)]);
+        const i16x4 q1 = lds_read_tr16(&sm.q[tile_off<D>(r0 + 8, dt * 32 + tcol)]);
         dk[dt] = mfma32(as, join_bf16x8(q0, q1), dk[dt]);
       }
     }
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       u32x2 w2;
       w2[0] = pack_bf16x2(pacc[gi * 4 + 0], pacc[gi * 4 + 1]);
       w2[1] = pack_bf16x2(pacc[gi * 4 + 2], pacc[gi * 4 + 3]);
-      *reinterpret_cast<u32x2*>(&sm.s[key_loc * SR + gi * 8 + hi * 4]) = w2;
+      *reinterpret_cast<u32x2*>(&sm.s[swz32(key_loc, gi * 8 + hi * 4)]) = w2;
     }
     lds_barrier();
 
@@ -401,10 +401,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       f32x16 c = f32x16{};
       for (int ks = ks_lo; ks < ks_hi; ++ks) {
         const int r0 = ks * 16 + hi * 8 + trow;
-        const i16x4 k0 = lds_read_tr16(&sm.k[r0 * KR + dtile * 32 + tcol]);
-        const i16x4 k1 = lds_read_tr16(&sm.k[(r0 + 4) * KR + dtile * 32 + tcol]);
-        const i16x4 a0 = lds_read_tr16(&sm.s[r0 * SR + tcol]);
-        const i16x4 a1 = lds_read_tr16(&sm.s[(r0 + 4) * SR + tcol]);
+        const i16x4 k0 = lds_read_tr16(&sm.k[tile_off<D>(r0, dtile * 32 + tcol)]);
+        const i16x4 k1 = lds_read_tr16(&sm.k[tile_off<D>(r0 + 4, dtile * 32 + tcol)]);
+        const i16x4 a0 = lds_read_tr16(&sm.s[swz32(r0, tcol)]);
+        const i16x4 a1 = lds_read_tr16(&sm.s[swz32(r0 + 4, tcol)]);
         c = mfma32(join_bf16x8(a0, a1), join_bf16x8(k0, k1), c);
       }
       if (ks_lo < ks_hi) {

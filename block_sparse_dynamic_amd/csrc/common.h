@@ -33,6 +33,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// LDS tile layouts.  A [rows][128] bf16 tile stores the 16-byte chunk c of row r at chunk
+// c ^ (4*(r%4) + (r/4)%4), rows unpadded.  With that, a 128-bit operand read (16 lanes on
+// 16 consecutive rows, one chunk each) and a transposing 64-bit read (4 consecutive rows x
+// 32 bytes per 16-lane group) both touch every bank once per cycle.  Narrower tiles keep
+// an 8-element row pad.
+__device__ __forceinline__ int swz128(int row, int col) {
+  const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+  return (row << 7) | ((((col >> 3) ^ f) << 3) | (col & 7));
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  if constexpr (D == 128) {
+    return swz128(row, col);
+  } else {
+    return row * (D + 8) + col;
+  }
+}
+template <int D>
+constexpr int tile_row() {
+  return D == 128 ? 128 : D + 8;
+}
+// A [rows][32] bf16 tile stores the 8-byte unit u of row r at unit u ^ ((r/4)%8): conflict
+// free for 8-byte writes of 32 consecutive rows and for transposing reads of 4-row groups.
+__device__ __forceinline__ int swz32(int row, int col) {
+  return (row << 5) | ((((col >> 2) ^ ((row >> 2) & 7)) << 2) | (col & 3));
+}
+
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits for
 // every outstanding global load, store and atomic of the wave (vmcnt(0)), which
 // would stall on the loads a kernel issues early to overlap them with compute.

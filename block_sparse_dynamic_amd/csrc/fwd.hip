@@ -53,15 +53,17 @@ struct FwdParams {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kStateChunkF = 1024;  // key blocks whose states are cached in LDS at a time
 constexpr uint16_t kBf16NegInf = 0xFF80u;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int kRow = D + 8;  // padded row (elements) of the K and V tiles
+  static constexpr int kRow = tile_row<D>();  // row (elements) of the K and V tiles (tile_off layout)
   static constexpr int kBRow = kBlock + 8;
   uint16_t k[kBlock * kRow];
   uint16_t v[kBlock * kRow];
   uint16_t b[kBlock * kBRow];  // effective bias, bf16 bits
+  uint8_t st[kStateChunkF];    // block states of this query block's row, a chunk at a time
 };
 
 template <int D, int HC>
@@ -110,33 +112,92 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   const int64_t plane_off = (int64_t)plane * p.lq * p.lk;
   const bool has_bias = p.bias != nullptr, has_mask = p.mask != nullptr;
 
-  for (int kb = 0; kb < p.nkb; ++kb) {
-    const uint8_t st = st_row[kb];
-    if (st == kSkip) continue;
-    const bool full = (st == kFull);
-    __syncthreads();  // the previous block's LDS reads are done
-    // ---- stage K, V (row-major) and the effective bias -------------------
-    for (int task = tid; task < kBlock * (D / 8); task += NT) {
+  // Block states of this row are cached in LDS a chunk at a time, so skipping a SKIP block
+  // costs an LDS read instead of a dependent global load.
+  int cache_lo = -kStateChunkF;  // cached key blocks: [cache_lo, cache_lo + kStateChunkF)
+  auto next_kb = [&](int from) -> int {
+    for (int kb = from; kb < p.nkb; ++kb) {
+      if (kb >= cache_lo + kStateChunkF) {
+        lds_barrier();  // every reader of the previous chunk is done
+        for (int t = tid; t < kStateChunkF; t += NT) sm.st[t] = (kb + t < p.nkb) ? st_row[kb + t] : kSkip;
+        lds_barrier();
+        cache_lo = kb;
+      }
+      if (sm.st[kb - cache_lo] != kSkip) return kb;
+    }
+    return p.nkb;
+  };
+
+  // Registers that carry the next non-SKIP block's K, V, bias and mask while the current
+  // block computes.  Every load is unconditional: lanes whose data is not needed (keys past
+  // lk, rows past lq, no bias, no mask or a FULL block's mask) load an in-bounds stand-in
+  // address and the value is discarded at staging, so no branch around a load makes the
+  // compiler wait for the whole prefetch.
+  constexpr int KN = kBlock * (D / 8) / NT, BN = kBlock * 8 / NT;
+  u32x4 pk[KN], pv[KN], pb[BN], pm[BN];
+  auto prefetch = [&](int kb, uint8_t st) {
+#pragma unroll
+    for (int n = 0; n < KN; ++n) {
+      const int task = tid + n * NT;
       const int r = task / (D / 8), c = task % (D / 8);
       const int64_t key = (int64_t)kb * kBlock + r;
-      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (key < p.lk) {
-        kw = *reinterpret_cast<const u32x4*>(kbase + key * p.hkv * D + c * 8);
-        vw = *reinterpret_cast<const u32x4*>(vbase + key * p.hkv * D + c * 8);
-      }
-      *reinterpret_cast<u32x4*>(&sm.k[r * KR + c * 8]) = kw;
-      *reinterpret_cast<u32x4*>(&sm.v[r * KR + c * 8]) = vw;
+      const int64_t off = (key < p.lk ? key : (int64_t)kb * kBlock) * p.hkv * D + c * 8;  // key kb*64 < lk
+      pk[n] = *reinterpret_cast<const u32x4*>(kbase + off);
+      pv[n] = *reinterpret_cast<const u32x4*>(vbase + off);
+    }
+    const int64_t corner = (int64_t)qb * kBlock * p.lk + (int64_t)kb * kBlock;  // (qb*64, kb*64): in bounds
+#pragma unroll
+    for (int n = 0; n < BN; ++n) {
+      const int task = tid + n * NT;
+      const int r = task >> 3, c = task & 7;
+      const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
+      const int64_t off = (i < p.lq && j0 < p.lk) ? i * p.lk + j0 : corner;
+      pb[n] = *reinterpret_cast<const u32x4*>(has_bias ? p.bias + plane_off + off : p.q);
+      pm[n] = *reinterpret_cast<const u32x4*>((has_mask && st != kFull) ? p.mask + plane_off + off : p.q);
+    }
+  };
+
+  // Per-lane LDS element offsets of the K operand reads and the transposing V reads; the
+  // loop adds compile-time row offsets only.  With the swizzled 128-wide layout the XOR of
+  // the chunk index factors into these per-lane terms (equal to tile_off<D> element for element).
+  const int l32 = lane & 31;
+  const int trow = (lane & 15) >> 2;                           // row offset inside a 4-row tr group
+  const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;    // column inside a 32-wide tile
+  int koff[D / 16], voff0[D / 32], voff1[D / 32];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) koff[s] = tile_off<D>(l32, s * 16 + hi * 8);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    voff0[dt] = tile_off<D>(hi * 4 + trow, dt * 32 + tcol);
+    voff1[dt] = tile_off<D>(hi * 4 + trow + 8, dt * 32 + tcol);
+  }
+
+  int kb = next_kb(0);
+  uint8_t st = kb < p.nkb ? sm.st[kb - cache_lo] : kSkip;
+  if (kb < p.nkb) prefetch(kb, st);
+  while (kb < p.nkb) {
+    const bool full = (st == kFull);
+    lds_barrier();  // the previous block's LDS reads are done
+    // ---- stage K, V (row-major) and the effective bias -------------------
+#pragma unroll
+    for (int n = 0; n < KN; ++n) {
+      const int task = tid + n * NT;
+      const int r = task / (D / 8), c = task % (D / 8);
+      const bool in = (int64_t)kb * kBlock + r < p.lk;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = in ? pk[n] : z;
+      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = in ? pv[n] : z;
     }
     if (has_bias || !full) {
-      for (int task = tid; task < kBlock * 8; task += NT) {
+#pragma unroll
+      for (int n = 0; n < BN; ++n) {
+        const int task = tid + n * NT;
         const int r = task >> 3, c = task & 7;
         const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
-        u32x4 bw = {0u, 0u, 0u, 0u};
         const bool inside = i < p.lq && j0 < p.lk;
-        if (has_bias && inside) bw = *reinterpret_cast<const u32x4*>(p.bias + plane_off + i * p.lk + j0);
+        u32x4 bw = (has_bias && inside) ? pb[n] : u32x4{0u, 0u, 0u, 0u};
         if (!full) {
-          u32x4 mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-          if (has_mask && inside) mw = *reinterpret_cast<const u32x4*>(p.mask + plane_off + i * p.lk + j0);
+          const u32x4 mw = has_mask ? pm[n] : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t j = j0 + 2 * e;
@@ -150,7 +211,11 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         *reinterpret_cast<u32x4*>(&sm.b[r * BR + c * 8]) = bw;
       }
     }
-    __syncthreads();
+    lds_barrier();
+    // ---- start loading the next non-SKIP block ------------------------------
+    const int kb_next = next_kb(kb + 1);
+    const uint8_t st_next = kb_next < p.nkb ? sm.st[kb_next - cache_lo] : kSkip;
+    if (kb_next < p.nkb) prefetch(kb_next, st_next);
 
     // ---- S^T = K Q^T --------------------------------------------------------
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -158,7 +223,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[(kt * 32 + (lane & 31)) * KR + s * 16 + hi * 8]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[koff[s] + kt * 32 * KR]);
         sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
       }
     }
@@ -218,8 +283,6 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     // carry ~16 significant bits: with a bf16 P alone its rounding (2^-9 relative) can
     // move O by more than the 1e-2 the output tolerance leaves after bf16 storage.
     // Both MFMAs read the same V^T operand.
-    const int trow = (lane & 15) >> 2;                           // row offset inside a 4-row tr group
-    const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;    // column inside a 32-wide tile
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -231,18 +294,20 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
           pw[e] = pack_bf16x2(p0, p1);
           lw[e] = pack_bf16x2(p0 - bf16_lo(pw[e]), p1 - bf16_hi(pw[e]));
         }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw), pl = __builtin_bit_cast(bf16x8, lw);
-        const int key0 = kt * 32 + hh * 16 + hi * 4 + trow;
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, pw), pl = __builtin_bit_cast(bf16x8, lw);
+        const int rbase = (kt * 32 + hh * 16) * KR;  // rows of this k-step, a compile-time offset
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const i16x4 a0 = lds_read_tr16(&sm.v[key0 * KR + dt * 32 + tcol]);
-          const i16x4 a1 = lds_read_tr16(&sm.v[(key0 + 8) * KR + dt * 32 + tcol]);
+          const i16x4 a0 = lds_read_tr16(&sm.v[voff0[dt] + rbase]);
+          const i16x4 a1 = lds_read_tr16(&sm.v[voff1[dt] + rbase]);
           const bf16x8 av = join_bf16x8(a0, a1);
-          oacc[dt] = mfma32(av, pb, oacc[dt]);
+          oacc[dt] = mfma32(av, ph, oacc[dt]);
           oacc[dt] = mfma32(av, pl, oacc[dt]);
         }
       }
     }
+    kb = kb_next;
+    st = st_next;
   }
 
   // ---- epilogue -----------------------------------------------------------------
