@@ -255,6 +255,32 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   // tr-read addressing: inside a 16-lane group, lane s points at row +s/4, column +4(s%4)
   const int trow = (lane & 15) >> 2;
   const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  // Per-lane LDS element offsets, computed once; the loops add compile-time row offsets
+  // only.  The swizzle's XOR term depends on the row modulo 16 (128-wide tiles) or 32 (the
+  // dS^T tile), so adding a multiple of that many rows is a plain add.
+  constexpr int DT = D / 32, WPT = 4 / DT, KCH = 8 / WPT;  // dQ: column tiles, waves per tile, k-steps per wave
+  static_assert(KCH % 2 == 0, "dQ k-steps per wave must pair up the 32-row halves of dS^T");
+  const int dtile = wave % DT, kpart = wave / DT;
+  int aoff[D / 16];                  // S/dP operand rows: l32 (+ wave*32 for K)
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) aoff[s] = tile_off<D>(l32, s * 16 + hi * 8);
+  int gq0[D / 32], gq1[D / 32];      // dV/dK transposing reads: rows hi*4 + trow (+8), + ks*16
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    gq0[dt] = tile_off<D>(hi * 4 + trow, dt * 32 + tcol);
+    gq1[dt] = tile_off<D>(hi * 4 + trow + 8, dt * 32 + tcol);
+  }
+  const int kq0 = tile_off<D>(hi * 8 + trow, dtile * 32 + tcol);      // dQ, K rows (+ ks*16)
+  const int kq1 = tile_off<D>(hi * 8 + trow + 4, dtile * 32 + tcol);
+  int sq[2][2];                      // dQ, dS^T rows (ks%2)*16 + hi*8 + trow (+4), + (ks/2)*32
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    sq[par][0] = swz32(par * 16 + hi * 8 + trow, tcol);
+    sq[par][1] = swz32(par * 16 + hi * 8 + trow + 4, tcol);
+  }
+  int sw[4];                         // dS^T writes: row l32 (+ wave*32)
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) sw[gi] = swz32(l32, gi * 8 + hi * 4);
 
   uint8_t cs0, cs1;  // states of the current item's two key blocks
   lds_barrier();        // K tile staged
@@ -302,7 +328,6 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     if (tid < kRows) sm.lse2[tid] = (tid < rows_left) ? prow_l * kLog2eB : INFINITY;
     else if (tid < 2 * kRows) sm.dr[tid - kRows] = (tid - kRows < rows_left) ? prow_d : 0.f;
     const uint8_t my_st = half ? cs1 : cs0;
-    const uint8_t s0_now = cs0, s1_now = cs1;
     lds_barrier();
 
     // ---- start loading the next item ------------------------------------------------
@@ -337,10 +362,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[tile_off<D>(key_loc, s * 16 + hi * 8)]);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[tile_off<D>(l32, s * 16 + hi * 8)]);
+      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[aoff[s] + wave * 32 * KR]);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[aoff[s]]);
       sacc = mfma32(aq, kbs, sacc);
-      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[tile_off<D>(l32, s * 16 + hi * 8)]);
+      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[aoff[s]]);
       pacc = mfma32(ag, vreg[s], pacc);
     }
     // ---- P = exp(S - lse) on valid entries, dS = P (dP - D) -----------------------------
@@ -354,8 +379,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e) {
         const int i = gi * 4 + e;
         const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale2, fmaf(bb[e], kLog2eB, -l2[e])));
-        const float ds = pv * (pacc[i] - dd[e]);
-        sacc[i] = pv;
+        // a SKIP half gives exactly zero whatever its K/V hold, so dQ can take all 128 keys
+        const float ds = (my_st != kSkip) ? pv * (pacc[i] - dd[e]) : 0.f;
+        sacc[i] = (my_st != kSkip) ? pv : 0.f;
         pacc[i] = ds;
         dbacc[i] += ds;
       }
@@ -370,14 +396,14 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         sw[e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
       }
       const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw);
-      const int r0 = ks * 16 + hi * 4 + trow;
+      const int rk = ks * 16 * KR;  // this k-step's rows: a compile-time offset
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const i16x4 g0 = lds_read_tr16(&sm.g[tile_off<D>(r0, dt * 32 + tcol)]);
-        const i16x4 g1 = lds_read_tr16(&sm.g[tile_off<D>(r0 + 8, dt * 32 + tcol)]);
+        const i16x4 g0 = lds_read_tr16(&sm.g[gq0[dt] + rk]);
+        const i16x4 g1 = lds_read_tr16(&sm.g[gq1[dt] + rk]);
         dv[dt] = mfma32(ap, join_bf16x8(g0, g1), dv[dt]);
-        const i16x4 q0 = lds_read_tr16(&sm.q[tile_off<D>(r0, dt * 32 + tcol)]);
-        const i16x4 q1 = lds_read_tr16(&sm.q[tile_off<D>(r0 + 8, dt * 32 + tcol)]);
+        const i16x4 q0 = lds_read_tr16(&sm.q[gq0[dt] + rk]);
+        const i16x4 q1 = lds_read_tr16(&sm.q[gq1[dt] + rk]);
         dk[dt] = mfma32(as, join_bf16x8(q0, q1), dk[dt]);
       }
     }
@@ -387,27 +413,28 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       u32x2 w2;
       w2[0] = pack_bf16x2(pacc[gi * 4 + 0], pacc[gi * 4 + 1]);
       w2[1] = pack_bf16x2(pacc[gi * 4 + 2], pacc[gi * 4 + 3]);
-      *reinterpret_cast<u32x2*>(&sm.s[swz32(key_loc, gi * 8 + hi * 4)]) = w2;
+      *reinterpret_cast<u32x2*>(&sm.s[sw[gi] + wave * 32 * SR]) = w2;
     }
     lds_barrier();
 
-    // ---- dQ[:, dtile*32 .. +31] += scale * dS K over the non-SKIP key halves ------------------
-    // D/32 column tiles of dQ; with d = 64 two waves share a tile and split the keys.
+    // ---- dQ[:, dtile*32 .. +31] += scale * dS K over the 128 keys ----------------------------
+    // D/32 column tiles of dQ; with d = 64 two waves share a tile and split the keys.  A SKIP
+    // half's dS rows are zero, so running every k-step adds nothing there and keeps the loop
+    // straight-line.
     {
-      constexpr int DT = D / 32, WPT = 4 / DT, KCH = 8 / WPT;
-      const int dtile = wave % DT, kpart = wave / DT;
-      const int ks_lo = max((s0_now != kSkip) ? 0 : 4, kpart * KCH);
-      const int ks_hi = min((s1_now != kSkip) ? 8 : 4, (kpart + 1) * KCH);
       f32x16 c = f32x16{};
-      for (int ks = ks_lo; ks < ks_hi; ++ks) {
-        const int r0 = ks * 16 + hi * 8 + trow;
-        const i16x4 k0 = lds_read_tr16(&sm.k[tile_off<D>(r0, dtile * 32 + tcol)]);
-        const i16x4 k1 = lds_read_tr16(&sm.k[tile_off<D>(r0 + 4, dtile * 32 + tcol)]);
-        const i16x4 a0 = lds_read_tr16(&sm.s[swz32(r0, tcol)]);
-        const i16x4 a1 = lds_read_tr16(&sm.s[swz32(r0 + 4, tcol)]);
+#pragma unroll
+      for (int kk = 0; kk < KCH; ++kk) {
+        const int ks = kpart * KCH + kk;
+        const int kofs = ks * 16 * KR, sofs = (ks >> 1) * 32 * SR;
+        const int par = kk & 1;  // == ks & 1, since KCH is even
+        const i16x4 k0 = lds_read_tr16(&sm.k[kq0 + kofs]);
+        const i16x4 k1 = lds_read_tr16(&sm.k[kq1 + kofs]);
+        const i16x4 a0 = lds_read_tr16(&sm.s[sq[par][0] + sofs]);
+        const i16x4 a1 = lds_read_tr16(&sm.s[sq[par][1] + sofs]);
         c = mfma32(join_bf16x8(a0, a1), join_bf16x8(k0, k1), c);
       }
-      if (ks_lo < ks_hi) {
+      {
         float* dqbase = p.dq_acc + ((bidx * p.lq + i0) * p.hq + h) * D + dtile * 32;
         uint32_t rstride = (uint32_t)(p.hq * D);
         asm volatile("" : "+s"(rstride));  // keep the row offsets below inside the loop (not hoisted)
