@@ -112,6 +112,8 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
       !aligned_or_null(dbias) || !aligned16(workspace))
     return DMA_ERR_INVALID_ARGUMENT;
   if (dbias && lk % 8 != 0) return DMA_ERR_INVALID_ARGUMENT;
+  // per-row byte ranges of the dQ accumulation and of dbias must stay within 32-bit offsets
+  if (lk > (int64_t(1) << 24) || hq * d > (int64_t(1) << 20)) return DMA_ERR_UNSUPPORTED;
   if (workspace_bytes < dma_attn_bwd_workspace_size(b, lq, hq, d)) return DMA_ERR_WORKSPACE_TOO_SMALL;
   dma::AttnArgs a = {};
   a.q = q;

@@ -97,7 +97,7 @@ constexpr int kRows = 32;   // query rows per item (half a classification block)
 constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LDS at a time
 
 template <int D>
-struct BwdSmem {
+struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay single 16-byte LDS accesses
   static constexpr int kRow = tile_row<D>();  // K, Q, dO tiles [row][d] (tile_off layout)
   static constexpr int kSRow = kRows;         // dS^T [key][query] (swz32 layout)
   static constexpr int kBRow = kKeys + 8;   // effective bias [query][key]
@@ -124,7 +124,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const int kb0 = 2 * KB;
   const bool has_kb1 = kb0 + 1 < p.nkb;
   const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wave and the block states below are uniform across a wave; readfirstlane tells the compiler
+  // so, which keeps the loop control and the buffer resources in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int half = wave >> 1;           // which 64-key classification block this wave is in
   const int key_loc = wave * 32 + l32;  // key of this lane inside the 128
@@ -135,6 +137,20 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const float scale2 = p.scale * kLog2eB;
   const uint8_t* st_col = p.state + (int64_t)plane * p.nqb * p.nkb + kb0;  // + qb * nkb (+1)
 
+  // Is each of the two key blocks non-SKIP for some query block?  The K and V rows of a key
+  // block that is SKIP everywhere are never read: they stay zero here (the dQ product runs
+  // over both halves, and 0 * K must not meet whatever such rows hold).
+  bool live[2];
+  {
+    int any0 = 0, any1 = 0;
+    for (int qb = tid; qb < p.nqb; qb += 256) {
+      any0 |= st_col[(int64_t)qb * p.nkb] != kSkip;
+      if (has_kb1) any1 |= st_col[(int64_t)qb * p.nkb + 1] != kSkip;
+    }
+    live[0] = __syncthreads_or(any0) != 0;
+    live[1] = __syncthreads_or(any1) != 0;
+  }
+
   // this lane's key row of V: B operand of dP = dO V^T (d = s*16 + hi*8 ..); the K operand of
   // S = Q K^T is read from the staged K tile
   bf16x8 vreg[D / 16];
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       u32x4 vw = {0u, 0u, 0u, 0u};
-      if (key_abs < p.lk) vw = *reinterpret_cast<const u32x4*>(p.v + off + s * 16);
+      if (key_abs < p.lk && live[half]) vw = *reinterpret_cast<const u32x4*>(p.v + off + s * 16);
       vreg[s] = __builtin_bit_cast(bf16x8, vw);
     }
   }
@@ -151,7 +167,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     const int r = task / (D / 8), c = task % (D / 8);
     const int64_t key = (int64_t)kb0 * kBlock + r;
     u32x4 kw = {0u, 0u, 0u, 0u};
-    if (key < p.lk) kw = *reinterpret_cast<const u32x4*>(p.k + ((bidx * p.lk + key) * p.hkv + g) * D + c * 8);
+    if (key < p.lk && live[r >> 6]) kw = *reinterpret_cast<const u32x4*>(p.k + ((bidx * p.lk + key) * p.hkv + g) * D + c * 8);
     *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = kw;
   }
 
@@ -177,8 +193,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   auto next_qb = [&](int from, uint8_t& s0, uint8_t& s1) -> int {
     for (int qb = from; qb >= 0; --qb) {
       if (qb < cache_lo) fill_cache(qb);
-      s0 = sm.st[0][qb - cache_lo];
-      s1 = sm.st[1][qb - cache_lo];
+      s0 = (uint8_t)__builtin_amdgcn_readfirstlane(sm.st[0][qb - cache_lo]);
+      s1 = (uint8_t)__builtin_amdgcn_readfirstlane(sm.st[1][qb - cache_lo]);
       if (s0 != kSkip || s1 != kSkip) return qb;
       if (p.dbias != nullptr) {
         for (int task = tid; task < kBlock * (kKeys / 8); task += 256) {
@@ -435,30 +451,35 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         c = mfma32(join_bf16x8(a0, a1), join_bf16x8(k0, k1), c);
       }
       {
-        float* dqbase = p.dq_acc + ((bidx * p.lq + i0) * p.hq + h) * D + dtile * 32;
-        uint32_t rstride = (uint32_t)(p.hq * D);
-        asm volatile("" : "+s"(rstride));  // keep the row offsets below inside the loop (not hoisted)
-        const uint32_t lane_off = (uint32_t)(hi * 4) * rstride + (uint32_t)l32;
+        // rows of the item at or past rows_left fall outside the resource and are dropped
+        const uint32_t rbytes = (uint32_t)(p.hq * D) * 4u;
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(p.dq_acc + ((bidx * p.lq + i0) * p.hq + h) * D + dtile * 32, (uint32_t)rows_left * rbytes);
+        uint32_t rb = rbytes;
+        asm volatile("" : "+s"(rb));  // keep the row offsets below inside the loop (not hoisted)
+        const uint32_t lane_off = (uint32_t)(hi * 4) * rb + (uint32_t)l32 * 4u;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int rc = (i >> 2) * 8 + (i & 3);  // row minus this lane's hi*4
-          float* rowp = dqbase + (uint32_t)rc * rstride;
-          if (rc + hi * 4 < rows_left) atomicAdd(rowp + lane_off, c[i] * p.scale);
+          const uint32_t rc = (i >> 2) * 8 + (i & 3);  // row minus this lane's hi*4
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(c[i] * p.scale, r, lane_off + rc * rb, 0, 0);
         }
       }
     }
 
     // ---- dBias of the item's rows, summed over the group: store after the last head -------------
-    if (hh == p.G - 1 && p.dbias != nullptr && key_abs < p.lk) {
-      uint16_t* dbbase = p.dbias + plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;
-      uint32_t lk32 = (uint32_t)p.lk;
-      asm volatile("" : "+s"(lk32));  // keep the row offsets below inside the loop (not hoisted)
-      const uint32_t lane_off = (uint32_t)(hi * 4) * lk32 + (uint32_t)key_loc;
+    if (hh == p.G - 1 && p.dbias != nullptr) {
+      // rows at or past rows_left fall outside the resource; a lane whose key is past lk
+      // takes an offset beyond it, so its stores are dropped as well
+      const uint32_t rbytes = (uint32_t)p.lk * 2u;
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(p.dbias + plane_off + i0 * p.lk + (int64_t)kb0 * kBlock, (uint32_t)rows_left * rbytes);
+      uint32_t rb = rbytes;
+      asm volatile("" : "+s"(rb));  // keep the row offsets below inside the loop (not hoisted)
+      const uint32_t lane_off = (key_abs < p.lk) ? (uint32_t)(hi * 4) * rb + (uint32_t)key_loc * 2u : kOutOfRange;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int rc = (i >> 2) * 8 + (i & 3);
-        uint16_t* rowp = dbbase + (uint32_t)rc * lk32;
-        if (rc + hi * 4 < rows_left) rowp[lane_off] = f32_to_bf16(my_st != kSkip ? dbacc[i] : 0.f);
+        const uint32_t rc = (i >> 2) * 8 + (i & 3);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dbacc[i]), r, lane_off + rc * rb, 0, 0);
       }
     }
     lds_barrier();  // every reader of this item's tiles is done before the next item overwrites them

@@ -17,6 +17,15 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Raw buffer resource over [base, base + bytes).  A buffer access whose per-lane offset (plus
+// its immediate offset) is at or past `bytes` is dropped by the hardware: stores and atomics
+// write nothing.  Word 3 is the data-format word of the gfx9 family.  The per-lane offset
+// must carry every part of the address that needs the check; the scalar offset is not checked.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past any range these kernels make
+
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

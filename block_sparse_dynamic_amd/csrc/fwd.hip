@@ -57,7 +57,7 @@ constexpr int kStateChunkF = 1024;  // key blocks whose states are cached in LDS
 constexpr uint16_t kBf16NegInf = 0xFF80u;
 
 template <int D>
-struct FwdSmem {
+struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay single 16-byte LDS accesses
   static constexpr int kRow = tile_row<D>();  // row (elements) of the K and V tiles (tile_off layout)
   static constexpr int kBRow = kBlock + 8;
   uint16_t k[kBlock * kRow];

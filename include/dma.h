@@ -125,7 +125,8 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t hq, int64_t d)
  *               NULL: then the bias gradient is not produced.
  *   workspace   device scratch of at least dma_attn_bwd_workspace_size() bytes,
  *               16-byte aligned, owned by the caller, contents on entry ignored
- * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL.
+ * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL, and
+ *   DMA_ERR_UNSUPPORTED for lk > 2^24 or hq * d > 2^20 (32-bit row offsets).
  */
 int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
                  const uint8_t* block_state, const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b,

@@ -37,6 +37,13 @@ def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
 
 
+def within_one_bf16_ulp(a: np.ndarray, b: np.ndarray) -> bool:
+    """Element-wise |a - b| <= one bf16 unit in the last place of max(|a|, |b|) (a, b: bf16 values)."""
+    m = np.maximum(np.abs(a), np.abs(b))
+    ulp = np.where(m > 0, np.exp2(np.floor(np.log2(np.where(m > 0, m, 1.0))) - 7), 0.0)
+    return bool(np.all(np.abs(a - b) <= ulp))
+
+
 def worst_elements(o: np.ndarray, ref: np.ndarray, n: int = 5) -> str:
     err = np.abs(o - ref).ravel()
     idx = np.argsort(err)[::-1][:n]

@@ -101,6 +101,7 @@ def test_fwd_ragged_lk_allowed_without_mask_and_bias(lib):
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID), (dict(dv=None), INVALID),
     (dict(ws=None), INVALID), (dict(lse=P + 4), INVALID), (dict(db=P + 2), INVALID),
     (dict(wsb=1000), WS_SMALL), (dict(d=80), UNSUPPORTED),
+    (dict(lk=(1 << 24) + 64), UNSUPPORTED), (dict(hq=16384, hkv=1024), UNSUPPORTED),
 ])
 def test_bwd_rejects(lib, kw, want):
     assert bwd(lib, **kw) == want

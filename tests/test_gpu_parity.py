@@ -79,7 +79,9 @@ def test_autograd_wrapper_matches_oracle():
 
 
 def test_repeatable():
-    """Two runs: O, LSE, dK, dV, dBias bit-identical (one writer per element); dQ within 1e-6 (fp32 atomics)."""
+    """Two runs: O, LSE, dK, dV, dBias bit-identical (one writer per element).  dQ is summed with
+    fp32 atomics in whatever order the workgroups reach them, so its bf16 rounding may differ by
+    one unit in the last place."""
     import gpu_harness as H
 
     c = Case("repeat", 24, 1, 512, 512, 8, 2, 128, True, "topk", 200)
@@ -93,19 +95,30 @@ def test_repeatable():
         outs.append([H.bits(t) for t in (dc.o, dc.dk, dc.dv, dc.dbias)] + [dc.lse.cpu().numpy(), H.f64(dc.dq)])
     for a, b in zip(outs[0][:5], outs[1][:5]):
         assert np.array_equal(a, b)
-    assert H.rel_l2(outs[0][5], outs[1][5]) < 1e-6
+    assert H.within_one_bf16_ulp(outs[0][5], outs[1][5])
+    assert H.rel_l2(outs[0][5], outs[1][5]) < 1e-4
 
 
 def test_skipped_tiles_do_not_leak():
-    """K/V rows and bias of SKIP blocks set to NaN change nothing (they are never loaded)."""
+    """K/V rows and bias of SKIP blocks set to NaN change neither the forward nor the backward:
+    the forward never loads them, the backward never lets them meet a nonzero weight."""
     import gpu_harness as H
 
     c = Case("skip_nan", 25, 1, 256, 256, 4, 2, 128, False, "blocks")
     dc = H.DeviceCase(c)
+    # carve out one key block per plane that no query attends, each paired (same 128-key
+    # workgroup of the backward) with a key block that stays live
+    mask2 = dc.mask_h.copy()
+    mask2[0, 0, :, 64:128] = 0
+    mask2[0, 1, :, 128:192] = 0
+    dc.mask_h, dc.mask = mask2, H.to_dev(mask2)
     dc.classify()
     dc.forward()
+    dc.backward()
     torch.cuda.synchronize()
     o1 = H.bits(dc.o)
+    g1 = [H.bits(t) for t in (dc.dk, dc.dv, dc.dbias)]
+    dq1 = H.f64(dc.dq)
     st = dc.state.cpu().numpy()
     bias2 = dc.bias_h.copy()
     for bb in range(c.b):
@@ -116,12 +129,22 @@ def test_skipped_tiles_do_not_leak():
                         bias2[bb, g, qb * 64:(qb + 1) * 64, kb * 64:(kb + 1) * 64] = 0x7FC0
     # a key block that is SKIP for every query block of a plane: poison its K and V rows
     k2, v2 = dc.k_h.copy(), dc.v_h.copy()
+    poisoned = 0
     for kb in range(st.shape[3]):
         for g in range(c.hkv):
             if np.all(st[0, g, :, kb] == oracle.SKIP):
+                poisoned += 1
                 k2[0, kb * 64:(kb + 1) * 64, g] = 0x7FC0
                 v2[0, kb * 64:(kb + 1) * 64, g] = 0x7FC0
+    assert poisoned == 2, "the carved key blocks must be SKIP for every query block"
+    assert (st[0, 0, :, 0] != oracle.SKIP).any() and (st[0, 1, :, 3] != oracle.SKIP).any()
     dc.bias, dc.k, dc.v = H.to_dev(bias2), H.to_dev(k2), H.to_dev(v2)
     dc.forward()
+    dc.backward()
     torch.cuda.synchronize()
     assert np.array_equal(H.bits(dc.o), o1)
+    for a, b in zip([H.bits(t) for t in (dc.dk, dc.dv, dc.dbias)], g1):
+        assert np.array_equal(a, b)
+    dq2 = H.f64(dc.dq)
+    assert np.all(np.isfinite(dq2))
+    assert H.within_one_bf16_ulp(dq2, dq1)
