@@ -298,17 +298,12 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) sw[gi] = swz32(l32, gi * 8 + hi * 4);
 
-  uint8_t cs0, cs1;  // states of the current item's two key blocks
-  lds_barrier();        // K tile staged
-  int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
-  int rh = 0, hh = 0;
-  if (qb >= 0) prefetch(qb, 0, 0, cs0, cs1);
-
-  while (qb >= 0) {
+  // Write the prefetched item into LDS: Q and dO rows (zero past lq), the effective bias of
+  // the item's rows (first head of the group only; it stays in registers for the others),
+  // and the row terms.
+  auto stage = [&](int qb, int rh, int hh, uint8_t cs0, uint8_t cs1) {
     const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
-    const int64_t h = g * p.G + hh;
     const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
-    // ---- write the prefetched item into LDS ----------------------------------------
 #pragma unroll
     for (int n = 0; n < QN; ++n) {
       const int task = tid + n * 256;
@@ -343,8 +338,27 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     }
     if (tid < kRows) sm.lse2[tid] = (tid < rows_left) ? prow_l * kLog2eB : INFINITY;
     else if (tid < 2 * kRows) sm.dr[tid - kRows] = (tid - kRows < rows_left) ? prow_d : 0.f;
+  };
+
+  // Item pipeline: item n+1 is loaded into registers while item n computes, and written
+  // into LDS once item n's Q, dO and bias tiles are no longer read (after the dS^T
+  // barrier), before item n's dQ atomics and dbias stores are issued.  A wait for the
+  // loads therefore never waits for those atomics and stores.
+  uint8_t cs0, cs1;  // states of the current item's two key blocks
+  lds_barrier();        // K tile staged
+  int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
+  int rh = 0, hh = 0;
+  if (qb >= 0) {
+    prefetch(qb, 0, 0, cs0, cs1);
+    stage(qb, 0, 0, cs0, cs1);
+  }
+  lds_barrier();
+
+  while (qb >= 0) {
+    const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
+    const int64_t h = g * p.G + hh;
+    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
     const uint8_t my_st = half ? cs1 : cs0;
-    lds_barrier();
 
     // ---- start loading the next item ------------------------------------------------
     int nqb = qb, nrh = rh, nhh = hh + 1;
@@ -450,6 +464,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         const i16x4 a1 = lds_read_tr16(&sm.s[sq[par][1] + sofs]);
         c = mfma32(join_bf16x8(a0, a1), join_bf16x8(k0, k1), c);
       }
+      // the next item's tiles go in while the dQ products run (they read only K and dS^T)
+      if (nqb >= 0) stage(nqb, nrh, nhh, ns0, ns1);
       {
         // rows of the item at or past rows_left fall outside the resource and are dropped
         const uint32_t rbytes = (uint32_t)(p.hq * D) * 4u;
@@ -482,7 +498,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dbacc[i]), r, lane_off + rc * rb, 0, 0);
       }
     }
-    lds_barrier();  // every reader of this item's tiles is done before the next item overwrites them
+    lds_barrier();  // the next item's tiles are visible; every dS^T read is done before it is rewritten
     qb = nqb;
     rh = nrh;
     hh = nhh;
