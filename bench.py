@@ -121,7 +121,8 @@ def main():
     lse = torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dbias = torch.empty((c.b, c.hkv, c.lq, c.lk), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.hq, c.d), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8,
+                     device="cuda")
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
@@ -182,7 +183,7 @@ def main():
     gbs = (b_cls + b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9
 
     # dominant launch: the one with the largest share of the step
-    phases = {"bwd": (t_bwd, f_bwd, "dma_attn_bwd (bwd_pre + bwd_main + dq_convert)"),
+    phases = {"bwd": (t_bwd, f_bwd, "dma_attn_bwd (bwd_pre + kt + pair_base + bwd_main + dq)"),
               "fwd": (t_fwd, f_fwd, "dma_attn_fwd (fwd_kernel)")}
     dom = max(phases, key=lambda k: phases[k][0])
     t_dom, f_dom, dom_name = phases[dom]

@@ -44,7 +44,7 @@ _lib.dma_attn_fwd.restype = _i32
 _lib.dma_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _i32, _vp, _vp,
                               _vp]
 _lib.dma_attn_bwd_workspace_size.restype = _sz
-_lib.dma_attn_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
+_lib.dma_attn_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32]
 _lib.dma_attn_bwd.restype = _i32
 _lib.dma_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -110,8 +110,8 @@ def dma_attn_fwd(q, k, v, mask, bias, block_state, scale: float, is_causal: bool
     _check("dma_attn_fwd", st)
 
 
-def dma_attn_bwd_workspace_size(b: int, lq: int, hq: int, d: int) -> int:
-    return int(_lib.dma_attn_bwd_workspace_size(b, lq, hq, d))
+def dma_attn_bwd_workspace_size(b: int, lq: int, lk: int, hq: int, hkv: int, d: int, is_causal: bool) -> int:
+    return int(_lib.dma_attn_bwd_workspace_size(b, lq, lk, hq, hkv, d, int(bool(is_causal))))
 
 
 def dma_attn_bwd(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq, dk, dv, dbias,
@@ -151,9 +151,11 @@ class _DMAttention(torch.autograd.Function):
     def backward(ctx, dout):
         q, k, v, m, bi, state, o, lse = ctx.saved_tensors
         b, lq, hq, d = q.shape
+        lk, hkv = k.shape[1], k.shape[2]
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dbias = torch.empty_like(bi) if ctx.bias_grad else None
-        ws = torch.empty(dma_attn_bwd_workspace_size(b, lq, hq, d), dtype=torch.uint8, device=q.device)
+        ws = torch.empty(dma_attn_bwd_workspace_size(b, lq, lk, hq, hkv, d, ctx.is_causal), dtype=torch.uint8,
+                         device=q.device)
         dma_attn_bwd(q, k, v, m, bi, state, o, dout.contiguous(), lse, ctx.scale, ctx.is_causal, dq, dk, dv, dbias, ws)
         return dq, dk, dv, None, dbias, None, None
 

@@ -94,11 +94,40 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   return hip_status(dma::launch_fwd(a, (hipStream_t)stream));
 }
 
-size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t hq, int64_t d) {
-  if (b < 1 || lq < 1 || hq < 1 || d < 1) return 0;
-  const size_t acc = (size_t)b * (size_t)lq * (size_t)hq * (size_t)d * sizeof(float);
-  const size_t rows = (size_t)b * (size_t)hq * (size_t)lq * sizeof(float);
-  return acc + ((rows + 255) / 256) * 256;
+}  // extern "C"
+
+namespace {
+// Byte offsets of the backward's workspace regions, each 256-byte aligned:
+//   drow       fp32 [b, hq, lq]                    D = rowsum(dO * O)
+//   pair_base  int64 [nqb + 1]                     first dS tile pair of each query block
+//   kt         bf16 [b, hkv, d, nkb2 * 128]        K transposed
+//   ds         bf16 [b, hkv, npairs, G, 2, 32*128] dS tiles of every live (query block, key pair)
+struct WsLayout {
+  size_t drow, pair_base, kt, ds, total;
+  int64_t npairs;
+};
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int causal) {
+  WsLayout w = {};
+  const int64_t nqb = (lq + 63) / 64, nkb2 = ((lk + 63) / 64 + 1) / 2;
+  int64_t np = 0;
+  for (int64_t qb = 0; qb < nqb; ++qb) np += dma::live_pairs(qb, lq, lk, causal);
+  w.npairs = np;
+  w.drow = 0;
+  w.pair_base = w.drow + up256((size_t)b * hq * lq * sizeof(float));
+  w.kt = w.pair_base + up256((size_t)(nqb + 1) * sizeof(int64_t));
+  w.ds = w.kt + up256((size_t)b * hkv * d * nkb2 * 128 * sizeof(uint16_t));
+  w.total = w.ds + up256((size_t)b * hq * np * 2 * 32 * 128 * sizeof(uint16_t));
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                                   int is_causal) {
+  if (!sizes_ok(b, lq, lk, hq, hkv) || d < 1 || hq % hkv != 0 || (is_causal != 0 && is_causal != 1)) return 0;
+  return ws_layout(b, lq, lk, hq, hkv, d, is_causal).total;
 }
 
 int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
@@ -112,9 +141,10 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
       !aligned_or_null(dbias) || !aligned16(workspace))
     return DMA_ERR_INVALID_ARGUMENT;
   if (dbias && lk % 8 != 0) return DMA_ERR_INVALID_ARGUMENT;
-  // per-row byte ranges of the dQ accumulation and of dbias must stay within 32-bit offsets
-  if (lk > (int64_t(1) << 24) || hq * d > (int64_t(1) << 20)) return DMA_ERR_UNSUPPORTED;
-  if (workspace_bytes < dma_attn_bwd_workspace_size(b, lq, hq, d)) return DMA_ERR_WORKSPACE_TOO_SMALL;
+  // per-row byte ranges of dbias must stay within 32-bit offsets
+  if (lk > (int64_t(1) << 24)) return DMA_ERR_UNSUPPORTED;
+  const WsLayout wl = ws_layout(b, lq, lk, hq, hkv, d, is_causal);
+  if (workspace_bytes < wl.total) return DMA_ERR_WORKSPACE_TOO_SMALL;
   dma::AttnArgs a = {};
   a.q = q;
   a.k = k;
@@ -129,8 +159,12 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   a.dk = dk;
   a.dv = dv;
   a.dbias = dbias;
-  a.dq_acc = static_cast<float*>(workspace);
-  a.drow = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)b * lq * hq * d * sizeof(float));
+  char* ws = static_cast<char*>(workspace);
+  a.drow = reinterpret_cast<float*>(ws + wl.drow);
+  a.pair_base = reinterpret_cast<int64_t*>(ws + wl.pair_base);
+  a.kt = reinterpret_cast<uint16_t*>(ws + wl.kt);
+  a.ds = reinterpret_cast<uint16_t*>(ws + wl.ds);
+  a.npairs = wl.npairs;
   a.b = b;
   a.lq = lq;
   a.lk = lk;

@@ -9,12 +9,14 @@
 //   dBias[g] = sum over the query heads of group g of dS.
 //
 // Kernels:
-//   bwd_pre_kernel    D = rowsum(dO * O) and a zeroed fp32 dQ accumulator.
+//   bwd_pre_kernel    D = rowsum(dO * O).
+//   kt_kernel         K transposed ([b, g, d, keys]), the A operand of the dQ products.
+//   pair_base_kernel  offsets of each query block's dS tiles (live 128-key pairs before it).
 //   bwd_main_kernel   one workgroup per (batch, kv head g, 128 keys = two
 //                     classification blocks); four wavefronts own 32 keys each.
 //                     Work items are (query block, 32-row half, head), heads
 //                     innermost.
-//                     K and V of the keys sit in registers for the whole kernel
+//                     K and V of the keys sit in LDS / registers for the whole kernel
 //                     and dK/dV accumulate in registers over every non-SKIP query
 //                     block and every head of the group, so they are written
 //                     once, without atomics.  Per query block the effective bias
@@ -23,18 +25,26 @@
 //                     heads in registers and stored once.  SKIP blocks get zeros
 //                     and no loads.  The Q/dO tiles (and the bias/mask of a new
 //                     query block) of the next item are loaded into registers
-//                     while the current item computes.  dQ: dS^T goes to LDS and
-//                     each wave multiplies it by 32 columns of K, adding into the
-//                     fp32 accumulator with atomics (query rows are shared by
-//                     all key blocks).
-//   dq_convert_kernel fp32 accumulator -> bf16 dQ.
+//                     while the current item computes.  Each item's dS (bf16) goes
+//                     to the workspace in the order the dQ kernel consumes it.
+//   dq_kernel         dQ = scale dS K: one workgroup per (batch, g, 64-row query block,
+//                     heads), summing over the live key pairs in registers and
+//                     writing bf16 dQ once.
+//
+// Why dQ is not accumulated with atomics: on this device every fp32 atomic add to global
+// memory is performed at the memory side, at about 3.4e11 adds/s whatever the access
+// pattern.  Adding each item's dS K into a dQ accumulator costs one add per (query, d,
+// 128-key pair): 4.3e9 adds, ~12.7 ms, at L = 16384 with causal top-k, more than all the
+// matrix work of the backward.  Writing dS (one bf16 per query, key and head) and reading
+// it back once is ~17 GB of plain traffic and no atomics; dQ also becomes deterministic.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 for all five products.  S = Q K^T puts one key
 // per lane (lane l%32) and 16 query rows per lane, which is the A-operand layout
 // of the key-major products dV = P^T dO and dK = dS^T Q (the query order inside
 // a k-step only has to agree between A and B); their B operands (dO, Q with the
 // query index as the contraction) come from the row-major tiles through
-// ds_read_b64_tr_b16, as do both operands of dQ = dS K.
+// ds_read_b64_tr_b16.  dQ^T = K^T dS^T takes K^T rows from LDS and the stored dS
+// chunks as B, so a result lane holds one query row.
 #include <math.h>
 
 #include "common.h"
@@ -46,8 +56,8 @@ constexpr uint16_t kNegInfB = 0xFF80u;
 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                      float* __restrict__ drow, float* __restrict__ dq_acc,
-                                                      int64_t rows, int64_t lq, int64_t hq, int d) {
+                                                      float* __restrict__ drow, int64_t rows, int64_t lq, int64_t hq,
+                                                      int d) {
   // rows = b * lq * hq (row index = (b*lq + i)*hq + h); d/8 lanes per row.
   const int lpr = d / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -59,15 +69,72 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     const u32x4 gw = *reinterpret_cast<const u32x4*>(dout + r * d + c * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc += bf16_lo(ow[e]) * bf16_lo(gw[e]) + bf16_hi(ow[e]) * bf16_hi(gw[e]);
-    float4* z = reinterpret_cast<float4*>(dq_acc + r * d + c * 8);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   for (int off = lpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, lpr);
   if (r < rows && c == 0) {
     const int64_t h = r % hq, bi = r / hq;  // bi = b*lq + i
     const int64_t bb = bi / lq, i = bi % lq;
     drow[(bb * hq + h) * lq + i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K^T for the dQ products: kt[(b*hkv + g)*d + c][j] = K[b, j, g, c] for j < lk, 0 up to the
+// next multiple of 128 keys.  One workgroup per (b, g, 64 keys), through an LDS tile.
+__global__ __launch_bounds__(256) void kt_kernel(const uint16_t* __restrict__ k, uint16_t* __restrict__ kt, int64_t lk,
+                                                 int64_t hkv, int64_t ktrow, int nkb64, int d) {
+  __shared__ uint16_t tile[64 * (128 + 2)];  // [key][d], odd-word row pad
+  const int tr = d + 2;
+  const int64_t plane = blockIdx.x / nkb64;
+  const int kb = blockIdx.x % nkb64;
+  const int64_t bb = plane / hkv, g = plane % hkv;
+  for (int t = threadIdx.x; t < 64 * (d / 8); t += 256) {
+    const int r = t / (d / 8), c = t % (d / 8);
+    const int64_t key = (int64_t)kb * 64 + r;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (key < lk) w = *reinterpret_cast<const u32x4*>(k + ((bb * lk + key) * hkv + g) * d + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[r * tr + c * 8 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+      tile[r * tr + c * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < d * 8; t += 256) {  // row c of K^T: 64 keys = 8 chunks
+    const int c = t / 8, j8 = t % 8;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[(j8 * 8 + 2 * e) * tr + c] | ((uint32_t)tile[(j8 * 8 + 2 * e + 1) * tr + c] << 16);
+    *reinterpret_cast<u32x4*>(kt + (plane * d + c) * ktrow + (int64_t)kb * 64 + j8 * 8) = w;
+  }
+}
+
+// pair_base[qb] = live key-block pairs of the query blocks before qb (the same for every
+// plane); pair_base[nqb] = all of them.  One workgroup.
+__global__ __launch_bounds__(1024) void pair_base_kernel(int64_t* __restrict__ pair_base, int64_t nqb, int64_t lq,
+                                                         int64_t lk, int causal) {
+  __shared__ int64_t part[1024];
+  const int64_t per = (nqb + 1023) / 1024;
+  const int64_t lo = min(nqb, (int64_t)threadIdx.x * per), hi = min(nqb, lo + per);
+  int64_t sum = 0;
+  for (int64_t qb = lo; qb < hi; ++qb) sum += live_pairs(qb, lq, lk, causal);
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int64_t x = part[i];
+      part[i] = run;
+      run += x;
+    }
+    pair_base[nqb] = run;
+  }
+  __syncthreads();
+  int64_t run = part[threadIdx.x];
+  for (int64_t qb = lo; qb < hi; ++qb) {
+    pair_base[qb] = run;
+    run += live_pairs(qb, lq, lk, causal);
   }
 }
 
@@ -82,7 +149,9 @@ struct BwdParams {
   const uint16_t* dout;
   const float* lse;
   const float* drow;
-  float* dq_acc;
+  const int64_t* pair_base;
+  uint16_t* ds;
+  int64_t npairs;
   uint16_t* dk;
   uint16_t* dv;
   uint16_t* dbias;
@@ -274,9 +343,6 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   // Per-lane LDS element offsets, computed once; the loops add compile-time row offsets
   // only.  The swizzle's XOR term depends on the row modulo 16 (128-wide tiles) or 32 (the
   // dS^T tile), so adding a multiple of that many rows is a plain add.
-  constexpr int DT = D / 32, WPT = 4 / DT, KCH = 8 / WPT;  // dQ: column tiles, waves per tile, k-steps per wave
-  static_assert(KCH % 2 == 0, "dQ k-steps per wave must pair up the 32-row halves of dS^T");
-  const int dtile = wave % DT, kpart = wave / DT;
   int aoff[D / 16];                  // S/dP operand rows: l32 (+ wave*32 for K)
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) aoff[s] = tile_off<D>(l32, s * 16 + hi * 8);
@@ -286,9 +352,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     gq0[dt] = tile_off<D>(hi * 4 + trow, dt * 32 + tcol);
     gq1[dt] = tile_off<D>(hi * 4 + trow + 8, dt * 32 + tcol);
   }
-  const int kq0 = tile_off<D>(hi * 8 + trow, dtile * 32 + tcol);      // dQ, K rows (+ ks*16)
-  const int kq1 = tile_off<D>(hi * 8 + trow + 4, dtile * 32 + tcol);
-  int sq[2][2];                      // dQ, dS^T rows (ks%2)*16 + hi*8 + trow (+4), + (ks/2)*32
+  int sq[2][2];                      // dS export, dS^T rows (ks%2)*16 + hi*8 + trow (+4), + (ks/2)*32
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     sq[par][0] = swz32(par * 16 + hi * 8 + trow, tcol);
@@ -447,40 +511,25 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     }
     lds_barrier();
 
-    // ---- dQ[:, dtile*32 .. +31] += scale * dS K over the 128 keys ----------------------------
-    // D/32 column tiles of dQ; with d = 64 two waves share a tile and split the keys.  A SKIP
-    // half's dS rows are zero, so running every k-step adds nothing there and keeps the loop
-    // straight-line.
+    // ---- dS of the item to the workspace, in the order the dQ kernel reads it --------------
+    // 16-byte chunk c holds keys (c/64)*16 + ((c/32)%2)*8 .. +7 of query row c%32.  This lane
+    // writes chunks tid and tid + 256: transposing reads of the dS^T tile give it those 8
+    // keys of its query (k-steps wave and wave + 4, rows hi*8 of the step), and consecutive
+    // lanes store consecutive chunks.
     {
-      f32x16 c = f32x16{};
+      uint16_t* tile =
+          p.ds + ((((int64_t)plane * p.npairs + p.pair_base[qb] + KB) * p.G + hh) * 2 + rh) * (kRows * kKeys);
 #pragma unroll
-      for (int kk = 0; kk < KCH; ++kk) {
-        const int ks = kpart * KCH + kk;
-        const int kofs = ks * 16 * KR, sofs = (ks >> 1) * 32 * SR;
-        const int par = kk & 1;  // == ks & 1, since KCH is even
-        const i16x4 k0 = lds_read_tr16(&sm.k[kq0 + kofs]);
-        const i16x4 k1 = lds_read_tr16(&sm.k[kq1 + kofs]);
-        const i16x4 a0 = lds_read_tr16(&sm.s[sq[par][0] + sofs]);
-        const i16x4 a1 = lds_read_tr16(&sm.s[sq[par][1] + sofs]);
-        c = mfma32(join_bf16x8(a0, a1), join_bf16x8(k0, k1), c);
-      }
-      // the next item's tiles go in while the dQ products run (they read only K and dS^T)
-      if (nqb >= 0) stage(nqb, nrh, nhh, ns0, ns1);
-      {
-        // rows of the item at or past rows_left fall outside the resource and are dropped
-        const uint32_t rbytes = (uint32_t)(p.hq * D) * 4u;
-        const __amdgpu_buffer_rsrc_t r =
-            make_rsrc(p.dq_acc + ((bidx * p.lq + i0) * p.hq + h) * D + dtile * 32, (uint32_t)rows_left * rbytes);
-        uint32_t rb = rbytes;
-        asm volatile("" : "+s"(rb));  // keep the row offsets below inside the loop (not hoisted)
-        const uint32_t lane_off = (uint32_t)(hi * 4) * rb + (uint32_t)l32 * 4u;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t rc = (i >> 2) * 8 + (i & 3);  // row minus this lane's hi*4
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(c[i] * p.scale, r, lane_off + rc * rb, 0, 0);
-        }
+      for (int hf = 0; hf < 2; ++hf) {
+        const int ks = wave + 4 * hf;
+        const int sofs = (ks >> 1) * 32 * SR;
+        const i16x4 a0 = lds_read_tr16(&sm.s[sq[ks & 1][0] + sofs]);
+        const i16x4 a1 = lds_read_tr16(&sm.s[sq[ks & 1][1] + sofs]);
+        *reinterpret_cast<bf16x8*>(tile + (tid + 256 * hf) * 8) = join_bf16x8(a0, a1);
       }
     }
+    // the next item's tiles go in now (the export above reads only dS^T)
+    if (nqb >= 0) stage(nqb, nrh, nhh, ns0, ns1);
 
     // ---- dBias of the item's rows, summed over the group: store after the last head -------------
     if (hh == p.G - 1 && p.dbias != nullptr) {
@@ -522,27 +571,151 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq,
-                                                         int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
-  const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
-  u32x4 w;
-  w[0] = pack_bf16x2(a.x, a.y);
-  w[1] = pack_bf16x2(a.z, a.w);
-  w[2] = pack_bf16x2(b.x, b.y);
-  w[3] = pack_bf16x2(b.z, b.w);
-  reinterpret_cast<u32x4*>(dq)[i] = w;
+// dQ = scale * sum over the live key-block pairs of dS K, without atomics.  One workgroup per
+// (batch, kv head g, 64-row query block, chunk of HC query heads); wave (head, 32-row half)
+// accumulates dQ^T = K^T dS^T for its 32 rows in registers:
+//   A = K^T rows d (staged once per pair for all heads, swizzled 128-key rows),
+//   B = the dS chunks the backward main kernel stored in fragment order (lane l reads
+//       chunk ks*64 + l of its tile: query l%32, keys ks*16 + (l/32)*8 .. +7),
+// so the result lane holds one query row and 4-element runs of d for the store.
+struct DqParams {
+  const uint8_t* state;
+  const int64_t* pair_base;
+  const uint16_t* kt;
+  const uint16_t* ds;
+  uint16_t* dq;
+  int64_t lq, lk, hq, hkv, npairs, ktrow;
+  int G, chunks, nqb, nkb, total_wg;
+  float scale;
+  int causal;
+};
+
+template <int D, int HC>
+__global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
+  constexpr int NT = HC * 128;
+  constexpr int KT = D * 16 / NT;  // 16-byte chunks of the K^T tile each thread stages
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[D * 128];  // [d][128 keys], swz128 rows
+
+  const int w = blockIdx.x;
+  const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
+  const int unit = t / p.nqb;
+  const int qb = p.nqb - 1 - (t % p.nqb);
+  const int plane = unit / p.chunks, chunk = unit % p.chunks;
+  const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int hh = chunk * HC + (wave >> 1), rh = wave & 1;
+  const int64_t head = g * p.G + hh;
+
+  const int64_t npair = live_pairs(qb, p.lq, p.lk, p.causal);
+  const int64_t pbase = p.pair_base[qb];
+  const uint8_t* st_row = p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
+  const uint16_t* ktp = p.kt + (int64_t)plane * D * p.ktrow;
+  // the tile of pair KB for this wave: + (pbase + KB) * G * 2 * 4096
+  const uint16_t* dsp = p.ds + (((int64_t)plane * p.npairs + pbase) * p.G + hh) * 2 * (kRows * kKeys) +
+                        (int64_t)rh * (kRows * kKeys);
+  const int64_t pair_stride = (int64_t)p.G * 2 * (kRows * kKeys);
+
+  auto live = [&](int64_t kb2) -> bool {
+    const uint8_t s0 = st_row[2 * kb2];
+    const uint8_t s1 = (2 * kb2 + 1 < p.nkb) ? st_row[2 * kb2 + 1] : kSkip;
+    return s0 != kSkip || s1 != kSkip;
+  };
+  auto next_pair = [&](int64_t from) -> int64_t {
+    for (int64_t kb2 = from; kb2 < npair; ++kb2)
+      if (live(kb2)) return kb2;
+    return npair;
+  };
+
+  u32x4 pkt[KT];
+  auto prefetch_kt = [&](int64_t kb2) {
+#pragma unroll
+    for (int n = 0; n < KT; ++n) {
+      const int task = tid + n * NT;
+      const int r = task >> 4, c = task & 15;
+      pkt[n] = *reinterpret_cast<const u32x4*>(ktp + (int64_t)r * p.ktrow + kb2 * 128 + c * 8);
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  int aoff[D / 32];  // A operand rows dt*32 + l32, keys hi*8 (+ ks*16: the XOR term is per row, so per-lane)
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) aoff[dt] = swz128(dt * 32 + l32, hi * 8);
+
+  int64_t kb2 = next_pair(0);
+  if (kb2 < npair) prefetch_kt(kb2);
+  while (kb2 < npair) {
+    // this pair's dS fragments (eight 16-byte chunks per lane), issued before the staging
+    bf16x8 bfr[8];
+    const uint16_t* tile = dsp + kb2 * pair_stride;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8*>(tile + (ks * 64 + lane) * 8);
+    // a key block that is SKIP for this query block has dS = 0 and may hold any K rows (they
+    // are never loaded elsewhere): its half of the tile is staged as zeros
+    const bool dead0 = st_row[2 * kb2] == kSkip;
+    const bool dead1 = (2 * kb2 + 1 < p.nkb) ? st_row[2 * kb2 + 1] == kSkip : true;
+    lds_barrier();  // every read of the previous K^T tile is done
+#pragma unroll
+    for (int n = 0; n < KT; ++n) {
+      const int task = tid + n * NT;
+      const int r = task >> 4, c = task & 15;
+      const bool dead = (c < 8) ? dead0 : dead1;
+      *reinterpret_cast<u32x4*>(&ktile[swz128(r, c * 8)]) = dead ? u32x4{0u, 0u, 0u, 0u} : pkt[n];
+    }
+    lds_barrier();
+    const int64_t kb2n = next_pair(kb2 + 1);
+    if (kb2n < npair) prefetch_kt(kb2n);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        // keys ks*16 + hi*8 are 16-byte chunk 2*ks + hi; swz128 XORs the chunk index, so the
+        // k-step flips bits 4..6 of the per-lane offset
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&ktile[aoff[dt] ^ (ks << 4)]);
+        acc[dt] = mfma32(av, bfr[ks], acc[dt]);
+      }
+    }
+    kb2 = kb2n;
+  }
+
+  // ---- dQ rows qb*64 + rh*32 + l32, d = dt*32 + gi*8 + hi*4 .. +3 ------------------------
+  const int64_t row = (int64_t)qb * kBlock + rh * kRows + l32;
+  if (row < p.lq) {
+    uint16_t* op = p.dq + ((bidx * p.lq + row) * p.hq + head) * D + hi * 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        u32x2 w2;
+        w2[0] = pack_bf16x2(acc[dt][gi * 4 + 0] * p.scale, acc[dt][gi * 4 + 1] * p.scale);
+        w2[1] = pack_bf16x2(acc[dt][gi * 4 + 2] * p.scale, acc[dt][gi * 4 + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(op + dt * 32 + gi * 8) = w2;
+      }
+  }
+}
+
+template <int D, int HC>
+static hipError_t launch_dq_t(const DqParams& q, hipStream_t stream) {
+  hipLaunchKernelGGL((dq_kernel<D, HC>), dim3(q.total_wg), dim3(HC * 128), 0, stream, q);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   const int64_t rows = a.b * a.lq * a.hq;
+  const int nqb = (int)((a.lq + kBlock - 1) / kBlock), nkb = (int)((a.lk + kBlock - 1) / kBlock);
+  const int nkb2 = (nkb + 1) / 2;
+  const int64_t ktrow = (int64_t)nkb2 * 128;
   {
     const int64_t threads = rows * (a.d / 8);
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.o, a.dout,
-                       a.drow, a.dq_acc, rows, a.lq, a.hq, (int)a.d);
+                       a.drow, rows, a.lq, a.hq, (int)a.d);
+    hipLaunchKernelGGL(kt_kernel, dim3((unsigned)(a.b * a.hkv * nkb2 * 2)), dim3(256), 0, stream, a.k, a.kt, a.lk,
+                       a.hkv, ktrow, nkb2 * 2, (int)a.d);
+    hipLaunchKernelGGL(pair_base_kernel, dim3(1), dim3(1024), 0, stream, a.pair_base, (int64_t)nqb, a.lq, a.lk,
+                       a.causal);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -556,7 +729,9 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.dout = a.dout;
   p.lse = a.lse_in;
   p.drow = a.drow;
-  p.dq_acc = a.dq_acc;
+  p.pair_base = a.pair_base;
+  p.ds = a.ds;
+  p.npairs = a.npairs;
   p.dk = a.dk;
   p.dv = a.dv;
   p.dbias = a.dbias;
@@ -565,9 +740,9 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.G = (int)(a.hq / a.hkv);
-  p.nqb = (int)((a.lq + kBlock - 1) / kBlock);
-  p.nkb = (int)((a.lk + kBlock - 1) / kBlock);
-  p.nkb2 = (p.nkb + 1) / 2;
+  p.nqb = nqb;
+  p.nkb = nkb;
+  p.nkb2 = nkb2;
   p.total_wg = (int)(a.b * a.hkv * p.nkb2);
   p.scale = a.scale;
   p.causal = a.causal;
@@ -577,9 +752,35 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_main_kernel<128>, dim3(p.total_wg), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n8 = rows * a.d / 8;
-  hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a.dq_acc, a.dq, n8);
-  return hipGetLastError();
+
+  DqParams q;
+  q.state = a.state;
+  q.pair_base = a.pair_base;
+  q.kt = a.kt;
+  q.ds = a.ds;
+  q.dq = a.dq;
+  q.lq = a.lq;
+  q.lk = a.lk;
+  q.hq = a.hq;
+  q.hkv = a.hkv;
+  q.npairs = a.npairs;
+  q.ktrow = ktrow;
+  q.G = p.G;
+  const int HC = q.G >= 4 ? 4 : q.G;
+  q.chunks = q.G / HC;
+  q.nqb = nqb;
+  q.nkb = nkb;
+  q.total_wg = (int)(a.b * a.hkv * q.chunks * nqb);
+  q.scale = a.scale;
+  q.causal = a.causal;
+  if (a.d == 64) {
+    if (HC == 1) return launch_dq_t<64, 1>(q, stream);
+    if (HC == 2) return launch_dq_t<64, 2>(q, stream);
+    return launch_dq_t<64, 4>(q, stream);
+  }
+  if (HC == 1) return launch_dq_t<128, 1>(q, stream);
+  if (HC == 2) return launch_dq_t<128, 2>(q, stream);
+  return launch_dq_t<128, 4>(q, stream);
 }
 
 }  // namespace dma

@@ -137,12 +137,27 @@ struct AttnArgs {
   uint16_t* dk;
   uint16_t* dv;
   uint16_t* dbias;
-  float* dq_acc;  // fp32 [b, lq, hq, d]
-  float* drow;    // fp32 [b, hq, lq]: rowsum(dO * O)
+  float* drow;        // fp32 [b, hq, lq]: rowsum(dO * O)
+  int64_t* pair_base; // [nqb + 1]: index of query block qb's first dS tile pair (live pairs before it)
+  uint16_t* kt;       // bf16 [b, hkv, d, nkb2 * 128]: K transposed, zero past lk
+  uint16_t* ds;       // bf16 dS tiles, see bwd_ds_tile
+  int64_t npairs;     // live key-block pairs of one plane (pair_base[nqb])
   int64_t b, lq, lk, hq, hkv, d;
   float scale;
   int causal;
 };
+
+// Key-block pairs (128 keys) that can hold a valid position for query block qb: all of them
+// without causality, else those whose first key is at most the block's last row + lk - lq.
+// Shared by the workspace sizing on the host and the kernels that index the dS tiles.
+__host__ __device__ inline int64_t live_pairs(int64_t qb, int64_t lq, int64_t lk, int causal) {
+  const int64_t nkb2 = ((lk + 63) / 64 + 1) / 2;
+  if (!causal) return nkb2;
+  const int64_t last = qb * 64 + 63 + (lk - lq);  // largest key a row of the block may attend
+  if (last < 0) return 0;
+  const int64_t n = last / 128 + 1;
+  return n < nkb2 ? n : nkb2;
+}
 
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);

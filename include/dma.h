@@ -106,9 +106,14 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
                  float scale, int is_causal, uint16_t* o, float* lse, void* stream);
 
-/* Bytes of device workspace dma_attn_bwd needs: fp32 dq accumulator [b, lq, hq, d]
- * plus the fp32 row terms D = rowsum(dO * O) [b, hq, lq]. */
-size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t hq, int64_t d);
+/* Bytes of device workspace dma_attn_bwd needs for these sizes (0 for invalid
+ * sizes): the fp32 row terms D = rowsum(dO * O) [b, hq, lq], K transposed
+ * (bf16), and the bf16 dS tile of every (query head, 64-row query block, 128-key
+ * pair of classification blocks) that causality leaves live, from which dQ is
+ * formed without atomics (FlashMask README: deterministic backward).  With
+ * is_causal the count of live pairs is about half of all pairs. */
+size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                                   int is_causal);
 
 /*
  * Backward pass (Flash-DMA README: gradients for query, key, value and bias,
@@ -126,7 +131,8 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t hq, int64_t d)
  *   workspace   device scratch of at least dma_attn_bwd_workspace_size() bytes,
  *               16-byte aligned, owned by the caller, contents on entry ignored
  * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL, and
- *   DMA_ERR_UNSUPPORTED for lk > 2^24 or hq * d > 2^20 (32-bit row offsets).
+ *   DMA_ERR_UNSUPPORTED for lk > 2^24 (32-bit row offsets of dbias).
+ * dq is deterministic: the same inputs give bit-identical outputs.
  */
 int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
                  const uint8_t* block_state, const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b,

@@ -37,13 +37,6 @@ def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
 
 
-def within_one_bf16_ulp(a: np.ndarray, b: np.ndarray) -> bool:
-    """Element-wise |a - b| <= one bf16 unit in the last place of max(|a|, |b|) (a, b: bf16 values)."""
-    m = np.maximum(np.abs(a), np.abs(b))
-    ulp = np.where(m > 0, np.exp2(np.floor(np.log2(np.where(m > 0, m, 1.0))) - 7), 0.0)
-    return bool(np.all(np.abs(a - b) <= ulp))
-
-
 def worst_elements(o: np.ndarray, ref: np.ndarray, n: int = 5) -> str:
     err = np.abs(o - ref).ravel()
     idx = np.argsort(err)[::-1][:n]
@@ -113,7 +106,7 @@ class DeviceCase:
         self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
         self.dbias = (torch.full((c.b, c.hkv, c.lq, c.lk), float("nan"), dtype=torch.bfloat16, device="cuda")
                       if want_dbias else None)
-        ws = torch.empty(self.dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.hq, c.d), dtype=torch.uint8,
+        ws = torch.empty(self.dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8,
                          device="cuda")
         self.dma.dma_attn_bwd(self.q, self.k, self.v, self.mask, self.bias, self.state, self.o, do, self.lse,
                               c.scale_f32, c.causal, self.dq, self.dk, self.dv, self.dbias, ws)
@@ -206,7 +199,7 @@ def check_full_case(c: synth.Case, n_blocks: int = 64, log=print):
     lse = torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dbias = torch.full((c.b, c.hkv, c.lq, c.lk), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.hq, c.d), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8, device="cuda")
     log(f"[{c.name}] classify / fwd / bwd on the GPU", flush=True)
     dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, state)
     dma.dma_attn_fwd(q, k, v, mask, bias, state, c.scale_f32, c.causal, o, lse)

@@ -25,7 +25,7 @@ def lib():
     L.dma_block_classify.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp]
     L.dma_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp]
     L.dma_attn_bwd_workspace_size.restype = sz
-    L.dma_attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+    L.dma_attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     L.dma_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp,
                                vp, vp, sz, vp]
     L.dma_status_string.restype = ctypes.c_char_p
@@ -101,16 +101,42 @@ def test_fwd_ragged_lk_allowed_without_mask_and_bias(lib):
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID), (dict(dv=None), INVALID),
     (dict(ws=None), INVALID), (dict(lse=P + 4), INVALID), (dict(db=P + 2), INVALID),
     (dict(wsb=1000), WS_SMALL), (dict(d=80), UNSUPPORTED),
-    (dict(lk=(1 << 24) + 64), UNSUPPORTED), (dict(hq=16384, hkv=1024), UNSUPPORTED),
+    (dict(lk=(1 << 24) + 64), UNSUPPORTED),
 ])
 def test_bwd_rejects(lib, kw, want):
     assert bwd(lib, **kw) == want
 
 
-def test_workspace_size(lib):
-    n = lib.dma_attn_bwd_workspace_size(2, 100, 8, 128)
-    assert n >= 2 * 100 * 8 * 128 * 4 + 2 * 8 * 100 * 4
-    assert lib.dma_attn_bwd_workspace_size(0, 1, 1, 1) == 0
+def live_pairs(qb, lq, lk, causal):
+    """128-key pairs of classification blocks that can hold a valid entry of 64-row block qb."""
+    nkb2 = ((lk + 63) // 64 + 1) // 2
+    if not causal:
+        return nkb2
+    last = qb * 64 + 63 + lk - lq  # largest key index a row of the block may attend
+    return 0 if last < 0 else min(nkb2, last // 128 + 1)
+
+
+@pytest.mark.parametrize("b,lq,lk,hq,hkv,d,causal", [
+    (2, 100, 100, 8, 2, 128, 0), (1, 4096, 4096, 32, 8, 128, 1), (1, 300, 1000, 4, 4, 64, 1),
+    (1, 1000, 300, 4, 1, 64, 1), (1, 64, 4096, 2, 1, 64, 1),
+])
+def test_workspace_size(lib, b, lq, lk, hq, hkv, d, causal):
+    # regions: D rows (fp32), pair offsets (int64), K^T (bf16, keys padded to 128), dS tiles
+    # (bf16, 64 x 128 per live pair and query head); each rounded up to 256 bytes
+    up = lambda x: (x + 255) // 256 * 256
+    nqb, nkb2 = (lq + 63) // 64, ((lk + 63) // 64 + 1) // 2
+    npairs = sum(live_pairs(qb, lq, lk, causal) for qb in range(nqb))
+    want = up(b * hq * lq * 4) + up((nqb + 1) * 8) + up(b * hkv * d * nkb2 * 128 * 2) + up(b * hq * npairs * 64 * 128 * 2)
+    assert lib.dma_attn_bwd_workspace_size(b, lq, lk, hq, hkv, d, causal) == want
+
+
+def test_workspace_size_causal_half_and_invalid(lib):
+    full = lib.dma_attn_bwd_workspace_size(1, 16384, 16384, 16, 4, 128, 0)
+    causal = lib.dma_attn_bwd_workspace_size(1, 16384, 16384, 16, 4, 128, 1)
+    assert 0.45 * full < causal < 0.55 * full
+    assert lib.dma_attn_bwd_workspace_size(0, 1, 1, 1, 1, 1, 0) == 0
+    assert lib.dma_attn_bwd_workspace_size(1, 64, 64, 3, 2, 64, 0) == 0  # hq % hkv != 0
+    assert lib.dma_attn_bwd_workspace_size(1, 64, 64, 2, 1, 64, 2) == 0  # is_causal not 0/1
 
 
 def test_classify_rejects(lib):

@@ -79,9 +79,9 @@ def test_autograd_wrapper_matches_oracle():
 
 
 def test_repeatable():
-    """Two runs: O, LSE, dK, dV, dBias bit-identical (one writer per element).  dQ is summed with
-    fp32 atomics in whatever order the workgroups reach them, so its bf16 rounding may differ by
-    one unit in the last place."""
+    """Two runs give bit-identical O, LSE, dQ, dK, dV and dBias: every output element has one
+    writer and a fixed order of accumulation (dQ is formed from the stored dS tiles by one
+    workgroup per query block, without atomics)."""
     import gpu_harness as H
 
     c = Case("repeat", 24, 1, 512, 512, 8, 2, 128, True, "topk", 200)
@@ -92,11 +92,9 @@ def test_repeatable():
         dc.forward()
         dc.backward()
         torch.cuda.synchronize()
-        outs.append([H.bits(t) for t in (dc.o, dc.dk, dc.dv, dc.dbias)] + [dc.lse.cpu().numpy(), H.f64(dc.dq)])
-    for a, b in zip(outs[0][:5], outs[1][:5]):
+        outs.append([H.bits(t) for t in (dc.o, dc.dq, dc.dk, dc.dv, dc.dbias)] + [dc.lse.cpu().numpy()])
+    for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
-    assert H.within_one_bf16_ulp(outs[0][5], outs[1][5])
-    assert H.rel_l2(outs[0][5], outs[1][5]) < 1e-4
 
 
 def test_skipped_tiles_do_not_leak():
@@ -145,6 +143,4 @@ def test_skipped_tiles_do_not_leak():
     assert np.array_equal(H.bits(dc.o), o1)
     for a, b in zip([H.bits(t) for t in (dc.dk, dc.dv, dc.dbias)], g1):
         assert np.array_equal(a, b)
-    dq2 = H.f64(dc.dq)
-    assert np.all(np.isfinite(dq2))
-    assert H.within_one_bf16_ulp(dq2, dq1)
+    assert np.array_equal(H.f64(dc.dq), dq1)
