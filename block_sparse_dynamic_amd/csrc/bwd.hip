@@ -167,25 +167,60 @@ constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LD
 
 template <int D>
 struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay single 16-byte LDS accesses
-  static constexpr int kRow = tile_row<D>();  // K, Q, dO tiles [row][d] (tile_off layout)
-  static constexpr int kSRow = kRows;         // dS^T [key][query] (swz32 layout)
-  static constexpr int kBRow = kKeys + 8;   // effective bias [query][key]
-  uint16_t q[kRows * kRow];
-  uint16_t g[kRows * kRow];
-  uint16_t s[kKeys * kSRow];
-  uint16_t b[kRows * kBRow];
-  float lse2[kRows];  // lse * log2(e); +inf outside the matrix
-  float dr[kRows];    // D = rowsum(dO * O)
+  static constexpr int kTile = kRows * D;       // Q or dO tile [row][d], tile_off<D> layout
+  static constexpr int kBTile = kRows * kKeys;  // raw bias or mask tile [row][key], swz128 layout
+  static constexpr int kSTile = kKeys * kRows;  // dS^T [key][query], swz32 layout
+  uint16_t k[kKeys * D];  // K of the workgroup's keys, tile_off<D> layout
+  // Two buffers each: the current item's and the next item's, which loads meanwhile.
+  uint16_t q[2][kTile];
+  uint16_t g[2][kTile];
+  uint16_t b[2][kBTile];
+  uint16_t m[2][kBTile];
+  uint16_t s[2][kSTile];
+  float lse[2][64];  // rows 32..63 take the out-of-range lanes of the load
+  float dr[2][64];   // D = rowsum(dO * O)
   uint8_t st[2][kStateChunk];  // block states of the two key blocks for a range of query blocks
-  uint16_t k[kKeys * kRow];
 };
+
+// Words of a raw buffer resource (the layout make_rsrc builds), uniform across the wave.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(const void, p));
+}
+// Loads straight into LDS (buffer_load ... lds): the wave's lane l fetches 16 (or 4) bytes at
+// its offset `voff` in buffer `r` and they land at LDS byte address lds + 16 l (or + 4 l).
+// Lanes whose offset is out of the buffer's range fetch nothing.  The compiler does not see
+// these LDS writes, so it neither waits for them nor orders LDS reads after them: the kernel
+// waits for them (vmcnt) and crosses a barrier before any wave reads the data.
+__device__ __forceinline__ void dma_x4(u32x4 r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_x1(u32x4 r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+// Barrier after this wave's loads into LDS have landed and its LDS accesses are done.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
-  constexpr int KR = BwdSmem<D>::kRow, SR = BwdSmem<D>::kSRow, BR = BwdSmem<D>::kBRow;
-  constexpr int QN = kRows * (D / 8) / 256;      // 16-byte chunks of a Q (or dO) item per thread
-  constexpr int BN = kRows * (kKeys / 8) / 256;  // 16-byte chunks of the bias (or mask) rows per thread
-  __shared__ BwdSmem<D> sm;
+  using Smem = BwdSmem<D>;
+  constexpr int SR = kRows;
+  constexpr int RPL = 512 / D;          // tile rows filled by one wave load (1 KB): 4 or 8
+  constexpr int QL = kRows / RPL / 4;   // wave loads per Q (or dO) tile and wave: 2 or 1
+  constexpr int CPR = D / 8;            // 16-byte chunks per Q row
+  __shared__ Smem sm;
 
   const int w = blockIdx.x;
   const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
@@ -205,6 +240,15 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const bool has_bias = p.bias != nullptr, has_mask = p.mask != nullptr;
   const float scale2 = p.scale * kLog2eB;
   const uint8_t* st_col = p.state + (int64_t)plane * p.nqb * p.nkb + kb0;  // + qb * nkb (+1)
+
+  // Every item buffer starts as zeros, so a lane of a load that fetches nothing (rows past
+  // lq, keys past lk, SKIP halves) leaves finite values behind whatever the hardware writes
+  // for it: zeros, or the earlier contents of a buffer that only ever held loaded data.
+  {
+    constexpr int kZero = (int)((sizeof(Smem) - sizeof(sm.k)) / 16);
+    u32x4* z = reinterpret_cast<u32x4*>(&sm.q[0][0]);
+    for (int i = tid; i < kZero; i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
+  }
 
   // Is each of the two key blocks non-SKIP for some query block?  The K and V rows of a key
   // block that is SKIP everywhere are never read: they stay zero here (the dQ product runs
@@ -277,55 +321,67 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     return -1;
   };
 
-  // Per-lane 32-bit offsets inside an item; the item's base pointers are uniform (scalar
-  // registers), so no 64-bit per-lane address stays live across items.
-  uint32_t qoff[QN], boff[BN];
+  // Per-lane byte offsets of the item loads.  Wave load n of this wave fills tile rows
+  // (wave * loads + n) * rows-per-load onwards; lane l lands on physical chunk l % chunks-per-row
+  // of row l / chunks-per-row there and fetches the logical chunk the swizzle keeps at that
+  // slot.  The item's base and the rows it may read (past lq the range check returns nothing)
+  // go into the buffer resource.
+  uint32_t qv[QL];
 #pragma unroll
-  for (int n = 0; n < QN; ++n) {
-    const int task = tid + n * 256;
-    qoff[n] = (uint32_t)(task / (D / 8)) * (uint32_t)(p.hq * D) + (uint32_t)(task % (D / 8)) * 8u;
+  for (int n = 0; n < QL; ++n) {
+    const int r = (wave * QL + n) * RPL + lane / CPR;
+    const int c = (lane % CPR) ^ tile_xor<D>(r);
+    qv[n] = (uint32_t)r * (uint32_t)(p.hq * D * 2) + (uint32_t)c * 16u;
   }
+  // bias and mask rows: 128 keys = 16 chunks, 4 rows per wave load, two loads per wave; a
+  // chunk past lk is never fetched, and bh records which key block the chunk is in
+  uint32_t bv[2];
+  bool bh[2];
 #pragma unroll
-  for (int n = 0; n < BN; ++n) {
-    const int task = tid + n * 256;
-    boff[n] = (uint32_t)(task / (kKeys / 8)) * (uint32_t)p.lk + (uint32_t)(task % (kKeys / 8)) * 8u;
+  for (int n = 0; n < 2; ++n) {
+    const int r = (wave * 2 + n) * 4 + lane / 16;
+    const int c = (lane % 16) ^ tile_xor<128>(r);
+    bv[n] = ((int64_t)kb0 * kBlock + c * 8 < p.lk) ? (uint32_t)r * (uint32_t)(p.lk * 2) + (uint32_t)c * 16u : kOutOfRange;
+    bh[n] = c >= 8;
   }
 
-  // Registers that carry the next item while the current one computes.  No branch
-  // surrounds a load (the compiler would wait for every outstanding memory operation,
-  // atomics included, where the paths join): lanes whose data is not needed load an
-  // in-bounds stand-in address and their value is discarded when the item is staged.
-  u32x4 pq[QN], pg[QN], pb[BN], pm[BN];
-  float prow_l, prow_d;
-  auto prefetch = [&](int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
+  // Start the loads of an item into buffer `buf`: Q and dO rows, the raw bias and mask rows
+  // of a new query block (first head of the group only), and the row terms lse and D.
+  auto issue = [&](int buf, int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
     const int64_t h = g * p.G + hh;
     const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
     const int rows_left = (int)min((int64_t)kRows, p.lq - i0);  // >= 1
     const int64_t item = ((bidx * p.lq + i0) * p.hq + h) * D;
+    const uint32_t qbytes = ((uint32_t)(rows_left - 1) * (uint32_t)(p.hq * D) + (uint32_t)D) * 2u;
+    const u32x4 rq = rsrc_words(p.q + item, qbytes), rg = rsrc_words(p.dout + item, qbytes);
 #pragma unroll
-    for (int n = 0; n < QN; ++n) {
-      const int task = tid + n * 256;
-      const uint32_t off = (task / (D / 8) < rows_left) ? qoff[n] : (uint32_t)(task % (D / 8)) * 8u;  // row 0
-      pq[n] = *reinterpret_cast<const u32x4*>(p.q + item + off);
-      pg[n] = *reinterpret_cast<const u32x4*>(p.dout + item + off);
+    for (int n = 0; n < QL; ++n) {
+      const uint32_t dst = (uint32_t)((wave * QL + n) * 1024);
+      dma_x4(rq, lds_addr(&sm.q[buf][0]) + dst, qv[n]);
+      dma_x4(rg, lds_addr(&sm.g[buf][0]) + dst, qv[n]);
     }
     if (hh == 0) {
-      const int64_t boff0 = plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;  // (row i0, key kb0*64): in bounds
-      const uint16_t* bsrc = has_bias ? p.bias + boff0 : p.q;
-      const uint16_t* msrc = has_mask ? p.mask + boff0 : p.q;
+      const int64_t boff0 = plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;
+      const uint32_t bbytes =
+          ((uint32_t)(rows_left - 1) * (uint32_t)p.lk + (uint32_t)min((int64_t)kKeys, p.lk - (int64_t)kb0 * kBlock)) * 2u;
+      if (has_bias) {
+        const u32x4 rb = rsrc_words(p.bias + boff0, bbytes);
 #pragma unroll
-      for (int n = 0; n < BN; ++n) {
-        const int task = tid + n * 256;
-        const int r = task / (kKeys / 8), c = task % (kKeys / 8);
-        const uint8_t st = (c < 8) ? s0 : s1;
-        const bool in = st != kSkip && r < rows_left && (int64_t)kb0 * kBlock + c * 8 < p.lk;
-        pb[n] = *reinterpret_cast<const u32x4*>(bsrc + ((has_bias && in) ? boff[n] : 0u));
-        pm[n] = *reinterpret_cast<const u32x4*>(msrc + ((has_mask && in && st == kPartial) ? boff[n] : 0u));
+        for (int n = 0; n < 2; ++n)
+          dma_x4(rb, lds_addr(&sm.b[buf][0]) + (uint32_t)((wave * 2 + n) * 1024),
+                 ((bh[n] ? s1 : s0) != kSkip) ? bv[n] : kOutOfRange);
+      }
+      if (has_mask) {
+        const u32x4 rm = rsrc_words(p.mask + boff0, bbytes);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          dma_x4(rm, lds_addr(&sm.m[buf][0]) + (uint32_t)((wave * 2 + n) * 1024),
+                 ((bh[n] ? s1 : s0) == kPartial) ? bv[n] : kOutOfRange);
       }
     }
-    const int64_t ridx = (bidx * p.hq + h) * p.lq + i0 + min(tid & (kRows - 1), rows_left - 1);
-    prow_l = p.lse[ridx];
-    prow_d = p.drow[ridx];
+    const int64_t ridx = (bidx * p.hq + h) * p.lq + i0;
+    if (wave == 0) dma_x1(rsrc_words(p.lse + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.lse[buf][0]), (uint32_t)lane * 4u);
+    if (wave == 1) dma_x1(rsrc_words(p.drow + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.dr[buf][0]), (uint32_t)lane * 4u);
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -341,7 +397,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const int trow = (lane & 15) >> 2;
   const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   // Per-lane LDS element offsets, computed once; the loops add compile-time row offsets
-  // only.  The swizzle's XOR term depends on the row modulo 16 (128-wide tiles) or 32 (the
+  // only.  The swizzle's XOR term depends on the row modulo 16 (Q, dO and K tiles) or 32 (the
   // dS^T tile), so adding a multiple of that many rows is a plain add.
   int aoff[D / 16];                  // S/dP operand rows: l32 (+ wave*32 for K)
 #pragma unroll
@@ -361,66 +417,25 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   int sw[4];                         // dS^T writes: row l32 (+ wave*32)
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) sw[gi] = swz32(l32, gi * 8 + hi * 4);
+  int boffr[4];                      // effective bias: rows gi*8 + hi*4 + trow, keys wave*32 + tcol
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) boffr[gi] = swz128(gi * 8 + hi * 4 + trow, wave * 32 + tcol);
 
-  // Write the prefetched item into LDS: Q and dO rows (zero past lq), the effective bias of
-  // the item's rows (first head of the group only; it stays in registers for the others),
-  // and the row terms.
-  auto stage = [&](int qb, int rh, int hh, uint8_t cs0, uint8_t cs1) {
-    const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
-    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
-#pragma unroll
-    for (int n = 0; n < QN; ++n) {
-      const int task = tid + n * 256;
-      const int r = task / (D / 8), c = task % (D / 8);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.q[tile_off<D>(r, c * 8)]) = (r < rows_left) ? pq[n] : z;
-      *reinterpret_cast<u32x4*>(&sm.g[tile_off<D>(r, c * 8)]) = (r < rows_left) ? pg[n] : z;
-    }
-    if (hh == 0) {
-#pragma unroll
-      for (int n = 0; n < BN; ++n) {
-        const int task = tid + n * 256;
-        const int r = task / (kKeys / 8), c = task % (kKeys / 8);
-        const uint8_t st = (c < 8) ? cs0 : cs1;
-        const int64_t i = i0 + r, j0 = (int64_t)kb0 * kBlock + c * 8;
-        const bool inside = i < p.lq && j0 < p.lk && st != kSkip;
-        u32x4 bw = has_bias ? pb[n] : u32x4{0u, 0u, 0u, 0u};
-        if (st != kFull) {
-          const u32x4 mw = has_mask ? pm[n] : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t j = j0 + 2 * e;
-            const bool v0 = inside && attends_lo(mw[e]) && (!p.causal || j <= i + shift);
-            const bool v1 = inside && attends_hi(mw[e]) && (!p.causal || j + 1 <= i + shift);
-            const uint32_t lo = v0 ? (bw[e] & 0xFFFFu) : kNegInfB;
-            const uint32_t hi16 = v1 ? (bw[e] >> 16) : kNegInfB;
-            bw[e] = lo | (hi16 << 16);
-          }
-        }
-        *reinterpret_cast<u32x4*>(&sm.b[r * BR + c * 8]) = bw;
-      }
-    }
-    if (tid < kRows) sm.lse2[tid] = (tid < rows_left) ? prow_l * kLog2eB : INFINITY;
-    else if (tid < 2 * kRows) sm.dr[tid - kRows] = (tid - kRows < rows_left) ? prow_d : 0.f;
-  };
-
-  // Item pipeline: item n+1 is loaded into registers while item n computes, and written
-  // into LDS once item n's Q, dO and bias tiles are no longer read (after the dS^T
-  // barrier), before item n's dQ atomics and dbias stores are issued.  A wait for the
-  // loads therefore never waits for those atomics and stores.
+  // Item pipeline: the loads of item n+1 go straight into the other buffer while item n
+  // computes.  One barrier per item, after the dS^T tile is written: every wave has waited for
+  // its own loads of item n+1 before it, and has finished reading item n's buffers, so the
+  // loads of item n+2 may start after it.  The dS^T tile alternates as well, so its export
+  // after the barrier does not race the next item's writes.
   uint8_t cs0, cs1;  // states of the current item's two key blocks
-  lds_barrier();        // K tile staged
+  lds_barrier();     // K tile staged, buffers zeroed
   int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
-  int rh = 0, hh = 0;
-  if (qb >= 0) {
-    prefetch(qb, 0, 0, cs0, cs1);
-    stage(qb, 0, 0, cs0, cs1);
-  }
-  lds_barrier();
+  int rh = 0, hh = 0, buf = 0;
+  int64_t pbc = p.pair_base[qb >= 0 ? qb : 0];  // first dS tile pair of the current query block
+  if (qb >= 0) issue(0, qb, 0, 0, cs0, cs1);
+  dma_barrier();
 
   while (qb >= 0) {
     const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
-    const int64_t h = g * p.G + hh;
     const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
     const uint8_t my_st = half ? cs1 : cs0;
 
@@ -435,16 +450,38 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         nqb = next_qb(qb - 1, ns0, ns1);
       }
     }
-    if (nqb >= 0) prefetch(nqb, nrh, nhh, ns0, ns1);
+    // first dS tile pair of the next item's query block, used after the next barrier
+    const int64_t pbn = p.pair_base[nqb >= 0 ? nqb : 0];
+    if (nqb >= 0) issue(buf ^ 1, nqb, nrh, nhh, ns0, ns1);
 
+    const uint16_t* qt = sm.q[buf];
+    const uint16_t* gt = sm.g[buf];
     if (hh == 0) {
-      // effective bias in the S layout: row group gi -> rows gi*8 + hi*4 .. +3 of the item
+      // Effective bias in the S layout, from the raw tiles: this lane's key (wave*32 + l32)
+      // and rows gi*8 + hi*4 .. +3 of the item.  Bias where the pair is valid (mask non-zero
+      // and causal order in a PARTIAL block; every in-range pair of a FULL block), -inf
+      // elsewhere, SKIP blocks included.
+      // (Tiles that were not loaded read as zeros: no bias is a zero bias, and the mask
+      // test is dropped without a mask; no branch, so the accumulators stay put.)
+      const bool key_ok = my_st != kSkip && key_abs < p.lk;
+      const bool partial = my_st == kPartial;
+      // causal: row r of the item is valid for this key when r >= key - (lk - lq) - i0
+      const int64_t cfirst = p.causal ? key_abs - shift - i0 : (int64_t)INT32_MIN;
+      const int first_r = (int)max((int64_t)INT32_MIN, min(cfirst, (int64_t)kRows));
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        const i16x4 x = lds_read_tr16(&sm.b[(gi * 8 + hi * 4 + trow) * BR + wave * 32 + tcol]);
-        const u32x2 u = __builtin_bit_cast(u32x2, x);
-        beff[gi][0] = u[0];
-        beff[gi][1] = u[1];
+        const i16x4 xb = lds_read_tr16(&sm.b[buf][boffr[gi]]);
+        const i16x4 xm = lds_read_tr16(&sm.m[buf][boffr[gi]]);
+        uint32_t e16[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = gi * 8 + hi * 4 + e;
+          const bool pv = (!has_mask || (xm[e] & 0x7FFF) != 0) && r >= first_r;
+          const bool v = key_ok && r < rows_left && (!partial || pv);
+          e16[e] = v ? (uint32_t)(uint16_t)xb[e] : (uint32_t)kNegInfB;
+        }
+        beff[gi][0] = e16[0] | (e16[1] << 16);
+        beff[gi][1] = e16[2] | (e16[3] << 16);
       }
       dbacc = f32x16{};
     }
@@ -456,23 +493,23 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[aoff[s] + wave * 32 * KR]);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[aoff[s]]);
+      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[aoff[s] + wave * 32 * D]);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&qt[aoff[s]]);
       sacc = mfma32(aq, kbs, sacc);
-      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[aoff[s]]);
+      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&gt[aoff[s]]);
       pacc = mfma32(ag, vreg[s], pacc);
     }
     // ---- P = exp(S - lse) on valid entries, dS = P (dP - D) -----------------------------
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       const int q0 = gi * 8 + hi * 4;
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[q0]);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dr[q0]);
+      const f32x4 ls = *reinterpret_cast<const f32x4*>(&sm.lse[buf][q0]);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dr[buf][q0]);
       const float bb[4] = {bf16_lo(beff[gi][0]), bf16_hi(beff[gi][0]), bf16_lo(beff[gi][1]), bf16_hi(beff[gi][1])};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = gi * 4 + e;
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale2, fmaf(bb[e], kLog2eB, -l2[e])));
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale2, (bb[e] - ls[e]) * kLog2eB));
         // a SKIP half gives exactly zero whatever its K/V hold, so dQ can take all 128 keys
         const float ds = (my_st != kSkip) ? pv * (pacc[i] - dd[e]) : 0.f;
         sacc[i] = (my_st != kSkip) ? pv : 0.f;
@@ -483,33 +520,34 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     // ---- dV += P^T dO, dK += dS^T Q: two k-steps of 16 queries ----------------------------
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u32x4 pw, sw;
+      u32x4 pw, sw2;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pw[e] = pack_bf16x2(sacc[ks * 8 + 2 * e], sacc[ks * 8 + 2 * e + 1]);
-        sw[e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
+        sw2[e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
       }
-      const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw);
-      const int rk = ks * 16 * KR;  // this k-step's rows: a compile-time offset
+      const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw2);
+      const int rk = ks * 16 * D;  // this k-step's rows: a compile-time offset
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const i16x4 g0 = lds_read_tr16(&sm.g[gq0[dt] + rk]);
-        const i16x4 g1 = lds_read_tr16(&sm.g[gq1[dt] + rk]);
+        const i16x4 g0 = lds_read_tr16(&gt[gq0[dt] + rk]);
+        const i16x4 g1 = lds_read_tr16(&gt[gq1[dt] + rk]);
         dv[dt] = mfma32(ap, join_bf16x8(g0, g1), dv[dt]);
-        const i16x4 q0 = lds_read_tr16(&sm.q[gq0[dt] + rk]);
-        const i16x4 q1 = lds_read_tr16(&sm.q[gq1[dt] + rk]);
+        const i16x4 q0 = lds_read_tr16(&qt[gq0[dt] + rk]);
+        const i16x4 q1 = lds_read_tr16(&qt[gq1[dt] + rk]);
         dk[dt] = mfma32(as, join_bf16x8(q0, q1), dk[dt]);
       }
     }
     // ---- dS^T row of this lane's key: 4 consecutive queries per row group -----------------
+    uint16_t* st_tile = sm.s[buf];
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       u32x2 w2;
       w2[0] = pack_bf16x2(pacc[gi * 4 + 0], pacc[gi * 4 + 1]);
       w2[1] = pack_bf16x2(pacc[gi * 4 + 2], pacc[gi * 4 + 3]);
-      *reinterpret_cast<u32x2*>(&sm.s[sw[gi] + wave * 32 * SR]) = w2;
+      *reinterpret_cast<u32x2*>(&st_tile[sw[gi] + wave * 32 * SR]) = w2;
     }
-    lds_barrier();
+    dma_barrier();  // dS^T complete; the next item's buffers are loaded; this item's are free
 
     // ---- dS of the item to the workspace, in the order the dQ kernel reads it --------------
     // 16-byte chunk c holds keys (c/64)*16 + ((c/32)%2)*8 .. +7 of query row c%32.  This lane
@@ -518,18 +556,16 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     // lanes store consecutive chunks.
     {
       uint16_t* tile =
-          p.ds + ((((int64_t)plane * p.npairs + p.pair_base[qb] + KB) * p.G + hh) * 2 + rh) * (kRows * kKeys);
+          p.ds + ((((int64_t)plane * p.npairs + pbc + KB) * p.G + hh) * 2 + rh) * (kRows * kKeys);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int ks = wave + 4 * hf;
         const int sofs = (ks >> 1) * 32 * SR;
-        const i16x4 a0 = lds_read_tr16(&sm.s[sq[ks & 1][0] + sofs]);
-        const i16x4 a1 = lds_read_tr16(&sm.s[sq[ks & 1][1] + sofs]);
+        const i16x4 a0 = lds_read_tr16(&st_tile[sq[ks & 1][0] + sofs]);
+        const i16x4 a1 = lds_read_tr16(&st_tile[sq[ks & 1][1] + sofs]);
         *reinterpret_cast<bf16x8*>(tile + (tid + 256 * hf) * 8) = join_bf16x8(a0, a1);
       }
     }
-    // the next item's tiles go in now (the export above reads only dS^T)
-    if (nqb >= 0) stage(nqb, nrh, nhh, ns0, ns1);
 
     // ---- dBias of the item's rows, summed over the group: store after the last head -------------
     if (hh == p.G - 1 && p.dbias != nullptr) {
@@ -547,7 +583,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dbacc[i]), r, lane_off + rc * rb, 0, 0);
       }
     }
-    lds_barrier();  // the next item's tiles are visible; every dS^T read is done before it is rewritten
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
+    buf ^= 1;
+    pbc = pbn;
     qb = nqb;
     rh = nrh;
     hh = nhh;

@@ -42,26 +42,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// LDS tile layouts.  A [rows][128] bf16 tile stores the 16-byte chunk c of row r at chunk
-// c ^ (4*(r%4) + (r/4)%4), rows unpadded.  With that, a 128-bit operand read (16 lanes on
-// 16 consecutive rows, one chunk each) and a transposing 64-bit read (4 consecutive rows x
-// 32 bytes per 16-lane group) both touch every bank once per cycle.  Narrower tiles keep
-// an 8-element row pad.
+// LDS tile layouts.  A [rows][D] bf16 tile stores the 16-byte chunk c of row r at chunk
+// c ^ tile_xor<D>(r), rows unpadded.  For D = 128 the XOR is 4*(r%4) + (r/4)%4: a 128-bit
+// operand read (16 lanes on 16 consecutive rows, one chunk each) and a transposing 64-bit
+// read (4 consecutive rows x 32 bytes per 16-lane group) both touch every bank once per
+// cycle.  For D = 64 it is (r/2)%8.  Every row offset that is a multiple of 16 leaves the
+// XOR unchanged, so such offsets add to a per-lane base.  Whole 16-byte chunks stay
+// together, which lets a buffer load write a tile straight into LDS (each lane fetches the
+// global chunk that belongs at its slot).
+template <int D>
+__device__ __forceinline__ int tile_xor(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return (row >> 1) & 7;
+  }
+}
 __device__ __forceinline__ int swz128(int row, int col) {
-  const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-  return (row << 7) | ((((col >> 3) ^ f) << 3) | (col & 7));
+  return (row << 7) | ((((col >> 3) ^ tile_xor<128>(row)) << 3) | (col & 7));
 }
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
-  if constexpr (D == 128) {
-    return swz128(row, col);
-  } else {
-    return row * (D + 8) + col;
-  }
+  return row * D + ((((col >> 3) ^ tile_xor<D>(row)) << 3) | (col & 7));
 }
 template <int D>
 constexpr int tile_row() {
-  return D == 128 ? 128 : D + 8;
+  return D;
 }
 // A [rows][32] bf16 tile stores the 8-byte unit u of row r at unit u ^ ((r/4)%8): conflict
 // free for 8-byte writes of 32 consecutive rows and for transposing reads of 4-row groups.

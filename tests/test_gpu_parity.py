@@ -144,3 +144,34 @@ def test_skipped_tiles_do_not_leak():
     for a, b in zip([H.bits(t) for t in (dc.dk, dc.dv, dc.dbias)], g1):
         assert np.array_equal(a, b)
     assert np.array_equal(H.f64(dc.dq), dq1)
+
+
+def test_memory_after_inputs_is_never_read():
+    """Every input sits at the start of a larger buffer whose remainder is NaN.  Ragged query
+    rows and key columns at the end of the tensors are clipped by the kernels' range checks,
+    so the outputs are bit-identical to those of plain allocations."""
+    import gpu_harness as H
+
+    c = Case("nan_after_inputs", 26, 1, 200, 200, 8, 2, 128, True, "blocks")
+    dc = H.DeviceCase(c)
+    dc.classify()
+    dc.forward()
+    dc.backward()
+    torch.cuda.synchronize()
+    ref = [H.bits(t) for t in (dc.o, dc.dq, dc.dk, dc.dv, dc.dbias)] + [dc.lse.cpu().numpy()]
+
+    def padded(t):
+        big = torch.full((t.numel() + 65536,), float("nan"), dtype=t.dtype, device="cuda")
+        view = big[: t.numel()].view(t.shape)
+        view.copy_(t)
+        return view
+
+    dc.q, dc.k, dc.v, dc.do, dc.mask, dc.bias = (padded(t) for t in (dc.q, dc.k, dc.v, dc.do, dc.mask, dc.bias))
+    dc.classify()
+    dc.forward()
+    dc.o, dc.lse = padded(dc.o), padded(dc.lse)
+    dc.backward()
+    torch.cuda.synchronize()
+    got = [H.bits(t) for t in (dc.o, dc.dq, dc.dk, dc.dv, dc.dbias)] + [dc.lse.cpu().numpy()]
+    for name, a, b in zip(("o", "dq", "dk", "dv", "dbias", "lse"), ref, got):
+        assert np.array_equal(a, b), f"{name} changed"
