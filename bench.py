@@ -38,9 +38,65 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps, so that a hardware counter "
                          "pass can relate its FETCH_SIZE / WRITE_SIZE to known bytes")
-    ap.add_argument("--traffic-json", default=None,
-                    help="JSON with measured HBM bytes per launch of the dominant call (from counter passes)")
+    ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
+                    help="measured HBM bytes per launch (written by --summarize-traffic); used only while the "
+                         "kernel sources still hash to the value recorded in it")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("COUNTER_DIR", "OUT_JSON"), default=None,
+                    help="turn two rocprofv3 counter passes (FETCH_SIZE and WRITE_SIZE csv files under "
+                         "COUNTER_DIR, each over a run with --calibrate-copy-mib N; give the same N here) into "
+                         "bytes per launch, then exit")
     return ap.parse_args()
+
+
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "headline_traffic.json")
+KERNEL_SOURCES = ["classify.hip", "fwd.hip", "bwd.hip", "common.h"]
+# kernels of each C-ABI call, matched by substring of the demangled name
+CALL_KERNELS = {"classify": ["classify_kernel"], "fwd": ["fwd_kernel"],
+                "bwd": ["bwd_pre_kernel", "kt_kernel", "pair_base_kernel", "bwd_main_kernel", "dq_kernel"]}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_dynamic_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_traffic(counter_dir: str, out_json: str, copy_mib: int):
+    """HBM bytes per launch of each call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+
+    Each counter is scaled by the ratio of known bytes to what it reads for the calibration
+    copy (a device copy of --calibrate-copy-mib MiB: that many bytes fetched and written)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    assert copy_mib > 0, "give the calibration copy's size with --calibrate-copy-mib"
+    out = {"source_hash": kernel_source_hash(), "calibration_mib": copy_mib, "counters": {}}
+    per_call = defaultdict(float)
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        files = glob.glob(os.path.join(counter_dir, "**", f"{counter}_counter_collection.csv"), recursive=True)
+        assert len(files) == 1, f"expected one {counter} csv under {counter_dir}, found {files}"
+        per = defaultdict(list)
+        for r in csv.DictReader(open(files[0])):
+            if r["Counter_Name"] == counter:
+                per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        copy = [max(v) for k, v in per.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+        assert copy, "no calibration copy kernel in the counter pass"
+        copy_kib = max(copy)
+        factor = copy_mib * 1024.0 / copy_kib
+        out["counters"][counter] = {"copy_kib": copy_kib, "factor": factor}
+        for call, subs in CALL_KERNELS.items():
+            for name, vals in per.items():
+                if any(sub in name for sub in subs):
+                    per_call[call] += sum(vals) / len(vals) * 1024.0 * factor
+    out["bytes_per_launch"] = {k: round(v) for k, v in per_call.items()}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def block_counts(state):
@@ -95,6 +151,9 @@ def cpu_baseline(c, blocks: int, f_total: float):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.calibrate_copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (each (batch, kv head) plane "
               "is independent, so several GPUs would each run this one-GPU kernel on their share).",
@@ -188,11 +247,12 @@ def main():
     dom = max(phases, key=lambda k: phases[k][0])
     t_dom, f_dom, dom_name = phases[dom]
     achieved = f_dom / (t_dom * 1e-3) / 1e12
-    traffic = None
-    if args.traffic_json:
+    traffic = None  # measured HBM bytes per launch, only while the kernels are the ones measured
+    if args.traffic_json and os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             tj = json.load(f)
-        traffic = tj.get(dom)  # bytes per launch, measured for these kernels
+        if tj.get("source_hash") == kernel_source_hash():
+            traffic = tj["bytes_per_launch"].get(dom)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
                 "ms_per_launch": round(t_dom, 4)}
