@@ -1,5 +1,6 @@
 // C ABI of libdma.so: argument validation and dispatch to the gfx950 kernels.
 // Declarations, layouts and error behaviour are documented in include/dma.h.
+#include <cmath>
 #include "../../include/dma.h"
 
 #include "common.h"
@@ -98,12 +99,12 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
 
 namespace {
 // Byte offsets of the backward's workspace regions, each 256-byte aligned:
-//   drow       fp32 [b, hq, lq]                    D = rowsum(dO * O)
+//   rows       fp32 2 x [b, hq, lq]                -rowsum(dO * O), then -lse * log2(e)
 //   pair_base  int64 [nqb + 1]                     first dS tile pair of each query block
 //   kt         bf16 [b, hkv, d, nkb2 * 128]        K transposed
 //   ds         bf16 [b, hkv, npairs, G, 2, 32*128] dS tiles of every live (query block, key pair)
 struct WsLayout {
-  size_t drow, pair_base, kt, ds, total;
+  size_t rows, pair_base, kt, ds, total;
   int64_t npairs;
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -113,8 +114,8 @@ WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, i
   int64_t np = 0;
   for (int64_t qb = 0; qb < nqb; ++qb) np += dma::live_pairs(qb, lq, lk, causal);
   w.npairs = np;
-  w.drow = 0;
-  w.pair_base = w.drow + up256((size_t)b * hq * lq * sizeof(float));
+  w.rows = 0;
+  w.pair_base = w.rows + up256((size_t)2 * b * hq * lq * sizeof(float));
   w.kt = w.pair_base + up256((size_t)(nqb + 1) * sizeof(int64_t));
   w.ds = w.kt + up256((size_t)b * hkv * d * nkb2 * 128 * sizeof(uint16_t));
   w.total = w.ds + up256((size_t)b * hq * np * 2 * 32 * 128 * sizeof(uint16_t));
@@ -141,8 +142,10 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
       !aligned_or_null(dbias) || !aligned16(workspace))
     return DMA_ERR_INVALID_ARGUMENT;
   if (dbias && lk % 8 != 0) return DMA_ERR_INVALID_ARGUMENT;
-  // per-row byte ranges of dbias must stay within 32-bit offsets
-  if (lk > (int64_t(1) << 24)) return DMA_ERR_UNSUPPORTED;
+  // the scores are carried as S + bias / scale: scale must be finite and nonzero
+  if (!(scale != 0.f) || !std::isfinite(scale)) return DMA_ERR_INVALID_ARGUMENT;
+  // per-row byte ranges of dbias and row indices must stay within 32-bit offsets
+  if (lk > (int64_t(1) << 24) || lq > (int64_t(1) << 24)) return DMA_ERR_UNSUPPORTED;
   const WsLayout wl = ws_layout(b, lq, lk, hq, hkv, d, is_causal);
   if (workspace_bytes < wl.total) return DMA_ERR_WORKSPACE_TOO_SMALL;
   dma::AttnArgs a = {};
@@ -160,7 +163,8 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   a.dv = dv;
   a.dbias = dbias;
   char* ws = static_cast<char*>(workspace);
-  a.drow = reinterpret_cast<float*>(ws + wl.drow);
+  a.nd = reinterpret_cast<float*>(ws + wl.rows);
+  a.nl2 = a.nd + b * hq * lq;
   a.pair_base = reinterpret_cast<int64_t*>(ws + wl.pair_base);
   a.kt = reinterpret_cast<uint16_t*>(ws + wl.kt);
   a.ds = reinterpret_cast<uint16_t*>(ws + wl.ds);

@@ -9,7 +9,7 @@
 //   dBias[g] = sum over the query heads of group g of dS.
 //
 // Kernels:
-//   bwd_pre_kernel    D = rowsum(dO * O).
+//   bwd_pre_kernel    row terms -D = -rowsum(dO * O) and -lse log2(e).
 //   kt_kernel         K transposed ([b, g, d, keys]), the A operand of the dQ products.
 //   pair_base_kernel  offsets of each query block's dS tiles (live 128-key pairs before it).
 //   bwd_main_kernel   one workgroup per (batch, kv head g, 128 keys = two
@@ -55,8 +55,11 @@ constexpr float kLog2eB = 1.4426950408889634f;
 constexpr uint16_t kNegInfB = 0xFF80u;
 
 // ---------------------------------------------------------------------------
+// Row terms of the backward, in the [b, hq, lq] order the main kernel loads them:
+// nd = -rowsum(dO * O) (so the dP accumulator starts at -D) and nl2 = -lse * log2(e).
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                      float* __restrict__ drow, int64_t rows, int64_t lq, int64_t hq,
+                                                      const float* __restrict__ lse, float* __restrict__ nd,
+                                                      float* __restrict__ nl2, int64_t rows, int64_t lq, int64_t hq,
                                                       int d) {
   // rows = b * lq * hq (row index = (b*lq + i)*hq + h); d/8 lanes per row.
   const int lpr = d / 8;
@@ -74,7 +77,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   if (r < rows && c == 0) {
     const int64_t h = r % hq, bi = r / hq;  // bi = b*lq + i
     const int64_t bb = bi / lq, i = bi % lq;
-    drow[(bb * hq + h) * lq + i] = acc;
+    const int64_t dst = (bb * hq + h) * lq + i;
+    nd[dst] = -acc;
+    nl2[dst] = -lse[dst] * kLog2eB;
   }
 }
 
@@ -147,8 +152,8 @@ struct BwdParams {
   const uint16_t* bias;
   const uint8_t* state;
   const uint16_t* dout;
-  const float* lse;
-  const float* drow;
+  const float* nl2;  // -lse * log2(e), fp32 [b, hq, lq]
+  const float* nd;   // -D, fp32 [b, hq, lq]
   const int64_t* pair_base;
   uint16_t* ds;
   int64_t npairs;
@@ -170,15 +175,18 @@ struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay s
   static constexpr int kTile = kRows * D;       // Q or dO tile [row][d], tile_off<D> layout
   static constexpr int kBTile = kRows * kKeys;  // raw bias or mask tile [row][key], swz128 layout
   static constexpr int kSTile = kKeys * kRows;  // dS^T [key][query], swz32 layout
-  uint16_t k[kKeys * D];  // K of the workgroup's keys, tile_off<D> layout
   // Two buffers each: the current item's and the next item's, which loads meanwhile.
   uint16_t q[2][kTile];
   uint16_t g[2][kTile];
   uint16_t b[2][kBTile];
   uint16_t m[2][kBTile];
   uint16_t s[2][kSTile];
-  float lse[2][64];  // rows 32..63 take the out-of-range lanes of the load
-  float dr[2][64];   // D = rowsum(dO * O)
+  float nl2[2][64];  // -lse * log2(e) of the item's rows (rows 32..63 take the out-of-range lanes of the load)
+  float nd[2][64];   // -D = -rowsum(dO * O)
+  // Initial values of the S accumulator in the S layout, one slot per lane: bias / scale on
+  // valid pairs, -inf (signed so that scale * it is -inf) elsewhere.  Written when a query
+  // block starts, read by the same lane for every head of the group.
+  f32x4 beff[4][4][64];  // [wave][row group][lane]
   uint8_t st[2][kStateChunk];  // block states of the two key blocks for a range of query blocks
 };
 
@@ -199,7 +207,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // its offset `voff` in buffer `r` and they land at LDS byte address lds + 16 l (or + 4 l).
 // Lanes whose offset is out of the buffer's range fetch nothing.  The compiler does not see
 // these LDS writes, so it neither waits for them nor orders LDS reads after them: the kernel
-// waits for them (vmcnt) and crosses a barrier before any wave reads the data.
+// waits for them (vmcnt) and crosses a barrier before any wave reads the data.  Nothing else
+// in these kernels uses M0.
 __device__ __forceinline__ void dma_x4(u32x4 r, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");
@@ -237,15 +246,17 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const int64_t key_abs = (int64_t)kb0 * kBlock + key_loc;
   const int64_t shift = p.lk - p.lq;
   const int64_t plane_off = (int64_t)plane * p.lq * p.lk;
-  const bool has_bias = p.bias != nullptr, has_mask = p.mask != nullptr;
+  const bool has_mask = p.mask != nullptr;
   const float scale2 = p.scale * kLog2eB;
+  const float inv_scale = 1.f / p.scale;
+  const float neg_inf_s = p.scale > 0.f ? -INFINITY : INFINITY;  // scale * neg_inf_s = -inf
   const uint8_t* st_col = p.state + (int64_t)plane * p.nqb * p.nkb + kb0;  // + qb * nkb (+1)
 
   // Every item buffer starts as zeros, so a lane of a load that fetches nothing (rows past
   // lq, keys past lk, SKIP halves) leaves finite values behind whatever the hardware writes
   // for it: zeros, or the earlier contents of a buffer that only ever held loaded data.
   {
-    constexpr int kZero = (int)((sizeof(Smem) - sizeof(sm.k)) / 16);
+    constexpr int kZero = (int)(sizeof(Smem) / 16);
     u32x4* z = reinterpret_cast<u32x4*>(&sm.q[0][0]);
     for (int i = tid; i < kZero; i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -264,24 +275,21 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     live[1] = __syncthreads_or(any1) != 0;
   }
 
-  // this lane's key row of V: B operand of dP = dO V^T (d = s*16 + hi*8 ..); the K operand of
-  // S = Q K^T is read from the staged K tile
-  bf16x8 vreg[D / 16];
+  // this lane's key rows of K and V, the B operands of S = Q K^T and dP = dO V^T
+  // (d = s*16 + hi*8 ..), held in registers for the whole kernel
+  bf16x8 kreg[D / 16], vreg[D / 16];
   {
     const int64_t off = ((bidx * p.lk + key_abs) * p.hkv + g) * D + hi * 8;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      u32x4 vw = {0u, 0u, 0u, 0u};
-      if (key_abs < p.lk && live[half]) vw = *reinterpret_cast<const u32x4*>(p.v + off + s * 16);
+      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+      if (key_abs < p.lk && live[half]) {
+        kw = *reinterpret_cast<const u32x4*>(p.k + off + s * 16);
+        vw = *reinterpret_cast<const u32x4*>(p.v + off + s * 16);
+      }
+      kreg[s] = __builtin_bit_cast(bf16x8, kw);
       vreg[s] = __builtin_bit_cast(bf16x8, vw);
     }
-  }
-  for (int task = tid; task < kKeys * (D / 8); task += 256) {
-    const int r = task / (D / 8), c = task % (D / 8);
-    const int64_t key = (int64_t)kb0 * kBlock + r;
-    u32x4 kw = {0u, 0u, 0u, 0u};
-    if (key < p.lk && live[r >> 6]) kw = *reinterpret_cast<const u32x4*>(p.k + ((bidx * p.lk + key) * p.hkv + g) * D + c * 8);
-    *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = kw;
   }
 
   // Query blocks are walked from the last to the first: the workgroups of one XCD start
@@ -344,44 +352,49 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     bv[n] = ((int64_t)kb0 * kBlock + c * 8 < p.lk) ? (uint32_t)r * (uint32_t)(p.lk * 2) + (uint32_t)c * 16u : kOutOfRange;
     bh[n] = c >= 8;
   }
+  const uint16_t* q_plane = p.q + (bidx * p.lq * p.hq + g * p.G) * D;     // + (i * hq + hh) * D
+  const uint16_t* g_plane = p.dout + (bidx * p.lq * p.hq + g * p.G) * D;
+  const float* nl2_plane = p.nl2 + (bidx * p.hq + g * p.G) * p.lq;       // + hh * lq + i
+  const float* nd_plane = p.nd + (bidx * p.hq + g * p.G) * p.lq;
+  const uint16_t* bias_plane = p.bias + plane_off + (int64_t)kb0 * kBlock;  // + i * lk
+  const uint16_t* mask_plane = p.mask + plane_off + (int64_t)kb0 * kBlock;
+  const uint32_t qrow_bytes = (uint32_t)(p.hq * D * 2);
+  const uint32_t krange = (uint32_t)min((int64_t)kKeys, p.lk - (int64_t)kb0 * kBlock) * 2u;
 
-  // Start the loads of an item into buffer `buf`: Q and dO rows, the raw bias and mask rows
-  // of a new query block (first head of the group only), and the row terms lse and D.
-  auto issue = [&](int buf, int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
-    const int64_t h = g * p.G + hh;
-    const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
-    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);  // >= 1
-    const int64_t item = ((bidx * p.lq + i0) * p.hq + h) * D;
-    const uint32_t qbytes = ((uint32_t)(rows_left - 1) * (uint32_t)(p.hq * D) + (uint32_t)D) * 2u;
-    const u32x4 rq = rsrc_words(p.q + item, qbytes), rg = rsrc_words(p.dout + item, qbytes);
+  // Start the loads of an item into buffer B: Q and dO rows, the raw bias and mask rows of a
+  // new query block (first head of the group only), and the row terms.
+  auto issue = [&](int B, int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
+    const int i0 = qb * kBlock + rh * kRows;
+    const int rows_left = min(kRows, (int)p.lq - i0);  // >= 1
+    const int64_t item = ((int64_t)i0 * p.hq + hh) * D;
+    const uint32_t qbytes = (uint32_t)(rows_left - 1) * qrow_bytes + (uint32_t)D * 2u;
+    const u32x4 rq = rsrc_words(q_plane + item, qbytes), rg = rsrc_words(g_plane + item, qbytes);
 #pragma unroll
     for (int n = 0; n < QL; ++n) {
       const uint32_t dst = (uint32_t)((wave * QL + n) * 1024);
-      dma_x4(rq, lds_addr(&sm.q[buf][0]) + dst, qv[n]);
-      dma_x4(rg, lds_addr(&sm.g[buf][0]) + dst, qv[n]);
+      dma_x4(rq, lds_addr(&sm.q[B][0]) + dst, qv[n]);
+      dma_x4(rg, lds_addr(&sm.g[B][0]) + dst, qv[n]);
     }
     if (hh == 0) {
-      const int64_t boff0 = plane_off + i0 * p.lk + (int64_t)kb0 * kBlock;
-      const uint32_t bbytes =
-          ((uint32_t)(rows_left - 1) * (uint32_t)p.lk + (uint32_t)min((int64_t)kKeys, p.lk - (int64_t)kb0 * kBlock)) * 2u;
-      if (has_bias) {
-        const u32x4 rb = rsrc_words(p.bias + boff0, bbytes);
+      const uint32_t bbytes = (uint32_t)(rows_left - 1) * (uint32_t)p.lk * 2u + krange;
+      if (p.bias != nullptr) {
+        const u32x4 rb = rsrc_words(bias_plane + (int64_t)i0 * p.lk, bbytes);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
-          dma_x4(rb, lds_addr(&sm.b[buf][0]) + (uint32_t)((wave * 2 + n) * 1024),
+          dma_x4(rb, lds_addr(&sm.b[B][0]) + (uint32_t)((wave * 2 + n) * 1024),
                  ((bh[n] ? s1 : s0) != kSkip) ? bv[n] : kOutOfRange);
       }
       if (has_mask) {
-        const u32x4 rm = rsrc_words(p.mask + boff0, bbytes);
+        const u32x4 rm = rsrc_words(mask_plane + (int64_t)i0 * p.lk, bbytes);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
-          dma_x4(rm, lds_addr(&sm.m[buf][0]) + (uint32_t)((wave * 2 + n) * 1024),
+          dma_x4(rm, lds_addr(&sm.m[B][0]) + (uint32_t)((wave * 2 + n) * 1024),
                  ((bh[n] ? s1 : s0) == kPartial) ? bv[n] : kOutOfRange);
       }
     }
-    const int64_t ridx = (bidx * p.hq + h) * p.lq + i0;
-    if (wave == 0) dma_x1(rsrc_words(p.lse + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.lse[buf][0]), (uint32_t)lane * 4u);
-    if (wave == 1) dma_x1(rsrc_words(p.drow + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.dr[buf][0]), (uint32_t)lane * 4u);
+    const int64_t ridx = (int64_t)hh * p.lq + i0;
+    if (wave == 0) dma_x1(rsrc_words(nl2_plane + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.nl2[B][0]), (uint32_t)lane * 4u);
+    if (wave == 1) dma_x1(rsrc_words(nd_plane + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.nd[B][0]), (uint32_t)lane * 4u);
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -391,35 +404,27 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     dv[dt] = f32x16{};
   }
   f32x16 dbacc = f32x16{};
-  uint32_t beff[4][2];  // effective bias of this lane's (query, key) pairs, bf16 pairs
 
   // tr-read addressing: inside a 16-lane group, lane s points at row +s/4, column +4(s%4)
   const int trow = (lane & 15) >> 2;
   const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  // Per-lane LDS element offsets, computed once; the loops add compile-time row offsets
-  // only.  The swizzle's XOR term depends on the row modulo 16 (Q, dO and K tiles) or 32 (the
-  // dS^T tile), so adding a multiple of that many rows is a plain add.
-  int aoff[D / 16];                  // S/dP operand rows: l32 (+ wave*32 for K)
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) aoff[s] = tile_off<D>(l32, s * 16 + hi * 8);
-  int gq0[D / 32], gq1[D / 32];      // dV/dK transposing reads: rows hi*4 + trow (+8), + ks*16
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    gq0[dt] = tile_off<D>(hi * 4 + trow, dt * 32 + tcol);
-    gq1[dt] = tile_off<D>(hi * 4 + trow + 8, dt * 32 + tcol);
-  }
+  // Per-lane LDS element offsets.  The swizzles XOR a per-row term into the 16-byte chunk
+  // index, so the offsets of the other column steps of one lane follow from the first by an
+  // XOR with a constant (bits 4 and up of the element offset), and a whole number of 16-row
+  // (Q, dO, K) or 32-row (dS^T) steps adds a constant: one base per lane, the rest in the
+  // instruction stream.  Buffer 1 of a tile sits one tile above buffer 0, beyond every bit
+  // the XORs touch.
+  const int aoff0 = tile_off<D>(l32, hi * 8);              // S/dP operands, column step s: ^ (s << 4)
+  const int goff0 = tile_off<D>(hi * 4 + trow, tcol);        // dV/dK tr reads, column step dt: ^ (dt << 5)
+  constexpr int kG1Xor = D == 128 ? 16 : 32;                 // 8 rows further down: + 8 D, then ^ this
+  const int swoff0 = swz32(l32, hi * 4) + wave * 32 * SR;    // dS^T writes, row group gi: ^ (gi << 3)
   int sq[2][2];                      // dS export, dS^T rows (ks%2)*16 + hi*8 + trow (+4), + (ks/2)*32
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     sq[par][0] = swz32(par * 16 + hi * 8 + trow, tcol);
     sq[par][1] = swz32(par * 16 + hi * 8 + trow + 4, tcol);
   }
-  int sw[4];                         // dS^T writes: row l32 (+ wave*32)
-#pragma unroll
-  for (int gi = 0; gi < 4; ++gi) sw[gi] = swz32(l32, gi * 8 + hi * 4);
-  int boffr[4];                      // effective bias: rows gi*8 + hi*4 + trow, keys wave*32 + tcol
-#pragma unroll
-  for (int gi = 0; gi < 4; ++gi) boffr[gi] = swz128(gi * 8 + hi * 4 + trow, wave * 32 + tcol);
+  const int boff0 = swz128(hi * 4 + trow, wave * 32 + tcol);  // raw bias and mask tiles, row group 0
 
   // Item pipeline: the loads of item n+1 go straight into the other buffer while item n
   // computes.  One barrier per item, after the dS^T tile is written: every wave has waited for
@@ -427,16 +432,18 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   // loads of item n+2 may start after it.  The dS^T tile alternates as well, so its export
   // after the barrier does not race the next item's writes.
   uint8_t cs0, cs1;  // states of the current item's two key blocks
-  lds_barrier();     // K tile staged, buffers zeroed
+  lds_barrier();     // buffers zeroed
   int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
-  int rh = 0, hh = 0, buf = 0;
+  int rh = 0, hh = 0;
   int64_t pbc = p.pair_base[qb >= 0 ? qb : 0];  // first dS tile pair of the current query block
+  int buf = 0;
   if (qb >= 0) issue(0, qb, 0, 0, cs0, cs1);
   dma_barrier();
 
   while (qb >= 0) {
-    const int64_t i0 = (int64_t)qb * kBlock + rh * kRows;
-    const int rows_left = (int)min((int64_t)kRows, p.lq - i0);
+    const int B = buf;
+    const int i0 = qb * kBlock + rh * kRows;
+    const int rows_left = min(kRows, (int)p.lq - i0);
     const uint8_t my_st = half ? cs1 : cs0;
 
     // ---- start loading the next item ------------------------------------------------
@@ -452,17 +459,13 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     }
     // first dS tile pair of the next item's query block, used after the next barrier
     const int64_t pbn = p.pair_base[nqb >= 0 ? nqb : 0];
-    if (nqb >= 0) issue(buf ^ 1, nqb, nrh, nhh, ns0, ns1);
+    if (nqb >= 0) issue(B ^ 1, nqb, nrh, nhh, ns0, ns1);
 
-    const uint16_t* qt = sm.q[buf];
-    const uint16_t* gt = sm.g[buf];
     if (hh == 0) {
-      // Effective bias in the S layout, from the raw tiles: this lane's key (wave*32 + l32)
-      // and rows gi*8 + hi*4 .. +3 of the item.  Bias where the pair is valid (mask non-zero
-      // and causal order in a PARTIAL block; every in-range pair of a FULL block), -inf
-      // elsewhere, SKIP blocks included.
-      // (Tiles that were not loaded read as zeros: no bias is a zero bias, and the mask
-      // test is dropped without a mask; no branch, so the accumulators stay put.)
+      // S-layout initial values from the raw tiles: this lane's key (wave*32 + l32) and rows
+      // gi*8 + hi*4 .. +3 of the item.  A pair is valid when it is in range and its block is
+      // FULL, or PARTIAL with a non-zero mask (none given: every pair) in causal order.
+      // Tiles that were not loaded read as zeros, and a zero bias is no bias.
       const bool key_ok = my_st != kSkip && key_abs < p.lk;
       const bool partial = my_st == kPartial;
       // causal: row r of the item is valid for this key when r >= key - (lk - lq) - i0
@@ -470,54 +473,85 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       const int first_r = (int)max((int64_t)INT32_MIN, min(cfirst, (int64_t)kRows));
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        const i16x4 xb = lds_read_tr16(&sm.b[buf][boffr[gi]]);
-        const i16x4 xm = lds_read_tr16(&sm.m[buf][boffr[gi]]);
-        uint32_t e16[4];
+        // 8 rows down the row term of the swizzle flips chunk bit 1 (element bit 4)
+        const int bo = (boff0 + gi * 8 * 128) ^ ((gi & 1) << 4);
+        const i16x4 xb = lds_read_tr16(&sm.b[B][bo]);
+        const i16x4 xm = lds_read_tr16(&sm.m[B][bo]);
+        f32x4 iv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = gi * 8 + hi * 4 + e;
           const bool pv = (!has_mask || (xm[e] & 0x7FFF) != 0) && r >= first_r;
           const bool v = key_ok && r < rows_left && (!partial || pv);
-          e16[e] = v ? (uint32_t)(uint16_t)xb[e] : (uint32_t)kNegInfB;
+          iv[e] = v ? __uint_as_float((uint32_t)(uint16_t)xb[e] << 16) * inv_scale : neg_inf_s;
         }
-        beff[gi][0] = e16[0] | (e16[1] << 16);
-        beff[gi][1] = e16[2] | (e16[3] << 16);
+        sm.beff[wave][gi][lane] = iv;
       }
       dbacc = f32x16{};
     }
 
-    // A SKIP half runs the same straight-line code: its effective bias is -inf everywhere,
-    // so P = dS = 0 exactly and it adds nothing (a branch here would make the compiler
-    // shuttle the dK/dV accumulators between register files on every item).
-    // ---- S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys ------------------
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 kbs = *reinterpret_cast<const bf16x8*>(&sm.k[aoff[s] + wave * 32 * D]);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&qt[aoff[s]]);
-      sacc = mfma32(aq, kbs, sacc);
-      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&gt[aoff[s]]);
-      pacc = mfma32(ag, vreg[s], pacc);
-    }
-    // ---- P = exp(S - lse) on valid entries, dS = P (dP - D) -----------------------------
+    // A SKIP half runs the same straight-line code: its initial S values are -inf, so P and
+    // dS are exactly zero and it adds nothing (a branch here would make the compiler shuttle
+    // the dK/dV accumulators between register files on every item).
+    // ---- S + bias/scale = Q K^T + init and dP - D = dO V^T - D: 32 queries x 32 keys -----------
+    f32x16 sacc, pacc;
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const int q0 = gi * 8 + hi * 4;
-      const f32x4 ls = *reinterpret_cast<const f32x4*>(&sm.lse[buf][q0]);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dr[buf][q0]);
-      const float bb[4] = {bf16_lo(beff[gi][0]), bf16_hi(beff[gi][0]), bf16_lo(beff[gi][1]), bf16_hi(beff[gi][1])};
+      const f32x4 iv = sm.beff[wave][gi][lane];
+      const f32x4 nd = *reinterpret_cast<const f32x4*>(&sm.nd[B][gi * 8 + hi * 4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sacc[gi * 4 + e] = iv[e];
+        pacc[gi * 4 + e] = nd[e];
+      }
+    }
+    // Every operand read is issued before the first product (a scheduling barrier keeps
+    // them there), so the products wait on LDS once instead of once per k-step.
+    const int qoff = aoff0 + B * Smem::kTile;  // this item's buffer of the Q and dO tiles
+    bf16x8 opq[D / 16], opg[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      opq[s] = *reinterpret_cast<const bf16x8*>(&sm.q[0][qoff ^ (s << 4)]);
+      opg[s] = *reinterpret_cast<const bf16x8*>(&sm.g[0][qoff ^ (s << 4)]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      sacc = mfma32(opq[s], kreg[s], sacc);
+      pacc = mfma32(opg[s], vreg[s], pacc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the transposing reads of the dV/dK operands do not depend on P or dS: issue them now,
+    // so that the softmax below covers their latency
+    const int gbuf = goff0 + B * Smem::kTile;
+    i16x4 trg[2][D / 32][2], trq[2][D / 32][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int t0 = (gbuf ^ (dt << 5)) + ks * 16 * D, t1 = ((gbuf ^ (dt << 5)) + 8 * D) ^ kG1Xor;
+        trg[ks][dt][0] = lds_read_tr16(&sm.g[0][t0]);
+        trg[ks][dt][1] = lds_read_tr16(&sm.g[0][t1 + ks * 16 * D]);
+        trq[ks][dt][0] = lds_read_tr16(&sm.q[0][t0]);
+        trq[ks][dt][1] = lds_read_tr16(&sm.q[0][t1 + ks * 16 * D]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- P = exp2(scale2 * S' - lse log2 e), dS = P (dP - D) -----------------------------------
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const f32x4 nl = *reinterpret_cast<const f32x4*>(&sm.nl2[B][gi * 8 + hi * 4]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = gi * 4 + e;
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale2, (bb[e] - ls[e]) * kLog2eB));
-        // a SKIP half gives exactly zero whatever its K/V hold, so dQ can take all 128 keys
-        const float ds = (my_st != kSkip) ? pv * (pacc[i] - dd[e]) : 0.f;
-        sacc[i] = (my_st != kSkip) ? pv : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale2, nl[e]));
+        const float ds = pv * pacc[i];
+        sacc[i] = pv;
         pacc[i] = ds;
         dbacc[i] += ds;
       }
     }
     // ---- dV += P^T dO, dK += dS^T Q: two k-steps of 16 queries ----------------------------
+    const int swb = swoff0 + B * Smem::kSTile;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 pw, sw2;
@@ -527,25 +561,19 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         sw2[e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
       }
       const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw2);
-      const int rk = ks * 16 * D;  // this k-step's rows: a compile-time offset
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const i16x4 g0 = lds_read_tr16(&gt[gq0[dt] + rk]);
-        const i16x4 g1 = lds_read_tr16(&gt[gq1[dt] + rk]);
-        dv[dt] = mfma32(ap, join_bf16x8(g0, g1), dv[dt]);
-        const i16x4 q0 = lds_read_tr16(&qt[gq0[dt] + rk]);
-        const i16x4 q1 = lds_read_tr16(&qt[gq1[dt] + rk]);
-        dk[dt] = mfma32(as, join_bf16x8(q0, q1), dk[dt]);
+        dv[dt] = mfma32(ap, join_bf16x8(trg[ks][dt][0], trg[ks][dt][1]), dv[dt]);
+        dk[dt] = mfma32(as, join_bf16x8(trq[ks][dt][0], trq[ks][dt][1]), dk[dt]);
       }
-    }
-    // ---- dS^T row of this lane's key: 4 consecutive queries per row group -----------------
-    uint16_t* st_tile = sm.s[buf];
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      u32x2 w2;
-      w2[0] = pack_bf16x2(pacc[gi * 4 + 0], pacc[gi * 4 + 1]);
-      w2[1] = pack_bf16x2(pacc[gi * 4 + 2], pacc[gi * 4 + 3]);
-      *reinterpret_cast<u32x2*>(&st_tile[sw[gi] + wave * 32 * SR]) = w2;
+      // the same bf16 pairs (rows gi*4 + 2e', + 1 of the S layout) form the dS^T rows below
+      u32x2 lo2, hi2;
+      lo2[0] = sw2[0];
+      lo2[1] = sw2[1];
+      hi2[0] = sw2[2];
+      hi2[1] = sw2[3];
+      *reinterpret_cast<u32x2*>(&sm.s[0][swb ^ ((2 * ks) << 3)]) = lo2;
+      *reinterpret_cast<u32x2*>(&sm.s[0][swb ^ ((2 * ks + 1) << 3)]) = hi2;
     }
     dma_barrier();  // dS^T complete; the next item's buffers are loaded; this item's are free
 
@@ -555,14 +583,13 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     // keys of its query (k-steps wave and wave + 4, rows hi*8 of the step), and consecutive
     // lanes store consecutive chunks.
     {
-      uint16_t* tile =
-          p.ds + ((((int64_t)plane * p.npairs + pbc + KB) * p.G + hh) * 2 + rh) * (kRows * kKeys);
+      uint16_t* tile = p.ds + ((((int64_t)plane * p.npairs + pbc + KB) * p.G + hh) * 2 + rh) * (kRows * kKeys);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int ks = wave + 4 * hf;
         const int sofs = (ks >> 1) * 32 * SR;
-        const i16x4 a0 = lds_read_tr16(&st_tile[sq[ks & 1][0] + sofs]);
-        const i16x4 a1 = lds_read_tr16(&st_tile[sq[ks & 1][1] + sofs]);
+        const i16x4 a0 = lds_read_tr16(&sm.s[B][sq[ks & 1][0] + sofs]);
+        const i16x4 a1 = lds_read_tr16(&sm.s[B][sq[ks & 1][1] + sofs]);
         *reinterpret_cast<bf16x8*>(tile + (tid + 256 * hf) * 8) = join_bf16x8(a0, a1);
       }
     }
@@ -573,7 +600,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       // takes an offset beyond it, so its stores are dropped as well
       const uint32_t rbytes = (uint32_t)p.lk * 2u;
       const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(p.dbias + plane_off + i0 * p.lk + (int64_t)kb0 * kBlock, (uint32_t)rows_left * rbytes);
+          make_rsrc(p.dbias + plane_off + (int64_t)i0 * p.lk + (int64_t)kb0 * kBlock, (uint32_t)rows_left * rbytes);
       uint32_t rb = rbytes;
       asm volatile("" : "+s"(rb));  // keep the row offsets below inside the loop (not hoisted)
       const uint32_t lane_off = (key_abs < p.lk) ? (uint32_t)(hi * 4) * rb + (uint32_t)key_loc * 2u : kOutOfRange;
@@ -583,8 +610,12 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dbacc[i]), r, lane_off + rc * rb, 0, 0);
       }
     }
+    // the dK/dV accumulators live in the accumulation registers: no VALU ever reads them in
+    // the loop, which keeps the vector registers for the S/dP work and its operands
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(kreg[s]), "+a"(vreg[s]));
     buf ^= 1;
     pbc = pbn;
     qb = nqb;
@@ -750,7 +781,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   {
     const int64_t threads = rows * (a.d / 8);
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.o, a.dout,
-                       a.drow, rows, a.lq, a.hq, (int)a.d);
+                       a.lse_in, a.nd, a.nl2, rows, a.lq, a.hq, (int)a.d);
     hipLaunchKernelGGL(kt_kernel, dim3((unsigned)(a.b * a.hkv * nkb2 * 2)), dim3(256), 0, stream, a.k, a.kt, a.lk,
                        a.hkv, ktrow, nkb2 * 2, (int)a.d);
     hipLaunchKernelGGL(pair_base_kernel, dim3(1), dim3(1024), 0, stream, a.pair_base, (int64_t)nqb, a.lq, a.lk,
@@ -766,8 +797,8 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.bias = a.bias;
   p.state = a.state;
   p.dout = a.dout;
-  p.lse = a.lse_in;
-  p.drow = a.drow;
+  p.nl2 = a.nl2;
+  p.nd = a.nd;
   p.pair_base = a.pair_base;
   p.ds = a.ds;
   p.npairs = a.npairs;

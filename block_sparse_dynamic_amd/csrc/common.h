@@ -143,7 +143,8 @@ struct AttnArgs {
   uint16_t* dk;
   uint16_t* dv;
   uint16_t* dbias;
-  float* drow;        // fp32 [b, hq, lq]: rowsum(dO * O)
+  float* nd;          // fp32 [b, hq, lq]: -rowsum(dO * O)
+  float* nl2;         // fp32 [b, hq, lq]: -lse * log2(e)
   int64_t* pair_base; // [nqb + 1]: index of query block qb's first dS tile pair (live pairs before it)
   uint16_t* kt;       // bf16 [b, hkv, d, nkb2 * 128]: K transposed, zero past lk
   uint16_t* ds;       // bf16 dS tiles, see bwd_ds_tile

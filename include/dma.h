@@ -107,7 +107,8 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  float scale, int is_causal, uint16_t* o, float* lse, void* stream);
 
 /* Bytes of device workspace dma_attn_bwd needs for these sizes (0 for invalid
- * sizes): the fp32 row terms D = rowsum(dO * O) [b, hq, lq], K transposed
+ * sizes): the fp32 row terms -rowsum(dO * O) and -lse log2(e), each
+ * [b, hq, lq], K transposed
  * (bf16), and the bf16 dS tile of every (query head, 64-row query block, 128-key
  * pair of classification blocks) that causality leaves live, from which dQ is
  * formed without atomics (FlashMask README: deterministic backward).  With
@@ -130,8 +131,10 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq
  *               NULL: then the bias gradient is not produced.
  *   workspace   device scratch of at least dma_attn_bwd_workspace_size() bytes,
  *               16-byte aligned, owned by the caller, contents on entry ignored
- * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL, and
- *   DMA_ERR_UNSUPPORTED for lk > 2^24 (32-bit row offsets of dbias).
+ * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL,
+ *   DMA_ERR_INVALID_ARGUMENT for a scale that is zero or not finite (the kernel
+ *   carries scores as q.k + bias / scale), and DMA_ERR_UNSUPPORTED for lq or lk
+ *   above 2^24 (32-bit row offsets).
  * dq is deterministic: the same inputs give bit-identical outputs.
  */
 int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,

@@ -101,7 +101,8 @@ def test_fwd_ragged_lk_allowed_without_mask_and_bias(lib):
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID), (dict(dv=None), INVALID),
     (dict(ws=None), INVALID), (dict(lse=P + 4), INVALID), (dict(db=P + 2), INVALID),
     (dict(wsb=1000), WS_SMALL), (dict(d=80), UNSUPPORTED),
-    (dict(lk=(1 << 24) + 64), UNSUPPORTED),
+    (dict(lk=(1 << 24) + 64), UNSUPPORTED), (dict(lq=(1 << 24) + 64), UNSUPPORTED),
+    (dict(scale=0.0), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=float("nan")), INVALID),
 ])
 def test_bwd_rejects(lib, kw, want):
     assert bwd(lib, **kw) == want
@@ -121,12 +122,12 @@ def live_pairs(qb, lq, lk, causal):
     (1, 1000, 300, 4, 1, 64, 1), (1, 64, 4096, 2, 1, 64, 1),
 ])
 def test_workspace_size(lib, b, lq, lk, hq, hkv, d, causal):
-    # regions: D rows (fp32), pair offsets (int64), K^T (bf16, keys padded to 128), dS tiles
+    # regions: row terms (2 fp32 per row), pair offsets (int64), K^T (bf16, keys padded to 128), dS tiles
     # (bf16, 64 x 128 per live pair and query head); each rounded up to 256 bytes
     up = lambda x: (x + 255) // 256 * 256
     nqb, nkb2 = (lq + 63) // 64, ((lk + 63) // 64 + 1) // 2
     npairs = sum(live_pairs(qb, lq, lk, causal) for qb in range(nqb))
-    want = up(b * hq * lq * 4) + up((nqb + 1) * 8) + up(b * hkv * d * nkb2 * 128 * 2) + up(b * hq * npairs * 64 * 128 * 2)
+    want = up(2 * b * hq * lq * 4) + up((nqb + 1) * 8) + up(b * hkv * d * nkb2 * 128 * 2) + up(b * hq * npairs * 64 * 128 * 2)
     assert lib.dma_attn_bwd_workspace_size(b, lq, lk, hq, hkv, d, causal) == want
 
 
