@@ -10,6 +10,8 @@ constexpr int kBlock = 64;  // classification block: 64 query rows x 64 key colu
 constexpr uint8_t kSkip = 0, kPartial = 1, kFull = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -41,6 +43,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+// Two fp32 values -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// A bf16 pair -> the same two values as an fp16 pair (exact for |x| in [2^-14, 65504]).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return pack_f16x2(bf16_lo(w), bf16_hi(w)); }
 
 // LDS tile layouts.  A [rows][D] bf16 tile stores the 16-byte chunk c of row r at chunk
 // c ^ tile_xor<D>(r), rows unpadded.  For D = 128 the XOR is 4*(r%4) + (r/4)%4: a 128-bit
@@ -115,6 +124,9 @@ __device__ __forceinline__ bf16x8 join_bf16x8(i16x4 a, i16x4 b) {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -26,11 +26,12 @@
 //      exp2 with log2(e) folded in; the running output is rescaled whenever a
 //      row maximum grows (the wave skips the rescale when none does), so the
 //      largest weight of a row always enters the PV product as exactly 1.0 and
-//      the bf16 rounding of P stays off the dominant term.
-//   4. O^T += V^T P^T: P^T goes from the accumulator registers straight into
-//      the B operand (the key order inside a k-step only has to agree between
-//      A and B), as a bf16 hi part plus a bf16 lo part; V^T comes out of the
-//      row-major V tile by ds_read_b64_tr_b16.
+//      the rounding of P stays off the dominant term.
+//   4. O^T += V^T P^T on v_mfma_f32_32x32x16_f16: P^T goes from the accumulator
+//      registers straight into the B operand as fp16 (the key order inside a
+//      k-step only has to agree between A and B); V^T comes out of the
+//      row-major V tile, staged in fp16 (bf16 values convert exactly for
+//      magnitudes in [2^-14, 65504]), by ds_read_b64_tr_b16.
 #include <math.h>
 
 #include "common.h"
@@ -186,7 +187,10 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       const bool in = (int64_t)kb * kBlock + r < p.lk;
       const u32x4 z = {0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = in ? pk[n] : z;
-      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = in ? pv[n] : z;
+      u32x4 vh;  // V in fp16 for the P V product
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vh[e] = bf16x2_to_f16x2(pv[n][e]);
+      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = in ? vh : z;
     }
     if (has_bias || !full) {
 #pragma unroll
@@ -279,30 +283,24 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       }
     l_part += rs;
     // ---- O^T += V^T P^T -------------------------------------------------------
-    // P goes in as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), so the weights
-    // carry ~16 significant bits: with a bf16 P alone its rounding (2^-9 relative) can
-    // move O by more than the 1e-2 the output tolerance leaves after bf16 storage.
-    // Both MFMAs read the same V^T operand.
+    // P and V enter in fp16 (V converted exactly when staged): P in [0, 1] keeps 11
+    // significant bits, against 8 in bf16, whose rounding (2^-9 relative) could move O by more
+    // than the 1e-2 the output tolerance leaves after bf16 storage.
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        u32x4 pw, lw;
+        u32x4 pw;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = sacc[kt][hh * 8 + 2 * e], p1 = sacc[kt][hh * 8 + 2 * e + 1];
-          pw[e] = pack_bf16x2(p0, p1);
-          lw[e] = pack_bf16x2(p0 - bf16_lo(pw[e]), p1 - bf16_hi(pw[e]));
-        }
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, pw), pl = __builtin_bit_cast(bf16x8, lw);
+        for (int e = 0; e < 4; ++e) pw[e] = pack_f16x2(sacc[kt][hh * 8 + 2 * e], sacc[kt][hh * 8 + 2 * e + 1]);
+        const f16x8 ph = __builtin_bit_cast(f16x8, pw);
         const int rbase = (kt * 32 + hh * 16) * KR;  // rows of this k-step, a compile-time offset
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const i16x4 a0 = lds_read_tr16(&sm.v[voff0[dt] + rbase]);
           const i16x4 a1 = lds_read_tr16(&sm.v[voff1[dt] + rbase]);
-          const bf16x8 av = join_bf16x8(a0, a1);
-          oacc[dt] = mfma32(av, ph, oacc[dt]);
-          oacc[dt] = mfma32(av, pl, oacc[dt]);
+          const f16x8 av = __builtin_bit_cast(f16x8, join_bf16x8(a0, a1));
+          oacc[dt] = mfma32_f16(av, ph, oacc[dt]);
         }
       }
     }

@@ -89,7 +89,8 @@ int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq,
  * valid scores scaled, bias added; softmax; times V).
  *
  *   q           bf16 [b, lq, hq, d]
- *   k, v        bf16 [b, lk, hkv, d]
+ *   k, v        bf16 [b, lk, hkv, d]; the P V product takes v in fp16, exact
+ *               for magnitudes in [2^-14, 65504] (larger ones saturate there)
  *   mask, bias  bf16 [b, hkv, lq, lk]; either may be NULL (no mask: every key
  *               attends; no bias: zero).  bias entries at masked positions
  *               are never read into the result (they may hold NaN or inf).
