@@ -187,6 +187,7 @@ struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay s
   // valid pairs, -inf (signed so that scale * it is -inf) elsewhere.  Written when a query
   // block starts, read by the same lane for every head of the group.
   f32x4 beff[4][4][64];  // [wave][row group][lane]
+  int64_t pb[kStateChunk];     // pair_base of the same query blocks (first dS tile pair of each)
   uint8_t st[2][kStateChunk];  // block states of the two key blocks for a range of query blocks
 };
 
@@ -294,8 +295,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 
   // Query blocks are walked from the last to the first: the workgroups of one XCD start
   // together on the same rows, so their Q/dO reads share the XCD's L2.  The states of
-  // this workgroup's two key blocks are cached in LDS a chunk of query blocks at a time,
-  // so the item loop never waits on a global load of the bitmap.
+  // this workgroup's two key blocks (and the query blocks' first dS tile pairs) are cached in
+  // LDS a chunk of query blocks at a time, so the item loop never waits on a global load.
   int cache_lo = p.nqb;  // cached query blocks: [cache_lo, cache_lo + kStateChunk)
   auto fill_cache = [&](int qb_hi) {
     lds_barrier();  // every reader of the previous chunk is done
@@ -305,6 +306,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       uint8_t v = kSkip;
       if (qb <= qb_hi && (hf == 0 || has_kb1)) v = st_col[(int64_t)qb * p.nkb + hf];
       sm.st[hf][j] = v;
+      if (hf == 0 && qb <= qb_hi) sm.pb[j] = p.pair_base[qb];
     }
     lds_barrier();
     cache_lo = lo;
@@ -432,10 +434,13 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   // loads of item n+2 may start after it.  The dS^T tile alternates as well, so its export
   // after the barrier does not race the next item's writes.
   uint8_t cs0, cs1;  // states of the current item's two key blocks
+  // Wait here for every load so far (K, V rows): the compiler then knows they are complete.
+  // Otherwise it waits for them (vmcnt) at their first use inside the loop on every item,
+  // which would also wait for the item loads issued there.
+  __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();     // buffers zeroed
   int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
   int rh = 0, hh = 0;
-  int64_t pbc = p.pair_base[qb >= 0 ? qb : 0];  // first dS tile pair of the current query block
   int buf = 0;
   if (qb >= 0) issue(0, qb, 0, 0, cs0, cs1);
   dma_barrier();
@@ -445,6 +450,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     const int i0 = qb * kBlock + rh * kRows;
     const int rows_left = min(kRows, (int)p.lq - i0);
     const uint8_t my_st = half ? cs1 : cs0;
+    const int64_t pbc = sm.pb[qb - cache_lo];  // read before the walk below may move the cache
 
     // ---- start loading the next item ------------------------------------------------
     int nqb = qb, nrh = rh, nhh = hh + 1;
@@ -457,8 +463,6 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         nqb = next_qb(qb - 1, ns0, ns1);
       }
     }
-    // first dS tile pair of the next item's query block, used after the next barrier
-    const int64_t pbn = p.pair_base[nqb >= 0 ? nqb : 0];
     if (nqb >= 0) issue(B ^ 1, nqb, nrh, nhh, ns0, ns1);
 
     if (hh == 0) {
@@ -617,7 +621,6 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(kreg[s]), "+a"(vreg[s]));
     buf ^= 1;
-    pbc = pbn;
     qb = nqb;
     rh = nrh;
     hh = nhh;
@@ -665,6 +668,8 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   constexpr int NT = HC * 128;
   constexpr int KT = D * 16 / NT;  // 16-byte chunks of the K^T tile each thread stages
   __shared__ __attribute__((aligned(16))) uint16_t ktile[D * 128];  // [d][128 keys], swz128 rows
+  constexpr int kPairChunk = 2048;
+  __shared__ uint8_t srow[2 * kPairChunk];  // block states of the query block's row, pairs [cache_lo, + kPairChunk)
 
   const int w = blockIdx.x;
   const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
@@ -686,25 +691,44 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
                         (int64_t)rh * (kRows * kKeys);
   const int64_t pair_stride = (int64_t)p.G * 2 * (kRows * kKeys);
 
-  auto live = [&](int64_t kb2) -> bool {
-    const uint8_t s0 = st_row[2 * kb2];
-    const uint8_t s1 = (2 * kb2 + 1 < p.nkb) ? st_row[2 * kb2 + 1] : kSkip;
-    return s0 != kSkip || s1 != kSkip;
+  // The block states of this query block's row are cached in LDS a chunk of pairs at a time:
+  // the pair walk then waits on LDS only, never on a global load that would also wait for the
+  // prefetches.  The chunk always holds the pair the walk last returned.
+  int64_t cache_lo = -kPairChunk;
+  auto fill = [&](int64_t lo) {
+    lds_barrier();  // every reader of the previous chunk is done
+    for (int j = tid; j < 2 * kPairChunk; j += NT) {
+      const int64_t kb = 2 * lo + j;
+      srow[j] = kb < p.nkb ? st_row[kb] : kSkip;
+    }
+    lds_barrier();
+    cache_lo = lo;
   };
+  auto state = [&](int64_t kb2, int hf) -> uint8_t { return srow[2 * (kb2 - cache_lo) + hf]; };
   auto next_pair = [&](int64_t from) -> int64_t {
-    for (int64_t kb2 = from; kb2 < npair; ++kb2)
-      if (live(kb2)) return kb2;
+    for (int64_t kb2 = from; kb2 < npair; ++kb2) {
+      if (kb2 >= cache_lo + kPairChunk) fill(kb2);
+      if (state(kb2, 0) != kSkip || state(kb2, 1) != kSkip) return kb2;
+    }
     return npair;
   };
 
+  // K^T chunks of a pair (staged into LDS one pair later) and this wave's dS fragments of a
+  // pair (eight 16-byte chunks per lane, consumed one pair later), both loaded a pair ahead so
+  // that their latency hides behind a pair of products.  A pair past the last is replaced by
+  // the current one: the loads stay unconditional and in bounds.
   u32x4 pkt[KT];
-  auto prefetch_kt = [&](int64_t kb2) {
+  bf16x8 bfr[8], bnx[8];
+  auto prefetch = [&](int64_t kb2, bf16x8* dst) {
 #pragma unroll
     for (int n = 0; n < KT; ++n) {
       const int task = tid + n * NT;
       const int r = task >> 4, c = task & 15;
       pkt[n] = *reinterpret_cast<const u32x4*>(ktp + (int64_t)r * p.ktrow + kb2 * 128 + c * 8);
     }
+    const uint16_t* tile = dsp + kb2 * pair_stride;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) dst[ks] = *reinterpret_cast<const bf16x8*>(tile + (ks * 64 + lane) * 8);
   };
 
   f32x16 acc[D / 32];
@@ -715,17 +739,12 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   for (int dt = 0; dt < D / 32; ++dt) aoff[dt] = swz128(dt * 32 + l32, hi * 8);
 
   int64_t kb2 = next_pair(0);
-  if (kb2 < npair) prefetch_kt(kb2);
+  if (kb2 < npair) prefetch(kb2, bfr);
   while (kb2 < npair) {
-    // this pair's dS fragments (eight 16-byte chunks per lane), issued before the staging
-    bf16x8 bfr[8];
-    const uint16_t* tile = dsp + kb2 * pair_stride;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bfr[ks] = *reinterpret_cast<const bf16x8*>(tile + (ks * 64 + lane) * 8);
     // a key block that is SKIP for this query block has dS = 0 and may hold any K rows (they
     // are never loaded elsewhere): its half of the tile is staged as zeros
-    const bool dead0 = st_row[2 * kb2] == kSkip;
-    const bool dead1 = (2 * kb2 + 1 < p.nkb) ? st_row[2 * kb2 + 1] == kSkip : true;
+    const bool dead0 = state(kb2, 0) == kSkip;
+    const bool dead1 = state(kb2, 1) == kSkip;
     lds_barrier();  // every read of the previous K^T tile is done
 #pragma unroll
     for (int n = 0; n < KT; ++n) {
@@ -736,7 +755,8 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
     }
     lds_barrier();
     const int64_t kb2n = next_pair(kb2 + 1);
-    if (kb2n < npair) prefetch_kt(kb2n);
+    prefetch(kb2n < npair ? kb2n : kb2, bnx);
+    asm volatile("" ::: "memory");  // keep the prefetch here: the compiler would sink it below the products
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
@@ -747,6 +767,8 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
         acc[dt] = mfma32(av, bfr[ks], acc[dt]);
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bfr[ks] = bnx[ks];
     kb2 = kb2n;
   }
 

@@ -101,6 +101,9 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       qreg[s] = __builtin_bit_cast(bf16x8, w4);
     }
   }
+  // Wait for Q here: the compiler then knows it is loaded, instead of waiting for it (vmcnt) at
+  // its first use inside the loop on every block, which would also wait for the prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 oacc[D / 32];
 #pragma unroll
