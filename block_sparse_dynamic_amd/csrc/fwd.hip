@@ -23,10 +23,10 @@
 //      lane l holds query l%32 and 16 keys of each 32-key half, so a row's
 //      64 scores live in lanes l and l^32.
 //   3. online softmax in fp32: row max over the lane pair (v_permlane32_swap),
-//      exp2 with log2(e) folded in; the running output is rescaled whenever a
-//      row maximum grows (the wave skips the rescale when none does), so the
-//      largest weight of a row always enters the PV product as exactly 1.0 and
-//      the rounding of P stays off the dominant term.
+//      exp2 with log2(e) folded in; the reference maximum (and with it the
+//      running output) moves only when a row maximum exceeds it by more than
+//      2^8 in weight, so weights stay in [0, 256] and the rescale runs rarely
+//      (the wave skips it when no row needs it).
 //   4. O^T += V^T P^T on v_mfma_f32_32x32x16_f16: P^T goes from the accumulator
 //      registers straight into the B operand as fp16 (the key order inside a
 //      k-step only has to agree between A and B); V^T comes out of the
@@ -54,7 +54,8 @@ struct FwdParams {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kStateChunkF = 1024;  // key blocks whose states are cached in LDS at a time
+constexpr int kStateChunkF = 1024;
+constexpr float kRescaleMargin = 8.f * 0.69314718f;  // natural-log units  // key blocks whose states are cached in LDS at a time
 constexpr uint16_t kBf16NegInf = 0xFF80u;
 
 template <int D>
@@ -264,7 +265,11 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     }
     mx = max_with_half_swap(mx);
     // ---- online softmax ----------------------------------------------------------
-    if (__any(mx > m_ref)) {
+    // The reference maximum moves only when a row's maximum exceeds it by more than
+    // kRescaleMargin (8 in log2 units): below that the weights exp(x - m_ref) stay under 256,
+    // which fp32 sums and fp16 P hold without loss, and the rescale of the accumulators
+    // (64 multiplies per lane) runs a few times per row instead of on most key blocks.
+    if (__any(mx > m_ref + kRescaleMargin)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_ref - m_new) * kLog2e);
       m_ref = m_new;
