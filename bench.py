@@ -223,6 +223,29 @@ def main():
     t_cls, t_fwd, t_bwd = per.mean(axis=0)  # ms
     ms_step = wall / args.steps * 1e3
 
+    # Next-row measurement, outside the step: the top-k mask construction (dma_topk_mask) on
+    # a fresh N(0,1) bf16 bias of the workload's shape, k = the workload's top-k.
+    next_rows = {}
+    if c.mask == "topk":
+        gen = torch.Generator(device="cuda").manual_seed(1234)
+        raw = torch.randn((c.b * c.hkv * c.lq, c.lk), generator=gen, device="cuda").to(torch.bfloat16)
+        mk, bo = torch.empty_like(raw), torch.empty_like(raw)
+        dma.dma_topk_mask(raw, c.topk, mk, bo, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record(stream)
+        for _ in range(reps):
+            dma.dma_topk_mask(raw, c.topk, mk, bo, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_topk = e0.elapsed_time(e1) / reps
+        bytes_topk = 3.0 * raw.numel() * 2  # bias read once, mask and bias written
+        next_rows["topk_mask"] = {"ms": round(t_topk, 4), "gbs": round(bytes_topk / (t_topk * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(bytes_topk / (t_topk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                  "rows": c.b * c.hkv * c.lq, "lk": c.lk, "k": c.topk}
+        del raw, mk, bo
+
     n_skip, n_p, n_f = block_counts(state)
     n_ns = n_p + n_f
     G, d = c.hq // c.hkv, c.d
@@ -283,6 +306,7 @@ def main():
                                  "fwd": round(b_fwd / (t_fwd * 1e-3) / 1e9, 1),
                                  "bwd": round(b_bwd / (t_bwd * 1e-3) / 1e9, 1)},
         "roofline": roofline,
+        "next_rows": next_rows,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, args.cpu_blocks, f_fwd + f_bwd)

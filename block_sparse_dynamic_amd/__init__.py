@@ -29,7 +29,7 @@ BLOCK_SKIP, BLOCK_PARTIAL, BLOCK_FULL = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m block_sparse_dynamic_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python block_sparse_dynamic_amd/build.py` "
         "(hipcc, gfx950); there is no fallback implementation")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -48,6 +48,8 @@ _lib.dma_attn_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
 _lib.dma_attn_bwd.restype = _i32
 _lib.dma_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dma_topk_mask.restype = _i32
+_lib.dma_topk_mask.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
 
 
 class DMAError(RuntimeError):
@@ -90,6 +92,17 @@ def _check(fn: str, st: int):
 def block_state_shape(b: int, hkv: int, lq: int, lk: int):
     n = dma_block_size()
     return (b, hkv, (lq + n - 1) // n, (lk + n - 1) // n)
+
+
+def dma_topk_mask(bias: torch.Tensor, k: int, mask_out: torch.Tensor, bias_out: torch.Tensor, stream=None) -> None:
+    """Keep the k largest bias values of each row (last dimension): mask_out 1 there, and
+    bias_out the bias there and the smallest bf16 elsewhere.  bias_out may be bias itself."""
+    lk = bias.shape[-1]
+    rows = bias.numel() // lk
+    st = _lib.dma_topk_mask(_ptr(bias, "bias", torch.bfloat16), rows, lk, int(k),
+                            _ptr(mask_out, "mask_out", torch.bfloat16), _ptr(bias_out, "bias_out", torch.bfloat16),
+                            _stream(stream))
+    _check("dma_topk_mask", st)
 
 
 def dma_block_classify(mask: Optional[torch.Tensor], b: int, hkv: int, lq: int, lk: int, is_causal: bool,

@@ -1,6 +1,6 @@
 """Build libdma.so (gfx950) from csrc/ with hipcc, in place.
 
-    python -m block_sparse_dynamic_amd.build
+    python block_sparse_dynamic_amd/build.py
 """
 from __future__ import annotations
 
@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdma.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "classify.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "classify.hip", "fwd.hip", "bwd.hip", "topk.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -180,4 +180,16 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   return hip_status(dma::launch_bwd(a, (hipStream_t)stream));
 }
 
+int dma_topk_mask(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out, uint16_t* bias_out,
+                  void* stream) {
+  if (!bias || !mask_out || !bias_out) return DMA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(bias) || !aligned16(mask_out) || !aligned16(bias_out)) return DMA_ERR_INVALID_ARGUMENT;
+  if (rows < 1 || lk < 1 || k < 1 || lk % 8 != 0) return DMA_ERR_INVALID_ARGUMENT;
+  if (mask_out == bias || mask_out == bias_out) return DMA_ERR_INVALID_ARGUMENT;
+  if (lk > 65536 || rows > 0x7FFFFFFF) return DMA_ERR_UNSUPPORTED;
+  return dma::launch_topk(bias, rows, lk, k, mask_out, bias_out, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DMA_OK
+             : DMA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -179,5 +179,7 @@ __host__ __device__ inline int64_t live_pairs(int64_t qb, int64_t lq, int64_t lk
 }
 
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_topk(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out,
+                       uint16_t* bias_out, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
 }  // namespace dma

@@ -143,6 +143,29 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq,
                  uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Top-k mask construction (Flash-DMA README, usage example: keep the
+ * keep_window_size largest bias values of every query row; everything else is
+ * masked, and its bias is set to the smallest bf16 value).
+ *
+ *   bias      bf16 [rows, lk] (rows = b * hkv * lq for a [b, hkv, lq, lk] bias)
+ *   k         keys kept per row (keep_window_size), >= 1
+ *   mask_out  out, bf16 [rows, lk]: 1.0 at the kept positions whose value is not
+ *             the smallest bf16 (-3.3895e38), 0 elsewhere
+ *   bias_out  out, bf16 [rows, lk]: the bias at positions where mask_out is 1,
+ *             the smallest bf16 elsewhere.  May be the same buffer as bias
+ *             (in place); mask_out must differ from both.
+ * A row with lk <= k keeps everything: mask all 1, bias copied unchanged.
+ * Order: numeric order of the bf16 values, +0 equal to -0, NaN below every
+ * number; ties at the k-th value go to the lowest key indices (the reading
+ * taken for the pages' unsorted top-k), so the result is fully determined.
+ * Errors: DMA_ERR_INVALID_ARGUMENT (NULL or misaligned pointers, rows, lk or
+ * k < 1, lk % 8 != 0, mask_out aliasing an input), DMA_ERR_UNSUPPORTED
+ * (lk > 65536: a row is held in LDS; rows > 2^31 - 1).
+ */
+int dma_topk_mask(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out, uint16_t* bias_out,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

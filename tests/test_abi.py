@@ -17,8 +17,11 @@ P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced by validat
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        import block_sparse_dynamic_amd.build as b
+        import importlib.util
 
+        spec = importlib.util.spec_from_file_location("_dma_build", os.path.join(ROOT, "block_sparse_dynamic_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     L = ctypes.CDLL(LIB)
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -29,6 +32,7 @@ def lib():
     L.dma_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp,
                                vp, vp, sz, vp]
     L.dma_status_string.restype = ctypes.c_char_p
+    L.dma_topk_mask.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     return L
 
 
@@ -41,7 +45,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("dma_block_classify", "dma_attn_fwd", "dma_attn_bwd", "dma_attn_bwd_workspace_size",
-                 "dma_block_size", "dma_status_string"):
+                 "dma_block_size", "dma_status_string", "dma_topk_mask"):
         assert name in syms
 
 
@@ -162,3 +166,16 @@ def test_package_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import block_sparse_dynamic_amd"], cwd=tmp_path,
                        capture_output=True, text=True)
     assert r.returncode != 0 and "libdma.so is missing" in r.stderr
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(bias=None), INVALID), (dict(mask=None), INVALID), (dict(out=None), INVALID),
+    (dict(bias=P + 2), INVALID), (dict(mask=P + 0x100008), INVALID),
+    (dict(rows=0), INVALID), (dict(lk=0), INVALID), (dict(k=0), INVALID), (dict(lk=100), INVALID),
+    (dict(mask=P), INVALID), (dict(mask=P + 0x200000, out=P + 0x200000), INVALID),
+    (dict(lk=65544), UNSUPPORTED), (dict(rows=1 << 31), UNSUPPORTED),
+])
+def test_topk_rejects(lib, kw, want):
+    a = dict(bias=P, rows=4, lk=1024, k=64, mask=P + 0x100000, out=P + 0x200000)
+    a.update(kw)
+    assert lib.dma_topk_mask(a["bias"], a["rows"], a["lk"], a["k"], a["mask"], a["out"], None) == want
