@@ -363,6 +363,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const uint32_t qrow_bytes = (uint32_t)(p.hq * D * 2);
   const uint32_t krange = (uint32_t)min((int64_t)kKeys, p.lk - (int64_t)kb0 * kBlock) * 2u;
 
+  // LDS byte addresses of the load destinations (buffer B of a tile is B tiles above buffer 0):
+  // plain integers, so no generic-to-LDS pointer conversion is redone on every item
+  constexpr uint32_t kTileBytes = Smem::kTile * 2, kBTileBytes = Smem::kBTile * 2;
+  const uint32_t lds_q = lds_addr(&sm.q[0][0]), lds_g = lds_addr(&sm.g[0][0]), lds_b = lds_addr(&sm.b[0][0]),
+                 lds_m = lds_addr(&sm.m[0][0]), lds_nl2 = lds_addr(&sm.nl2[0][0]), lds_nd = lds_addr(&sm.nd[0][0]);
   // Start the loads of an item into buffer B: Q and dO rows, the raw bias and mask rows of a
   // new query block (first head of the group only), and the row terms.
   auto issue = [&](int B, int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
@@ -374,8 +379,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
     for (int n = 0; n < QL; ++n) {
       const uint32_t dst = (uint32_t)((wave * QL + n) * 1024);
-      dma_x4(rq, lds_addr(&sm.q[B][0]) + dst, qv[n]);
-      dma_x4(rg, lds_addr(&sm.g[B][0]) + dst, qv[n]);
+      dma_x4(rq, lds_q + (uint32_t)B * kTileBytes + dst, qv[n]);
+      dma_x4(rg, lds_g + (uint32_t)B * kTileBytes + dst, qv[n]);
     }
     if (hh == 0) {
       const uint32_t bbytes = (uint32_t)(rows_left - 1) * (uint32_t)p.lk * 2u + krange;
@@ -383,20 +388,20 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         const u32x4 rb = rsrc_words(bias_plane + (int64_t)i0 * p.lk, bbytes);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
-          dma_x4(rb, lds_addr(&sm.b[B][0]) + (uint32_t)((wave * 2 + n) * 1024),
+          dma_x4(rb, lds_b + (uint32_t)B * kBTileBytes + (uint32_t)((wave * 2 + n) * 1024),
                  ((bh[n] ? s1 : s0) != kSkip) ? bv[n] : kOutOfRange);
       }
       if (has_mask) {
         const u32x4 rm = rsrc_words(mask_plane + (int64_t)i0 * p.lk, bbytes);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
-          dma_x4(rm, lds_addr(&sm.m[B][0]) + (uint32_t)((wave * 2 + n) * 1024),
+          dma_x4(rm, lds_m + (uint32_t)B * kBTileBytes + (uint32_t)((wave * 2 + n) * 1024),
                  ((bh[n] ? s1 : s0) == kPartial) ? bv[n] : kOutOfRange);
       }
     }
     const int64_t ridx = (int64_t)hh * p.lq + i0;
-    if (wave == 0) dma_x1(rsrc_words(nl2_plane + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.nl2[B][0]), (uint32_t)lane * 4u);
-    if (wave == 1) dma_x1(rsrc_words(nd_plane + ridx, (uint32_t)rows_left * 4u), lds_addr(&sm.nd[B][0]), (uint32_t)lane * 4u);
+    if (wave == 0) dma_x1(rsrc_words(nl2_plane + ridx, (uint32_t)rows_left * 4u), lds_nl2 + (uint32_t)B * 256u, (uint32_t)lane * 4u);
+    if (wave == 1) dma_x1(rsrc_words(nd_plane + ridx, (uint32_t)rows_left * 4u), lds_nd + (uint32_t)B * 256u, (uint32_t)lane * 4u);
   };
 
   f32x16 dk[D / 32], dv[D / 32];
