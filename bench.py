@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements (top-k construction)")
     ap.add_argument("--cpu-blocks", type=int, default=16, help="query-row blocks the oracle times")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps, so that a hardware counter "
@@ -226,7 +227,7 @@ def main():
     # Next-row measurement, outside the step: the top-k mask construction (dma_topk_mask) on
     # a fresh N(0,1) bf16 bias of the workload's shape, k = the workload's top-k.
     next_rows = {}
-    if c.mask == "topk":
+    if c.mask == "topk" and not args.no_next and args.calibrate_copy_mib == 0:
         gen = torch.Generator(device="cuda").manual_seed(1234)
         raw = torch.randn((c.b * c.hkv * c.lq, c.lk), generator=gen, device="cuda").to(torch.bfloat16)
         mk, bo = torch.empty_like(raw), torch.empty_like(raw)
