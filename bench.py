@@ -150,6 +150,72 @@ def cpu_baseline(c, blocks: int, f_total: float):
     }
 
 
+def time_ranges(args, dma, synth, np):
+    import torch
+    from synth.device import upload_dense, upload_mask_bias
+
+    c = synth.CASES["docpacked"]
+    q, k, v, do = upload_dense(c)
+    mask, bias = upload_mask_bias(c)
+    bounds = synth.doc_bounds(c)
+    j = np.arange(c.lk)
+    end = bounds[np.searchsorted(bounds, j, side="right")]
+    rs = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(j, (c.b, c.hkv, c.lk)).astype(np.int32))).cuda()
+    re = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(end, (c.b, c.hkv, c.lk)).astype(np.int32))).cuda()
+    st = torch.empty(dma.block_state_shape(c.b, c.hkv, c.lq, c.lk), dtype=torch.uint8, device="cuda")
+    o, lse = torch.empty_like(q), torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = torch.empty((c.b, c.hkv, c.lq, c.lk), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ranges):
+        if ranges:
+            dma.dma_block_classify_ranges(rs, re, c.b, c.hkv, c.lq, c.lk, c.causal, st, stream)
+            dma.dma_attn_fwd_ranges(q, k, v, rs, re, bias, st, c.scale_f32, c.causal, o, lse, stream)
+            dma.dma_attn_bwd_ranges(q, k, v, rs, re, bias, st, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias,
+                                    ws, stream)
+        else:
+            dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, st, stream)
+            dma.dma_attn_fwd(q, k, v, mask, bias, st, c.scale_f32, c.causal, o, lse, stream)
+            dma.dma_attn_bwd(q, k, v, mask, bias, st, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws, stream)
+
+    out = {"workload": f"{c.name}: b={c.b} L={c.lq} Hq={c.hq} Hkv={c.hkv} d={c.d} document mask, causal"}
+    for ranges in (False, True):
+        step(ranges)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record(stream)
+        for _ in range(reps):
+            step(ranges)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["ranges_ms" if ranges else "dense_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+    n_p = int((st == 1).sum())
+    n_f = int((st == 2).sum())
+    live = int(((st == 1) | (st == 2)).sum())
+    G = c.hq // c.hkv
+    flops = 14.0 * c.d * 64 * 64 * G * (n_p + n_f)
+    # mandatory HBM bytes: bias (+ mask) of non-SKIP blocks in the forward and the backward, the
+    # mask scan of classification, all of dBias; the range path reads 8 B per key and plane
+    n_live_blocks = int(((np.arange((c.lq + 63) // 64)[:, None] * 64 + 63 + (c.lk - c.lq)) >=
+                         (np.arange((c.lk + 63) // 64)[None, :] * 64)).sum()) * c.b * c.hkv
+    bias_b = 2.0 * 64 * 64 * (n_p + n_f)
+    mask_b = 2.0 * 64 * 64 * n_p
+    dbias_b = 2.0 * c.b * c.hkv * c.lq * c.lk
+    out["bytes_dense"] = 2.0 * 64 * 64 * n_live_blocks + 2 * (bias_b + mask_b) + dbias_b
+    out["bytes_ranges"] = 8.0 * c.b * c.hkv * c.lk + 2 * bias_b + dbias_b
+    out["tflops_dense"] = round(flops / (out["dense_ms"] * 1e-3) / 1e12, 2)
+    out["tflops_ranges"] = round(flops / (out["ranges_ms"] * 1e-3) / 1e12, 2)
+    out["gbs_ranges"] = round(out["bytes_ranges"] / (out["ranges_ms"] * 1e-3) / 1e9, 1)
+    out["blocks_partial"], out["blocks_full"] = n_p, n_f
+    del q, k, v, do, mask, bias, dbias, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -246,6 +312,12 @@ def main():
                                   "frac_hbm": round(bytes_topk / (t_topk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                   "rows": c.b * c.hkv * c.lq, "lk": c.lk, "k": c.topk}
         del raw, mk, bo
+
+    # Next-row measurement, outside the step: column-range mask input on the Doc-packed workload
+    # (the pages' column-wise form), one classify + forward + backward with the dense mask and
+    # with the ranges, each timed over a few repetitions.
+    if not args.no_next and args.calibrate_copy_mib == 0:
+        next_rows["column_ranges"] = time_ranges(args, dma, synth, np)
 
     n_skip, n_p, n_f = block_counts(state)
     n_ns = n_p + n_f

@@ -48,6 +48,14 @@ _lib.dma_attn_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
 _lib.dma_attn_bwd.restype = _i32
 _lib.dma_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dma_block_classify_ranges.restype = _i32
+_lib.dma_block_classify_ranges.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp]
+_lib.dma_attn_fwd_ranges.restype = _i32
+_lib.dma_attn_fwd_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _i32,
+                                     _vp, _vp, _vp]
+_lib.dma_attn_bwd_ranges.restype = _i32
+_lib.dma_attn_bwd_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                     _i64, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dma_topk_mask.restype = _i32
 _lib.dma_topk_mask.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
 
@@ -140,6 +148,44 @@ def dma_attn_bwd(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, i
                            _ptr(dbias, "dbias", torch.bfloat16), _ptr(workspace, "workspace"),
                            workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dma_attn_bwd", st)
+
+
+def dma_block_classify_ranges(start_row, end_row, b: int, hkv: int, lq: int, lk: int, is_causal: bool, block_state,
+                              stream=None) -> None:
+    """Block classes from column ranges: key j of plane (b, g) attends rows start_row <= i < end_row."""
+    st = _lib.dma_block_classify_ranges(_ptr(start_row, "start_row", torch.int32), _ptr(end_row, "end_row", torch.int32),
+                                        b, hkv, lq, lk, int(bool(is_causal)),
+                                        _ptr(block_state, "block_state", torch.uint8), _stream(stream))
+    _check("dma_block_classify_ranges", st)
+
+
+def dma_attn_fwd_ranges(q, k, v, start_row, end_row, bias, block_state, scale: float, is_causal: bool, o, lse,
+                        stream=None) -> None:
+    b, lq, hq, d = q.shape
+    lk, hkv = k.shape[1], k.shape[2]
+    st = _lib.dma_attn_fwd_ranges(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                  _ptr(v, "v", torch.bfloat16), _ptr(start_row, "start_row", torch.int32),
+                                  _ptr(end_row, "end_row", torch.int32), _ptr(bias, "bias", torch.bfloat16),
+                                  _ptr(block_state, "block_state", torch.uint8), b, lq, lk, hq, hkv, d, float(scale),
+                                  int(bool(is_causal)), _ptr(o, "o", torch.bfloat16), _ptr(lse, "lse", torch.float32),
+                                  _stream(stream))
+    _check("dma_attn_fwd_ranges", st)
+
+
+def dma_attn_bwd_ranges(q, k, v, start_row, end_row, bias, block_state, o, dout, lse, scale: float, is_causal: bool,
+                        dq, dk, dv, dbias, workspace, stream=None) -> None:
+    b, lq, hq, d = q.shape
+    lk, hkv = k.shape[1], k.shape[2]
+    st = _lib.dma_attn_bwd_ranges(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                  _ptr(v, "v", torch.bfloat16), _ptr(start_row, "start_row", torch.int32),
+                                  _ptr(end_row, "end_row", torch.int32), _ptr(bias, "bias", torch.bfloat16),
+                                  _ptr(block_state, "block_state", torch.uint8), _ptr(o, "o", torch.bfloat16),
+                                  _ptr(dout, "dout", torch.bfloat16), _ptr(lse, "lse", torch.float32), b, lq, lk, hq,
+                                  hkv, d, float(scale), int(bool(is_causal)), _ptr(dq, "dq", torch.bfloat16),
+                                  _ptr(dk, "dk", torch.bfloat16), _ptr(dv, "dv", torch.bfloat16),
+                                  _ptr(dbias, "dbias", torch.bfloat16), _ptr(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dma_attn_bwd_ranges", st)
 
 
 class _DMAttention(torch.autograd.Function):

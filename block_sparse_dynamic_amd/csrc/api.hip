@@ -69,9 +69,17 @@ int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq,
   return hip_status(dma::launch_classify(mask, b, hkv, lq, lk, is_causal, block_state, (hipStream_t)stream));
 }
 
-int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
-                 const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
-                 float scale, int is_causal, uint16_t* o, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shared by the dense-mask and the column-range entry points (at most one of mask and
+// rstart / rend is given).
+int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const int32_t* rstart,
+                  const int32_t* rend, const uint16_t* bias, const uint8_t* block_state, int64_t b, int64_t lq,
+                  int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* o, float* lse,
+                  void* stream) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !lse || !aligned16(o) || !aligned16(lse)) return DMA_ERR_INVALID_ARGUMENT;
@@ -80,6 +88,8 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   a.k = k;
   a.v = v;
   a.mask = mask;
+  a.rstart = rstart;
+  a.rend = rend;
   a.bias = bias;
   a.state = block_state;
   a.o_out = o;
@@ -93,6 +103,35 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   a.scale = scale;
   a.causal = is_causal;
   return hip_status(dma::launch_fwd(a, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
+                 const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                 float scale, int is_causal, uint16_t* o, float* lse, void* stream) {
+  return attn_fwd_impl(q, k, v, mask, nullptr, nullptr, bias, block_state, b, lq, lk, hq, hkv, d, scale, is_causal, o,
+                       lse, stream);
+}
+
+int dma_block_classify_ranges(const int32_t* start_row, const int32_t* end_row, int64_t b, int64_t hkv, int64_t lq,
+                              int64_t lk, int is_causal, uint8_t* block_state, void* stream) {
+  if (!start_row || !end_row || !block_state || !sizes_ok(b, lq, lk, 1, hkv)) return DMA_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return DMA_ERR_INVALID_ARGUMENT;
+  if (!aligned4(start_row) || !aligned4(end_row)) return DMA_ERR_INVALID_ARGUMENT;
+  if (b * hkv > 65535 || (lq + 63) / 64 > 65535) return DMA_ERR_UNSUPPORTED;
+  return hip_status(
+      dma::launch_classify_ranges(start_row, end_row, b, hkv, lq, lk, is_causal, block_state, (hipStream_t)stream));
+}
+
+int dma_attn_fwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* start_row,
+                        const int32_t* end_row, const uint16_t* bias, const uint8_t* block_state, int64_t b, int64_t lq,
+                        int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* o,
+                        float* lse, void* stream) {
+  if (!start_row || !end_row || !aligned4(start_row) || !aligned4(end_row)) return DMA_ERR_INVALID_ARGUMENT;
+  return attn_fwd_impl(q, k, v, nullptr, start_row, end_row, bias, block_state, b, lq, lk, hq, hkv, d, scale,
+                       is_causal, o, lse, stream);
 }
 
 }  // extern "C"
@@ -131,10 +170,14 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq
   return ws_layout(b, lq, lk, hq, hkv, d, is_causal).total;
 }
 
-int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
-                 const uint8_t* block_state, const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b,
-                 int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq,
-                 uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const int32_t* rstart,
+                  const int32_t* rend, const uint16_t* bias, const uint8_t* block_state, const uint16_t* o,
+                  const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv,
+                  int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !dout || !lse || !dq || !dk || !dv || !workspace) return DMA_ERR_INVALID_ARGUMENT;
@@ -153,6 +196,8 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   a.k = k;
   a.v = v;
   a.mask = mask;
+  a.rstart = rstart;
+  a.rend = rend;
   a.bias = bias;
   a.state = block_state;
   a.o = o;
@@ -178,6 +223,27 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
   a.scale = scale;
   a.causal = is_causal;
   return hip_status(dma::launch_bwd(a, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
+                 const uint8_t* block_state, const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b,
+                 int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq,
+                 uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd_impl(q, k, v, mask, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d, scale,
+                       is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+}
+
+int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* start_row,
+                        const int32_t* end_row, const uint16_t* bias, const uint8_t* block_state, const uint16_t* o,
+                        const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq,
+                        int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                        uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!start_row || !end_row || !aligned4(start_row) || !aligned4(end_row)) return DMA_ERR_INVALID_ARGUMENT;
+  return attn_bwd_impl(q, k, v, nullptr, start_row, end_row, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d,
+                       scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 int dma_topk_mask(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out, uint16_t* bias_out,

@@ -149,6 +149,8 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* mask;
+  const int32_t* rstart;  // column ranges (instead of the mask): key j attends rows rstart[j] <= i < rend[j]
+  const int32_t* rend;
   const uint16_t* bias;
   const uint8_t* state;
   const uint16_t* dout;
@@ -223,7 +225,7 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D>
+template <int D, bool R>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   using Smem = BwdSmem<D>;
   constexpr int SR = kRows;
@@ -274,6 +276,14 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     }
     live[0] = __syncthreads_or(any0) != 0;
     live[1] = __syncthreads_or(any1) != 0;
+  }
+
+  // range input: this lane's key attends the rows [krs, kre) (its column range, fixed for the kernel)
+  int krs = 0, kre = 0;
+  if constexpr (R) {
+    const int64_t j = min(key_abs, p.lk - 1);
+    krs = p.rstart[(int64_t)plane * p.lk + j];
+    kre = p.rend[(int64_t)plane * p.lk + j];
   }
 
   // this lane's key rows of K and V, the B operands of S = Q K^T and dP = dO V^T
@@ -490,7 +500,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = gi * 8 + hi * 4 + e;
-          const bool pv = (!has_mask || (xm[e] & 0x7FFF) != 0) && r >= first_r;
+          bool attends = !has_mask || (xm[e] & 0x7FFF) != 0;
+          if constexpr (R) attends = krs <= i0 + r && i0 + r < kre;
+          const bool pv = attends && r >= first_r;
           const bool v = key_ok && r < rows_left && (!partial || pv);
           iv[e] = v ? __uint_as_float((uint32_t)(uint16_t)xb[e] << 16) * inv_scale : neg_inf_s;
         }
@@ -821,6 +833,8 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.k = a.k;
   p.v = a.v;
   p.mask = a.mask;
+  p.rstart = a.rstart;
+  p.rend = a.rend;
   p.bias = a.bias;
   p.state = a.state;
   p.dout = a.dout;
@@ -843,10 +857,18 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.total_wg = (int)(a.b * a.hkv * p.nkb2);
   p.scale = a.scale;
   p.causal = a.causal;
-  if (a.d == 64)
-    hipLaunchKernelGGL(bwd_main_kernel<64>, dim3(p.total_wg), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(bwd_main_kernel<128>, dim3(p.total_wg), dim3(256), 0, stream, p);
+  const bool R = a.rstart != nullptr;
+  if (a.d == 64) {
+    if (R)
+      hipLaunchKernelGGL((bwd_main_kernel<64, true>), dim3(p.total_wg), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_main_kernel<64, false>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  } else {
+    if (R)
+      hipLaunchKernelGGL((bwd_main_kernel<128, true>), dim3(p.total_wg), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_main_kernel<128, false>), dim3(p.total_wg), dim3(256), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -59,6 +59,50 @@ __global__ __launch_bounds__(256) void classify_kernel(const uint16_t* __restric
   if (lane == 0) *out = block_any ? (block_all ? kFull : kPartial) : kSkip;
 }
 
+// The same classes from column ranges (FlashMask README, column-wise sparse representation):
+// key column j attends rows start_row[j] <= i < end_row[j].  One wavefront per block, lane c
+// on column j0 + c: the rows of its column that are valid inside the block form one interval,
+// so "any" and "all" of the block follow from 64 intervals and two ballots, without reading
+// any mask.
+__global__ __launch_bounds__(256) void classify_ranges_kernel(const int32_t* __restrict__ rstart,
+                                                               const int32_t* __restrict__ rend, int64_t lq,
+                                                               int64_t lk, int nqb, int nkb, int causal,
+                                                               uint8_t* __restrict__ state) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kb = blockIdx.x * 4 + wave;
+  const int qb = blockIdx.y;
+  const int64_t plane = blockIdx.z;
+  if (kb >= nkb) return;
+  const int64_t i0 = (int64_t)qb * kBlock, j0 = (int64_t)kb * kBlock;
+  const int64_t i_end = min(i0 + kBlock, lq);
+  const int64_t shift = lk - lq;
+  uint8_t* out = state + ((plane * nqb + qb) * (int64_t)nkb + kb);
+  if (causal && j0 > i_end - 1 + shift) {
+    if (lane == 0) *out = kSkip;
+    return;
+  }
+  const int64_t j = j0 + lane;
+  bool any = false, all = false;
+  if (j < lk) {
+    int64_t lo = max((int64_t)rstart[plane * lk + j], i0);
+    const int64_t hi = min((int64_t)rend[plane * lk + j], i_end);
+    if (causal) lo = max(lo, j - shift);
+    any = lo < hi;
+    all = lo == i0 && hi == i0 + kBlock;  // every one of the block's 64 rows exists and is valid
+  }
+  const bool block_any = __any(any);
+  const bool block_all = __all(all);
+  if (lane == 0) *out = block_any ? (block_all ? kFull : kPartial) : kSkip;
+}
+
+hipError_t launch_classify_ranges(const int32_t* rstart, const int32_t* rend, int64_t b, int64_t hkv, int64_t lq,
+                                  int64_t lk, int causal, uint8_t* state, hipStream_t stream) {
+  const int nqb = (int)((lq + kBlock - 1) / kBlock), nkb = (int)((lk + kBlock - 1) / kBlock);
+  dim3 grid((nkb + 3) / 4, nqb, (unsigned)(b * hkv));
+  hipLaunchKernelGGL(classify_ranges_kernel, grid, dim3(256), 0, stream, rstart, rend, lq, lk, nqb, nkb, causal, state);
+  return hipGetLastError();
+}
+
 hipError_t launch_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int causal,
                            uint8_t* state, hipStream_t stream) {
   const int nqb = (int)((lq + kBlock - 1) / kBlock), nkb = (int)((lk + kBlock - 1) / kBlock);

@@ -138,12 +138,16 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 namespace dma {
 hipError_t launch_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int causal,
                            uint8_t* state, hipStream_t stream);
+hipError_t launch_classify_ranges(const int32_t* rstart, const int32_t* rend, int64_t b, int64_t hkv, int64_t lq,
+                                  int64_t lk, int causal, uint8_t* state, hipStream_t stream);
 
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* mask;
+  const int32_t* rstart;  // column ranges instead of the mask: key j attends rows rstart[j] <= i < rend[j]
+  const int32_t* rend;
   const uint16_t* bias;
   const uint8_t* state;
   const uint16_t* o;

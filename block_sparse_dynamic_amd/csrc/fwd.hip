@@ -43,6 +43,8 @@ struct FwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* mask;
+  const int32_t* rstart;  // column ranges (instead of the mask): key j attends rows rstart[j] <= i < rend[j]
+  const int32_t* rend;
   const uint16_t* bias;
   const uint8_t* state;
   uint16_t* o;
@@ -54,8 +56,8 @@ struct FwdParams {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kStateChunkF = 1024;
-constexpr float kRescaleMargin = 8.f * 0.69314718f;  // natural-log units  // key blocks whose states are cached in LDS at a time
+constexpr int kStateChunkF = 1024;                    // key blocks whose states are cached in LDS at a time
+constexpr float kRescaleMargin = 8.f * 0.69314718f;  // natural-log units
 constexpr uint16_t kBf16NegInf = 0xFF80u;
 
 template <int D>
@@ -66,9 +68,11 @@ struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay s
   uint16_t v[kBlock * kRow];
   uint16_t b[kBlock * kBRow];  // effective bias, bf16 bits
   uint8_t st[kStateChunkF];    // block states of this query block's row, a chunk at a time
+  int32_t rs[2][kBlock];       // column ranges of the current and the next key block (range input)
+  int32_t re[2][kBlock];
 };
 
-template <int D, int HC>
+template <int D, int HC, bool R>
 __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   constexpr int NT = HC * 128;
   constexpr int KR = FwdSmem<D>::kRow, BR = FwdSmem<D>::kBRow;
@@ -140,7 +144,15 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   // compiler wait for the whole prefetch.
   constexpr int KN = kBlock * (D / 8) / NT, BN = kBlock * 8 / NT;
   u32x4 pk[KN], pv[KN], pb[BN], pm[BN];
+  int32_t prs = 0, pre = 0;  // column range of key kb*64 + tid (range input, tid < 64)
+  const int32_t* rs_plane = R ? p.rstart + (int64_t)plane * p.lk : nullptr;
+  const int32_t* re_plane = R ? p.rend + (int64_t)plane * p.lk : nullptr;
   auto prefetch = [&](int kb, uint8_t st) {
+    if constexpr (R) {  // first, so that waiting for them never waits for the tiles below
+      const int64_t j = min((int64_t)kb * kBlock + (tid & 63), p.lk - 1);
+      prs = rs_plane[j];
+      pre = re_plane[j];
+    }
 #pragma unroll
     for (int n = 0; n < KN; ++n) {
       const int task = tid + n * NT;
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
       const int64_t off = (i < p.lq && j0 < p.lk) ? i * p.lk + j0 : corner;
       pb[n] = *reinterpret_cast<const u32x4*>(has_bias ? p.bias + plane_off + off : p.q);
-      pm[n] = *reinterpret_cast<const u32x4*>((has_mask && st != kFull) ? p.mask + plane_off + off : p.q);
+      if constexpr (!R) pm[n] = *reinterpret_cast<const u32x4*>((has_mask && st != kFull) ? p.mask + plane_off + off : p.q);
     }
   };
 
@@ -180,6 +192,13 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   int kb = next_kb(0);
   uint8_t st = kb < p.nkb ? sm.st[kb - cache_lo] : kSkip;
   if (kb < p.nkb) prefetch(kb, st);
+  int rpar = 0;  // which of the two range buffers holds the current block's ranges
+  if constexpr (R) {
+    if (tid < kBlock) {
+      sm.rs[0][tid] = prs;
+      sm.re[0][tid] = pre;
+    }
+  }
   while (kb < p.nkb) {
     const bool full = (st == kFull);
     lds_barrier();  // the previous block's LDS reads are done
@@ -205,7 +224,23 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         const bool inside = i < p.lq && j0 < p.lk;
         u32x4 bw = (has_bias && inside) ? pb[n] : u32x4{0u, 0u, 0u, 0u};
         if (!full) {
-          const u32x4 mw = has_mask ? pm[n] : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+          u32x4 mw;
+          if constexpr (R) {  // attends iff start <= i < end of the key's column
+            const int4 s0 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8]);
+            const int4 s1 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8 + 4]);
+            const int4 e0 = *reinterpret_cast<const int4*>(&sm.re[rpar][c * 8]);
+            const int4 e1 = *reinterpret_cast<const int4*>(&sm.re[rpar][c * 8 + 4]);
+            const int rs8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            const int re8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool a0 = rs8[2 * e] <= i && i < re8[2 * e];
+              const bool a1 = rs8[2 * e + 1] <= i && i < re8[2 * e + 1];
+              mw[e] = (a0 ? 0x3F80u : 0u) | (a1 ? 0x3F800000u : 0u);
+            }
+          } else {
+            mw = has_mask ? pm[n] : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t j = j0 + 2 * e;
@@ -312,6 +347,13 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         }
       }
     }
+    if constexpr (R) {  // the next block's ranges go to the other buffer, read after the next barrier
+      if (tid < kBlock) {
+        sm.rs[rpar ^ 1][tid] = prs;
+        sm.re[rpar ^ 1][tid] = pre;
+      }
+      rpar ^= 1;
+    }
     kb = kb_next;
     st = st_next;
   }
@@ -336,7 +378,10 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 
 template <int D, int HC>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, HC>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
+  if (p.rstart != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<D, HC, true>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, HC, false>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -346,6 +391,8 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.k = a.k;
   p.v = a.v;
   p.mask = a.mask;
+  p.rstart = a.rstart;
+  p.rend = a.rend;
   p.bias = a.bias;
   p.state = a.state;
   p.o = a.o_out;

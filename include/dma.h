@@ -144,6 +144,37 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Column-range mask input (FlashMask README, column-wise sparse representation:
+ * per key column, the rows that may attend form one interval; O(L) memory).
+ * Instead of the dense mask, key column j of plane (b, g) attends exactly the
+ * rows i with start_row[b,g,j] <= i < end_row[b,g,j]; causality, the bias and
+ * everything else are as in the dense entry points, and every result equals the
+ * dense entry point's on the expanded mask (mask[b,g,i,j] = 1.0 on those rows,
+ * 0 elsewhere).  An empty interval (start >= end) masks the whole column; the
+ * bounds may lie outside [0, lq).
+ *
+ *   start_row, end_row  int32 [b, hkv, lk], device pointers, 4-byte aligned
+ *
+ * dma_block_classify_ranges writes the same bitmap as dma_block_classify on the
+ * expanded mask, reading 8 bytes per key column and block row instead of the
+ * mask.  dma_attn_fwd_ranges / dma_attn_bwd_ranges take the ranges where the
+ * dense entry points take mask; their other arguments, layouts, workspace and
+ * errors are those of dma_attn_fwd / dma_attn_bwd (NULL or misaligned ranges:
+ * DMA_ERR_INVALID_ARGUMENT).
+ */
+int dma_block_classify_ranges(const int32_t* start_row, const int32_t* end_row, int64_t b, int64_t hkv, int64_t lq,
+                              int64_t lk, int is_causal, uint8_t* block_state, void* stream);
+int dma_attn_fwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* start_row,
+                        const int32_t* end_row, const uint16_t* bias, const uint8_t* block_state, int64_t b, int64_t lq,
+                        int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* o,
+                        float* lse, void* stream);
+int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* start_row,
+                        const int32_t* end_row, const uint16_t* bias, const uint8_t* block_state, const uint16_t* o,
+                        const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq,
+                        int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                        uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Top-k mask construction (Flash-DMA README, usage example: keep the
  * keep_window_size largest bias values of every query row; everything else is
  * masked, and its bias is set to the smallest bf16 value).

@@ -33,6 +33,10 @@ def lib():
                                vp, vp, sz, vp]
     L.dma_status_string.restype = ctypes.c_char_p
     L.dma_topk_mask.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    L.dma_block_classify_ranges.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp, vp]
+    L.dma_attn_fwd_ranges.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp]
+    L.dma_attn_bwd_ranges.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp,
+                                      vp, vp, vp, vp, sz, vp]
     return L
 
 
@@ -45,7 +49,8 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("dma_block_classify", "dma_attn_fwd", "dma_attn_bwd", "dma_attn_bwd_workspace_size",
-                 "dma_block_size", "dma_status_string", "dma_topk_mask"):
+                 "dma_block_size", "dma_status_string", "dma_topk_mask", "dma_block_classify_ranges",
+                 "dma_attn_fwd_ranges", "dma_attn_bwd_ranges"):
         assert name in syms
 
 
@@ -179,3 +184,22 @@ def test_topk_rejects(lib, kw, want):
     a = dict(bias=P, rows=4, lk=1024, k=64, mask=P + 0x100000, out=P + 0x200000)
     a.update(kw)
     assert lib.dma_topk_mask(a["bias"], a["rows"], a["lk"], a["k"], a["mask"], a["out"], None) == want
+
+
+def test_ranges_reject(lib):
+    # NULL or misaligned ranges; the rest of the validation is shared with the dense entry points
+    c = lib.dma_block_classify_ranges
+    assert c(None, P, 1, 1, 128, 128, 1, P, None) == INVALID
+    assert c(P, P + 2, 1, 1, 128, 128, 1, P, None) == INVALID
+    assert c(P, P, 1, 1, 128, 128, 2, P, None) == INVALID
+    assert c(P, P, 0, 1, 128, 128, 1, P, None) == INVALID
+    f = lib.dma_attn_fwd_ranges
+    args = [P, P, P, P, P, P, P, 1, 128, 128, 4, 2, 128, 0.1, 1, P, P, None]
+    assert f(*args[:3], None, *args[4:]) == INVALID
+    assert f(*args[:4], P + 1, *args[5:]) == INVALID
+    assert f(*args[:12], 96, *args[13:]) == UNSUPPORTED
+    g = lib.dma_attn_bwd_ranges
+    bargs = [P, P, P, P, P, P, P, P, P, P, 1, 128, 128, 4, 2, 128, 0.1, 1, P, P, P, P, P, 1 << 40, None]
+    assert g(*bargs[:3], None, *bargs[4:]) == INVALID
+    assert g(*bargs[:15], 80, *bargs[16:]) == UNSUPPORTED
+    assert g(*bargs[:16], 0.0, *bargs[17:]) == INVALID
