@@ -11,6 +11,10 @@ MMA FLOPs over the non-SKIP 64x64 blocks (4*d per block element per query head
 forward, 10*d backward; FlashMask README, Performance: theoretical FLOPs count
 only the core matrix multiplies) divided by the time of the whole step,
 classification included.
+
+``next_rows`` (outside the step, skipped with --no-next): the GPU top-k mask construction on a
+fresh N(0,1) bias of the workload's shape, and one classify + forward + backward of the
+Doc-packed workload with the dense mask and with column ranges.
 """
 from __future__ import annotations
 
