@@ -13,8 +13,9 @@ only the core matrix multiplies) divided by the time of the whole step,
 classification included.
 
 ``next_rows`` (outside the step, skipped with --no-next): the GPU top-k mask construction on a
-fresh N(0,1) bias of the workload's shape, and one classify + forward + backward of the
-Doc-packed workload with the dense mask and with column ranges.
+fresh N(0,1) bias of the workload's shape; the step with the bit-packed PARTIAL-block mask
+instead of the bf16 mask, per phase; and one classify + forward + backward of the Doc-packed
+workload with the dense mask and with column ranges.
 """
 from __future__ import annotations
 
@@ -220,6 +221,36 @@ def time_ranges(args, dma, synth, np):
     return out
 
 
+def time_bits(c, dma, np, q, k, v, do, mask, bias, o, lse, dq, dk, dv, dbias, ws, stream, dense_ms):
+    import torch
+
+    st = torch.empty(dma.block_state_shape(c.b, c.hkv, c.lq, c.lk), dtype=torch.uint8, device="cuda")
+    mb = torch.empty((dma.dma_mask_bits_size(c.b, c.hkv, c.lq, c.lk),), dtype=torch.uint8, device="cuda")
+    reps = 3
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + 1)]
+    for r in range(reps + 1):  # the first repetition warms up
+        e = ev[r]
+        e[0].record(stream)
+        dma.dma_block_classify_bits(mask, c.b, c.hkv, c.lq, c.lk, c.causal, st, mb, stream)
+        e[1].record(stream)
+        dma.dma_attn_fwd_bits(q, k, v, mb, bias, st, c.scale_f32, c.causal, o, lse, stream)
+        e[2].record(stream)
+        dma.dma_attn_bwd_bits(q, k, v, mb, bias, st, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws, stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in ev[1:]])
+    t = t.mean(axis=0)
+    n_p = int((st == 1).sum())
+    out = {"classify_ms": round(float(t[0]), 4), "fwd_ms": round(float(t[1]), 4), "bwd_ms": round(float(t[2]), 4),
+           "step_ms": round(float(t.sum()), 4), "dense_step_ms": round(float(sum(dense_ms)), 4),
+           "blocks_partial": n_p,
+           # mask bytes read by forward + backward: bf16 tiles of the dense path, bits here
+           "mask_bytes_dense": 2 * 2.0 * 64 * 64 * n_p, "mask_bytes_bits": 2 * 512.0 * n_p,
+           "bits_bytes_written": 512.0 * n_p}
+    del st, mb
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -316,6 +347,13 @@ def main():
                                   "frac_hbm": round(bytes_topk / (t_topk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                   "rows": c.b * c.hkv * c.lq, "lk": c.lk, "k": c.topk}
         del raw, mk, bo
+
+    # Next-row measurement, outside the step: the same step with the bit-packed PARTIAL-block
+    # mask (classification writes 512 B per PARTIAL block; forward and backward read those bits
+    # instead of the bf16 mask), per phase over a few repetitions.
+    if c.mask != "none" and not args.no_next and args.calibrate_copy_mib == 0:
+        next_rows["mask_bits"] = time_bits(c, dma, np, q, k, v, do, mask, bias, o, lse, dq, dk, dv, dbias, ws,
+                                           stream, (t_cls, t_fwd, t_bwd))
 
     # Next-row measurement, outside the step: column-range mask input on the Doc-packed workload
     # (the pages' column-wise form), one classify + forward + backward with the dense mask and

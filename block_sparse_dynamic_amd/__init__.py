@@ -56,6 +56,16 @@ _lib.dma_attn_fwd_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i
 _lib.dma_attn_bwd_ranges.restype = _i32
 _lib.dma_attn_bwd_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                      _i64, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dma_mask_bits_size.restype = _sz
+_lib.dma_mask_bits_size.argtypes = [_i64, _i64, _i64, _i64]
+_lib.dma_block_classify_bits.restype = _i32
+_lib.dma_block_classify_bits.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp]
+_lib.dma_attn_fwd_bits.restype = _i32
+_lib.dma_attn_fwd_bits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _i32, _vp,
+                                   _vp, _vp]
+_lib.dma_attn_bwd_bits.restype = _i32
+_lib.dma_attn_bwd_bits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                   _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dma_topk_mask.restype = _i32
 _lib.dma_topk_mask.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
 
@@ -188,6 +198,48 @@ def dma_attn_bwd_ranges(q, k, v, start_row, end_row, bias, block_state, o, dout,
     _check("dma_attn_bwd_ranges", st)
 
 
+def dma_mask_bits_size(b: int, hkv: int, lq: int, lk: int) -> int:
+    """Bytes of the bit-packed PARTIAL-block mask: 512 per 64 x 64 block."""
+    return int(_lib.dma_mask_bits_size(b, hkv, lq, lk))
+
+
+def dma_block_classify_bits(mask, b: int, hkv: int, lq: int, lk: int, is_causal: bool, block_state, mask_bits,
+                            stream=None) -> None:
+    """dma_block_classify plus, in the same pass, the mask bits of every PARTIAL block."""
+    st = _lib.dma_block_classify_bits(_ptr(mask, "mask", torch.bfloat16), b, hkv, lq, lk, int(bool(is_causal)),
+                                      _ptr(block_state, "block_state", torch.uint8),
+                                      _ptr(mask_bits, "mask_bits", torch.uint8), _stream(stream))
+    _check("dma_block_classify_bits", st)
+
+
+def dma_attn_fwd_bits(q, k, v, mask_bits, bias, block_state, scale: float, is_causal: bool, o, lse,
+                      stream=None) -> None:
+    b, lq, hq, d = q.shape
+    lk, hkv = k.shape[1], k.shape[2]
+    st = _lib.dma_attn_fwd_bits(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                _ptr(v, "v", torch.bfloat16), _ptr(mask_bits, "mask_bits", torch.uint8),
+                                _ptr(bias, "bias", torch.bfloat16), _ptr(block_state, "block_state", torch.uint8), b,
+                                lq, lk, hq, hkv, d, float(scale), int(bool(is_causal)), _ptr(o, "o", torch.bfloat16),
+                                _ptr(lse, "lse", torch.float32), _stream(stream))
+    _check("dma_attn_fwd_bits", st)
+
+
+def dma_attn_bwd_bits(q, k, v, mask_bits, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq, dk, dv,
+                      dbias, workspace, stream=None) -> None:
+    b, lq, hq, d = q.shape
+    lk, hkv = k.shape[1], k.shape[2]
+    st = _lib.dma_attn_bwd_bits(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                _ptr(v, "v", torch.bfloat16), _ptr(mask_bits, "mask_bits", torch.uint8),
+                                _ptr(bias, "bias", torch.bfloat16), _ptr(block_state, "block_state", torch.uint8),
+                                _ptr(o, "o", torch.bfloat16), _ptr(dout, "dout", torch.bfloat16),
+                                _ptr(lse, "lse", torch.float32), b, lq, lk, hq, hkv, d, float(scale),
+                                int(bool(is_causal)), _ptr(dq, "dq", torch.bfloat16), _ptr(dk, "dk", torch.bfloat16),
+                                _ptr(dv, "dv", torch.bfloat16), _ptr(dbias, "dbias", torch.bfloat16),
+                                _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check("dma_attn_bwd_bits", st)
+
+
 class _DMAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, query, key, value, attn_mask, attn_bias, is_causal, scale):
@@ -233,4 +285,6 @@ def dma_attention(query, key, value, attn_mask=None, attn_bias=None, is_causal=F
 __all__ = [
     "dma_block_size", "dma_status_string", "dma_block_classify", "dma_attn_fwd", "dma_attn_bwd_workspace_size",
     "dma_attn_bwd", "dma_attention", "block_state_shape", "DMAError", "LIB_PATH", "HEADER_PATH",
+    "dma_block_classify_ranges", "dma_attn_fwd_ranges", "dma_attn_bwd_ranges", "dma_topk_mask", "dma_mask_bits_size",
+    "dma_block_classify_bits", "dma_attn_fwd_bits", "dma_attn_bwd_bits",
 ]

@@ -66,7 +66,24 @@ int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq,
   if (is_causal != 0 && is_causal != 1) return DMA_ERR_INVALID_ARGUMENT;
   if (mask && (lk % 8 != 0 || !aligned16(mask))) return DMA_ERR_INVALID_ARGUMENT;
   if (b * hkv > 65535 || (lq + 63) / 64 > 65535) return DMA_ERR_UNSUPPORTED;
-  return hip_status(dma::launch_classify(mask, b, hkv, lq, lk, is_causal, block_state, (hipStream_t)stream));
+  return hip_status(dma::launch_classify(mask, b, hkv, lq, lk, is_causal, block_state, nullptr, (hipStream_t)stream));
+}
+
+size_t dma_mask_bits_size(int64_t b, int64_t hkv, int64_t lq, int64_t lk) {
+  if (!sizes_ok(b, lq, lk, 1, hkv)) return 0;
+  return (size_t)b * hkv * ((lq + 63) / 64) * ((lk + 63) / 64) * dma::kBitsPerBlock;
+}
+
+int dma_block_classify_bits(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int is_causal,
+                            uint8_t* block_state, uint8_t* mask_bits, void* stream) {
+  if (!mask || !mask_bits) return DMA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(mask_bits)) return DMA_ERR_INVALID_ARGUMENT;
+  if (!block_state || !sizes_ok(b, lq, lk, 1, hkv)) return DMA_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return DMA_ERR_INVALID_ARGUMENT;
+  if (lk % 8 != 0 || !aligned16(mask)) return DMA_ERR_INVALID_ARGUMENT;
+  if (b * hkv > 65535 || (lq + 63) / 64 > 65535) return DMA_ERR_UNSUPPORTED;
+  return hip_status(
+      dma::launch_classify(mask, b, hkv, lq, lk, is_causal, block_state, mask_bits, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -77,9 +94,9 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Shared by the dense-mask and the column-range entry points (at most one of mask and
 // rstart / rend is given).
 int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const int32_t* rstart,
-                  const int32_t* rend, const uint16_t* bias, const uint8_t* block_state, int64_t b, int64_t lq,
-                  int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* o, float* lse,
-                  void* stream) {
+                  const int32_t* rend, const uint8_t* mbits, const uint16_t* bias, const uint8_t* block_state,
+                  int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal,
+                  uint16_t* o, float* lse, void* stream) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !lse || !aligned16(o) || !aligned16(lse)) return DMA_ERR_INVALID_ARGUMENT;
@@ -90,6 +107,7 @@ int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.mask = mask;
   a.rstart = rstart;
   a.rend = rend;
+  a.mbits = mbits;
   a.bias = bias;
   a.state = block_state;
   a.o_out = o;
@@ -111,8 +129,8 @@ extern "C" {
 int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
                  const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
                  float scale, int is_causal, uint16_t* o, float* lse, void* stream) {
-  return attn_fwd_impl(q, k, v, mask, nullptr, nullptr, bias, block_state, b, lq, lk, hq, hkv, d, scale, is_causal, o,
-                       lse, stream);
+  return attn_fwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, b, lq, lk, hq, hkv, d, scale,
+                       is_causal, o, lse, stream);
 }
 
 int dma_block_classify_ranges(const int32_t* start_row, const int32_t* end_row, int64_t b, int64_t hkv, int64_t lq,
@@ -125,12 +143,20 @@ int dma_block_classify_ranges(const int32_t* start_row, const int32_t* end_row, 
       dma::launch_classify_ranges(start_row, end_row, b, hkv, lq, lk, is_causal, block_state, (hipStream_t)stream));
 }
 
+int dma_attn_fwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* mask_bits,
+                      const uint16_t* bias, const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq,
+                      int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* o, float* lse, void* stream) {
+  if (!mask_bits || !aligned16(mask_bits)) return DMA_ERR_INVALID_ARGUMENT;
+  return attn_fwd_impl(q, k, v, nullptr, nullptr, nullptr, mask_bits, bias, block_state, b, lq, lk, hq, hkv, d, scale,
+                       is_causal, o, lse, stream);
+}
+
 int dma_attn_fwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* start_row,
                         const int32_t* end_row, const uint16_t* bias, const uint8_t* block_state, int64_t b, int64_t lq,
                         int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* o,
                         float* lse, void* stream) {
   if (!start_row || !end_row || !aligned4(start_row) || !aligned4(end_row)) return DMA_ERR_INVALID_ARGUMENT;
-  return attn_fwd_impl(q, k, v, nullptr, start_row, end_row, bias, block_state, b, lq, lk, hq, hkv, d, scale,
+  return attn_fwd_impl(q, k, v, nullptr, start_row, end_row, nullptr, bias, block_state, b, lq, lk, hq, hkv, d, scale,
                        is_causal, o, lse, stream);
 }
 
@@ -174,8 +200,8 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq
 
 namespace {
 int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const int32_t* rstart,
-                  const int32_t* rend, const uint16_t* bias, const uint8_t* block_state, const uint16_t* o,
-                  const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv,
+                  const int32_t* rend, const uint8_t* mbits, const uint16_t* bias, const uint8_t* block_state,
+                  const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv,
                   int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
                   void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
@@ -198,6 +224,7 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.mask = mask;
   a.rstart = rstart;
   a.rend = rend;
+  a.mbits = mbits;
   a.bias = bias;
   a.state = block_state;
   a.o = o;
@@ -232,8 +259,18 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  const uint8_t* block_state, const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b,
                  int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq,
                  uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
-  return attn_bwd_impl(q, k, v, mask, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d, scale,
-                       is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+  return attn_bwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d,
+                       scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+}
+
+int dma_attn_bwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* mask_bits,
+                      const uint16_t* bias, const uint8_t* block_state, const uint16_t* o, const uint16_t* dout,
+                      const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                      float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!mask_bits || !aligned16(mask_bits)) return DMA_ERR_INVALID_ARGUMENT;
+  return attn_bwd_impl(q, k, v, nullptr, nullptr, nullptr, mask_bits, bias, block_state, o, dout, lse, b, lq, lk, hq,
+                       hkv, d, scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* start_row,
@@ -242,8 +279,8 @@ int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                         uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
   if (!start_row || !end_row || !aligned4(start_row) || !aligned4(end_row)) return DMA_ERR_INVALID_ARGUMENT;
-  return attn_bwd_impl(q, k, v, nullptr, start_row, end_row, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d,
-                       scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+  return attn_bwd_impl(q, k, v, nullptr, start_row, end_row, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq,
+                       hkv, d, scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 int dma_topk_mask(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out, uint16_t* bias_out,

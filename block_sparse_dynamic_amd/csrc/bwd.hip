@@ -151,6 +151,7 @@ struct BwdParams {
   const uint16_t* mask;
   const int32_t* rstart;  // column ranges (instead of the mask): key j attends rows rstart[j] <= i < rend[j]
   const int32_t* rend;
+  const uint8_t* mbits;  // bit-packed PARTIAL blocks (instead of the mask)
   const uint16_t* bias;
   const uint8_t* state;
   const uint16_t* dout;
@@ -181,7 +182,7 @@ struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay s
   uint16_t q[2][kTile];
   uint16_t g[2][kTile];
   uint16_t b[2][kBTile];
-  uint16_t m[2][kBTile];
+  uint16_t m[2][kBTile];  // raw mask tile, or (bit input) the item's rows of the two blocks' bits
   uint16_t s[2][kSTile];
   float nl2[2][64];  // -lse * log2(e) of the item's rows (rows 32..63 take the out-of-range lanes of the load)
   float nd[2][64];   // -D = -rowsum(dO * O)
@@ -225,7 +226,7 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D, bool R>
+template <int D, int MK>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   using Smem = BwdSmem<D>;
   constexpr int SR = kRows;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 
   // range input: this lane's key attends the rows [krs, kre) (its column range, fixed for the kernel)
   int krs = 0, kre = 0;
-  if constexpr (R) {
+  if constexpr (MK == kMaskRanges) {
     const int64_t j = min(key_abs, p.lk - 1);
     krs = p.rstart[(int64_t)plane * p.lk + j];
     kre = p.rend[(int64_t)plane * p.lk + j];
@@ -408,6 +409,17 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
           dma_x4(rm, lds_m + (uint32_t)B * kBTileBytes + (uint32_t)((wave * 2 + n) * 1024),
                  ((bh[n] ? s1 : s0) == kPartial) ? bv[n] : kOutOfRange);
       }
+      if constexpr (MK == kMaskBits) {
+        // rows rh*32 .. +31 of a PARTIAL key block are 256 contiguous bytes of its bits: wave
+        // 2 + hf fetches those of block hf, one dword per lane, to bytes hf*256 .. of the tile
+        const int hf = wave - 2;
+        if (hf >= 0 && (hf ? s1 : s0) == kPartial) {
+          const uint8_t* src =
+              p.mbits + (((int64_t)plane * p.nqb + qb) * p.nkb + kb0 + hf) * kBitsPerBlock + rh * (kRows * 8);
+          dma_x1(rsrc_words(src, kRows * 8), lds_m + (uint32_t)B * kBTileBytes + (uint32_t)hf * 256u,
+                 (uint32_t)lane * 4u);
+        }
+      }
     }
     const int64_t ridx = (int64_t)hh * p.lq + i0;
     if (wave == 0) dma_x1(rsrc_words(nl2_plane + ridx, (uint32_t)rows_left * 4u), lds_nl2 + (uint32_t)B * 256u, (uint32_t)lane * 4u);
@@ -490,18 +502,22 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       // causal: row r of the item is valid for this key when r >= key - (lk - lq) - i0
       const int64_t cfirst = p.causal ? key_abs - shift - i0 : (int64_t)INT32_MIN;
       const int first_r = (int)max((int64_t)INT32_MIN, min(cfirst, (int64_t)kRows));
+      // bit input: row r's bits of this lane's key are bit l32 of dword r*2 + (wave & 1) of its block
+      const uint32_t* mrow = reinterpret_cast<const uint32_t*>(&sm.m[B][0]) + half * 64 + (wave & 1);
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         // 8 rows down the row term of the swizzle flips chunk bit 1 (element bit 4)
         const int bo = (boff0 + gi * 8 * 128) ^ ((gi & 1) << 4);
         const i16x4 xb = lds_read_tr16(&sm.b[B][bo]);
-        const i16x4 xm = lds_read_tr16(&sm.m[B][bo]);
+        i16x4 xm = {0, 0, 0, 0};
+        if constexpr (MK == kMaskDense) xm = lds_read_tr16(&sm.m[B][bo]);
         f32x4 iv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = gi * 8 + hi * 4 + e;
           bool attends = !has_mask || (xm[e] & 0x7FFF) != 0;
-          if constexpr (R) attends = krs <= i0 + r && i0 + r < kre;
+          if constexpr (MK == kMaskRanges) attends = krs <= i0 + r && i0 + r < kre;
+          if constexpr (MK == kMaskBits) attends = ((mrow[r * 2] >> l32) & 1u) != 0;
           const bool pv = attends && r >= first_r;
           const bool v = key_ok && r < rows_left && (!partial || pv);
           iv[e] = v ? __uint_as_float((uint32_t)(uint16_t)xb[e] << 16) * inv_scale : neg_inf_s;
@@ -833,6 +849,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.k = a.k;
   p.v = a.v;
   p.mask = a.mask;
+  p.mbits = a.mbits;
   p.rstart = a.rstart;
   p.rend = a.rend;
   p.bias = a.bias;
@@ -857,17 +874,16 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.total_wg = (int)(a.b * a.hkv * p.nkb2);
   p.scale = a.scale;
   p.causal = a.causal;
-  const bool R = a.rstart != nullptr;
+  const int MK = a.rstart != nullptr ? kMaskRanges : a.mbits != nullptr ? kMaskBits : kMaskDense;
+  auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(p.total_wg), dim3(256), 0, stream, p); };
   if (a.d == 64) {
-    if (R)
-      hipLaunchKernelGGL((bwd_main_kernel<64, true>), dim3(p.total_wg), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((bwd_main_kernel<64, false>), dim3(p.total_wg), dim3(256), 0, stream, p);
+    if (MK == kMaskRanges) launch_main(bwd_main_kernel<64, kMaskRanges>);
+    else if (MK == kMaskBits) launch_main(bwd_main_kernel<64, kMaskBits>);
+    else launch_main(bwd_main_kernel<64, kMaskDense>);
   } else {
-    if (R)
-      hipLaunchKernelGGL((bwd_main_kernel<128, true>), dim3(p.total_wg), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((bwd_main_kernel<128, false>), dim3(p.total_wg), dim3(256), 0, stream, p);
+    if (MK == kMaskRanges) launch_main(bwd_main_kernel<128, kMaskRanges>);
+    else if (MK == kMaskBits) launch_main(bwd_main_kernel<128, kMaskBits>);
+    else launch_main(bwd_main_kernel<128, kMaskDense>);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -13,7 +13,8 @@
 namespace dma {
 
 __global__ __launch_bounds__(256) void classify_kernel(const uint16_t* __restrict__ mask, int64_t lq, int64_t lk,
-                                                        int nqb, int nkb, int causal, uint8_t* __restrict__ state) {
+                                                        int nqb, int nkb, int causal, uint8_t* __restrict__ state,
+                                                        uint8_t* __restrict__ mbits) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kb = blockIdx.x * 4 + wave;
   const int qb = blockIdx.y;
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(256) void classify_kernel(const uint16_t* __restric
   }
   bool any = false, all = true;
   const int64_t j = j0 + (lane & 7) * 8;
+  uint32_t bytes[2] = {0u, 0u};  // the mask bits of this lane's 8 columns in its 8 rows, one byte per row
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int64_t i = i0 + it * 8 + (lane >> 3);
@@ -43,6 +45,7 @@ __global__ __launch_bounds__(256) void classify_kernel(const uint16_t* __restric
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         bool a0 = attends_lo(w[e]), a1 = attends_hi(w[e]);
+        bytes[it >> 2] |= ((uint32_t)a0 << (2 * e) | (uint32_t)a1 << (2 * e + 1)) << (8 * (it & 3));
         if (diag) {
           a0 = a0 && (j + 2 * e <= i + shift);
           a1 = a1 && (j + 2 * e + 1 <= i + shift);
@@ -57,6 +60,14 @@ __global__ __launch_bounds__(256) void classify_kernel(const uint16_t* __restric
   const bool block_any = __any(any);
   const bool block_all = __all(all);
   if (lane == 0) *out = block_any ? (block_all ? kFull : kPartial) : kSkip;
+  // Bit-packed PARTIAL blocks (the only ones whose mask the attention kernels read): row r of
+  // the block is the 64-bit word at bytes 8r .. 8r+7, bit c = mask of column c (causality not
+  // applied); this lane owns byte lane%8 of rows it*8 + lane/8.
+  if (mbits != nullptr && block_any && !block_all) {
+    uint8_t* dst = mbits + ((plane * nqb + qb) * (int64_t)nkb + kb) * kBitsPerBlock + (lane >> 3) * 8 + (lane & 7);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) dst[it * 64] = (uint8_t)(bytes[it >> 2] >> (8 * (it & 3)));
+  }
 }
 
 // The same classes from column ranges (FlashMask README, column-wise sparse representation):
@@ -104,10 +115,10 @@ hipError_t launch_classify_ranges(const int32_t* rstart, const int32_t* rend, in
 }
 
 hipError_t launch_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int causal,
-                           uint8_t* state, hipStream_t stream) {
+                           uint8_t* state, uint8_t* mbits, hipStream_t stream) {
   const int nqb = (int)((lq + kBlock - 1) / kBlock), nkb = (int)((lk + kBlock - 1) / kBlock);
   dim3 grid((nkb + 3) / 4, nqb, (unsigned)(b * hkv));
-  hipLaunchKernelGGL(classify_kernel, grid, dim3(256), 0, stream, mask, lq, lk, nqb, nkb, causal, state);
+  hipLaunchKernelGGL(classify_kernel, grid, dim3(256), 0, stream, mask, lq, lk, nqb, nkb, causal, state, mbits);
   return hipGetLastError();
 }
 

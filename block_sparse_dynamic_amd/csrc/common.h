@@ -8,6 +8,10 @@ namespace dma {
 
 constexpr int kBlock = 64;  // classification block: 64 query rows x 64 key columns
 constexpr uint8_t kSkip = 0, kPartial = 1, kFull = 2;
+// How the attention kernels learn which (query, key) pairs attend: a dense bf16 mask (or none),
+// per-key row intervals, or the bit-packed PARTIAL blocks written by the classification.
+constexpr int kMaskDense = 0, kMaskRanges = 1, kMaskBits = 2;
+constexpr int kBitsPerBlock = kBlock * kBlock / 8;  // bytes of one block's bits: row r at bytes 8r .. 8r+7
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -137,7 +141,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // Host-side launchers (one per kernel file).
 namespace dma {
 hipError_t launch_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int causal,
-                           uint8_t* state, hipStream_t stream);
+                           uint8_t* state, uint8_t* mbits, hipStream_t stream);
 hipError_t launch_classify_ranges(const int32_t* rstart, const int32_t* rend, int64_t b, int64_t hkv, int64_t lq,
                                   int64_t lk, int causal, uint8_t* state, hipStream_t stream);
 
@@ -148,6 +152,7 @@ struct AttnArgs {
   const uint16_t* mask;
   const int32_t* rstart;  // column ranges instead of the mask: key j attends rows rstart[j] <= i < rend[j]
   const int32_t* rend;
+  const uint8_t* mbits;  // bit-packed PARTIAL blocks instead of the mask, see launch_classify
   const uint16_t* bias;
   const uint8_t* state;
   const uint16_t* o;

@@ -45,6 +45,7 @@ struct FwdParams {
   const uint16_t* mask;
   const int32_t* rstart;  // column ranges (instead of the mask): key j attends rows rstart[j] <= i < rend[j]
   const int32_t* rend;
+  const uint8_t* mbits;   // bit-packed PARTIAL blocks (instead of the mask)
   const uint16_t* bias;
   const uint8_t* state;
   uint16_t* o;
@@ -72,7 +73,7 @@ struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay s
   int32_t re[2][kBlock];
 };
 
-template <int D, int HC, bool R>
+template <int D, int HC, int MK>
 __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   constexpr int NT = HC * 128;
   constexpr int KR = FwdSmem<D>::kRow, BR = FwdSmem<D>::kBRow;
@@ -145,10 +146,12 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   constexpr int KN = kBlock * (D / 8) / NT, BN = kBlock * 8 / NT;
   u32x4 pk[KN], pv[KN], pb[BN], pm[BN];
   int32_t prs = 0, pre = 0;  // column range of key kb*64 + tid (range input, tid < 64)
-  const int32_t* rs_plane = R ? p.rstart + (int64_t)plane * p.lk : nullptr;
-  const int32_t* re_plane = R ? p.rend + (int64_t)plane * p.lk : nullptr;
+  uint32_t pmb[BN];          // mask bits of this thread's 8 keys of its row (bit input)
+  const uint8_t* mb_row = MK == kMaskBits ? p.mbits + ((int64_t)plane * p.nqb + qb) * p.nkb * kBitsPerBlock : nullptr;
+  const int32_t* rs_plane = MK == kMaskRanges ? p.rstart + (int64_t)plane * p.lk : nullptr;
+  const int32_t* re_plane = MK == kMaskRanges ? p.rend + (int64_t)plane * p.lk : nullptr;
   auto prefetch = [&](int kb, uint8_t st) {
-    if constexpr (R) {  // first, so that waiting for them never waits for the tiles below
+    if constexpr (MK == kMaskRanges) {  // first, so that waiting for them never waits for the tiles below
       const int64_t j = min((int64_t)kb * kBlock + (tid & 63), p.lk - 1);
       prs = rs_plane[j];
       pre = re_plane[j];
@@ -170,7 +173,9 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
       const int64_t off = (i < p.lq && j0 < p.lk) ? i * p.lk + j0 : corner;
       pb[n] = *reinterpret_cast<const u32x4*>(has_bias ? p.bias + plane_off + off : p.q);
-      if constexpr (!R) pm[n] = *reinterpret_cast<const u32x4*>((has_mask && st != kFull) ? p.mask + plane_off + off : p.q);
+      if constexpr (MK == kMaskDense)
+        pm[n] = *reinterpret_cast<const u32x4*>((has_mask && st != kFull) ? p.mask + plane_off + off : p.q);
+      if constexpr (MK == kMaskBits) pmb[n] = mb_row[(int64_t)kb * kBitsPerBlock + r * 8 + c];
     }
   };
 
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   uint8_t st = kb < p.nkb ? sm.st[kb - cache_lo] : kSkip;
   if (kb < p.nkb) prefetch(kb, st);
   int rpar = 0;  // which of the two range buffers holds the current block's ranges
-  if constexpr (R) {
+  if constexpr (MK == kMaskRanges) {
     if (tid < kBlock) {
       sm.rs[0][tid] = prs;
       sm.re[0][tid] = pre;
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         u32x4 bw = (has_bias && inside) ? pb[n] : u32x4{0u, 0u, 0u, 0u};
         if (!full) {
           u32x4 mw;
-          if constexpr (R) {  // attends iff start <= i < end of the key's column
+          if constexpr (MK == kMaskRanges) {  // attends iff start <= i < end of the key's column
             const int4 s0 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8]);
             const int4 s1 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8 + 4]);
             const int4 e0 = *reinterpret_cast<const int4*>(&sm.re[rpar][c * 8]);
@@ -238,6 +243,10 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
               const bool a1 = rs8[2 * e + 1] <= i && i < re8[2 * e + 1];
               mw[e] = (a0 ? 0x3F80u : 0u) | (a1 ? 0x3F800000u : 0u);
             }
+          } else if constexpr (MK == kMaskBits) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              mw[e] = (((pmb[n] >> (2 * e)) & 1u) ? 0x3F80u : 0u) | (((pmb[n] >> (2 * e + 1)) & 1u) ? 0x3F800000u : 0u);
           } else {
             mw = has_mask ? pm[n] : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
           }
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         }
       }
     }
-    if constexpr (R) {  // the next block's ranges go to the other buffer, read after the next barrier
+    if constexpr (MK == kMaskRanges) {  // the next block's ranges go to the other buffer, read after the next barrier
       if (tid < kBlock) {
         sm.rs[rpar ^ 1][tid] = prs;
         sm.re[rpar ^ 1][tid] = pre;
@@ -379,9 +388,11 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 template <int D, int HC>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   if (p.rstart != nullptr)
-    hipLaunchKernelGGL((fwd_kernel<D, HC, true>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, HC, kMaskRanges>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
+  else if (p.mbits != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<D, HC, kMaskBits>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, HC, false>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, HC, kMaskDense>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -393,6 +404,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.mask = a.mask;
   p.rstart = a.rstart;
   p.rend = a.rend;
+  p.mbits = a.mbits;
   p.bias = a.bias;
   p.state = a.state;
   p.o = a.o_out;

@@ -175,6 +175,44 @@ int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bit-packed mask of the PARTIAL blocks (a variant of the unified skip design
+ * of the Flash-DMA README, key design: the classification pass reads the whole
+ * mask once anyway, so it can keep what the attention passes need of it, one
+ * bit per element of each PARTIAL block, and they read 1/16 of the bf16 mask's
+ * bytes).  The pages define no such format; the results equal the dense entry
+ * points' bit for bit.
+ *
+ *   mask_bits  device buffer of dma_mask_bits_size() bytes, 16-byte aligned,
+ *              owned by the caller.  Block (b, g, qb, kb) owns the 512 bytes
+ *              at ((b*hkv + g)*nqb + qb)*nkb + kb times 512 (nqb, nkb as in
+ *              block_state); row r of the block is the little-endian 64-bit
+ *              word at byte 8r of them, bit c = 1 iff mask[b,g,qb*64+r,kb*64+c]
+ *              attends (bf16 bits & 0x7FFF != 0; 0 past lq or lk; causality
+ *              not applied).  Only PARTIAL blocks are written; the bytes of
+ *              the other blocks are left as they were and never read.
+ *
+ * dma_mask_bits_size returns that size (0 for invalid sizes).
+ * dma_block_classify_bits writes block_state as dma_block_classify does and, in
+ * the same pass, the bits of every PARTIAL block; mask must not be NULL.
+ * dma_attn_fwd_bits / dma_attn_bwd_bits take mask_bits where the dense entry
+ * points take mask, with the block_state written together with those bits (the
+ * bits of any other PARTIAL block are undefined).  Other arguments, layouts,
+ * workspace and errors are those of dma_attn_fwd / dma_attn_bwd (NULL or
+ * misaligned mask_bits: DMA_ERR_INVALID_ARGUMENT).
+ */
+size_t dma_mask_bits_size(int64_t b, int64_t hkv, int64_t lq, int64_t lk);
+int dma_block_classify_bits(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int is_causal,
+                            uint8_t* block_state, uint8_t* mask_bits, void* stream);
+int dma_attn_fwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* mask_bits,
+                      const uint16_t* bias, const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq,
+                      int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* o, float* lse, void* stream);
+int dma_attn_bwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* mask_bits,
+                      const uint16_t* bias, const uint8_t* block_state, const uint16_t* o, const uint16_t* dout,
+                      const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                      float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Top-k mask construction (Flash-DMA README, usage example: keep the
  * keep_window_size largest bias values of every query row; everything else is
  * masked, and its bias is set to the smallest bf16 value).

@@ -37,6 +37,12 @@ def lib():
     L.dma_attn_fwd_ranges.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp]
     L.dma_attn_bwd_ranges.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp,
                                       vp, vp, vp, vp, sz, vp]
+    L.dma_mask_bits_size.restype = sz
+    L.dma_mask_bits_size.argtypes = [i64, i64, i64, i64]
+    L.dma_block_classify_bits.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp, vp]
+    L.dma_attn_fwd_bits.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp]
+    L.dma_attn_bwd_bits.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp,
+                                    vp, vp, vp, sz, vp]
     return L
 
 
@@ -50,7 +56,8 @@ def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("dma_block_classify", "dma_attn_fwd", "dma_attn_bwd", "dma_attn_bwd_workspace_size",
                  "dma_block_size", "dma_status_string", "dma_topk_mask", "dma_block_classify_ranges",
-                 "dma_attn_fwd_ranges", "dma_attn_bwd_ranges"):
+                 "dma_attn_fwd_ranges", "dma_attn_bwd_ranges", "dma_mask_bits_size", "dma_block_classify_bits",
+                 "dma_attn_fwd_bits", "dma_attn_bwd_bits"):
         assert name in syms
 
 
@@ -203,3 +210,33 @@ def test_ranges_reject(lib):
     assert g(*bargs[:3], None, *bargs[4:]) == INVALID
     assert g(*bargs[:15], 80, *bargs[16:]) == UNSUPPORTED
     assert g(*bargs[:16], 0.0, *bargs[17:]) == INVALID
+
+
+def test_mask_bits_size(lib):
+    # 512 bytes per 64 x 64 block, ragged edges rounded up; invalid sizes give 0
+    assert lib.dma_mask_bits_size(1, 1, 64, 64) == 512
+    assert lib.dma_mask_bits_size(2, 3, 130, 200) == 2 * 3 * 3 * 4 * 512
+    assert lib.dma_mask_bits_size(1, 2, 16384, 16384) == 2 * 256 * 256 * 512
+    assert lib.dma_mask_bits_size(0, 1, 64, 64) == 0
+    assert lib.dma_mask_bits_size(1, 1, 64, 0) == 0
+
+
+def test_bits_reject(lib):
+    c = lib.dma_block_classify_bits
+    assert c(None, 1, 1, 128, 128, 1, P, P, None) == INVALID  # the bits need the mask
+    assert c(P, 1, 1, 128, 128, 1, P, None, None) == INVALID
+    assert c(P, 1, 1, 128, 128, 1, P, P + 4, None) == INVALID
+    assert c(P, 1, 1, 128, 128, 1, None, P, None) == INVALID
+    assert c(P, 1, 1, 128, 100, 1, P, P, None) == INVALID
+    assert c(P, 1, 1, 128, 128, 2, P, P, None) == INVALID
+    assert c(P, 70000, 1, 128, 128, 1, P, P, None) == UNSUPPORTED
+    f = lib.dma_attn_fwd_bits
+    args = [P, P, P, P, P, P, 1, 128, 128, 4, 2, 128, 0.1, 1, P, P, None]
+    assert f(*args[:3], None, *args[4:]) == INVALID
+    assert f(*args[:3], P + 8, *args[4:]) == INVALID
+    assert f(*args[:11], 96, *args[12:]) == UNSUPPORTED
+    g = lib.dma_attn_bwd_bits
+    bargs = [P, P, P, P, P, P, P, P, P, 1, 128, 128, 4, 2, 128, 0.1, 1, P, P, P, P, P, 1 << 40, None]
+    assert g(*bargs[:3], None, *bargs[4:]) == INVALID
+    assert g(*bargs[:14], 80, *bargs[15:]) == UNSUPPORTED
+    assert g(*bargs[:15], 0.0, *bargs[16:]) == INVALID
