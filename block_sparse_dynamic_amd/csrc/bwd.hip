@@ -447,6 +447,18 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   const int goff0 = tile_off<D>(hi * 4 + trow, tcol);        // dV/dK tr reads, column step dt: ^ (dt << 5)
   constexpr int kG1Xor = D == 128 ? 16 : 32;                 // 8 rows further down: + 8 D, then ^ this
   const int swoff0 = swz32(l32, hi * 4) + wave * 32 * SR;    // dS^T writes, row group gi: ^ (gi << 3)
+  // the same offsets with every XOR applied, in elements of buffer 0: an item adds its buffer's
+  // base, so each read costs one add
+  int aoffs[D / 16], goffs[D / 32][2], swoffs[4];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) aoffs[s] = aoff0 ^ (s << 4);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    goffs[dt][0] = goff0 ^ (dt << 5);
+    goffs[dt][1] = ((goff0 ^ (dt << 5)) + 8 * D) ^ kG1Xor;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) swoffs[j] = swoff0 ^ (j << 3);
   int sq[2][2];                      // dS export, dS^T rows (ks%2)*16 + hi*8 + trow (+4), + (ks/2)*32
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -473,6 +485,13 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   dma_barrier();
 
   while (qb >= 0) {
+    // The loop-carried accumulators and K/V operands sit in accumulation registers at both ends
+    // of the item: pinned at the end only, the allocator parks some of them in vector registers
+    // during the item (64 moves per item) to give the S and dP tiles their place.
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(kreg[s]), "+a"(vreg[s]));
     const int B = buf;
     const int i0 = qb * kBlock + rh * kRows;
     const int rows_left = min(kRows, (int)p.lq - i0);
@@ -544,73 +563,98 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     }
     // Every operand read is issued before the first product (a scheduling barrier keeps
     // them there), so the products wait on LDS once instead of once per k-step.
-    const int qoff = aoff0 + B * Smem::kTile;  // this item's buffer of the Q and dO tiles
     bf16x8 opq[D / 16], opg[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      opq[s] = *reinterpret_cast<const bf16x8*>(&sm.q[0][qoff ^ (s << 4)]);
-      opg[s] = *reinterpret_cast<const bf16x8*>(&sm.g[0][qoff ^ (s << 4)]);
+      opq[s] = *reinterpret_cast<const bf16x8*>(&sm.q[B][aoffs[s]]);
+      opg[s] = *reinterpret_cast<const bf16x8*>(&sm.g[B][aoffs[s]]);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    f32x4 nl[4];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      sacc = mfma32(opq[s], kreg[s], sacc);
-      pacc = mfma32(opg[s], vreg[s], pacc);
-    }
+    for (int gi = 0; gi < 4; ++gi) nl[gi] = *reinterpret_cast<const f32x4*>(&sm.nl2[B][gi * 8 + hi * 4]);
     __builtin_amdgcn_sched_barrier(0);
-    // the transposing reads of the dV/dK operands do not depend on P or dS: issue them now,
-    // so that the softmax below covers their latency
-    const int gbuf = goff0 + B * Smem::kTile;
+    // The wave issues in order and is the only one on its SIMD, so the vector work of the item
+    // only overlaps the matrix products if it sits between them: S first; then the dP products
+    // with P = exp2(...) of the finished S between them; the dV products (they need P only)
+    // with dS = P (dP - D); the dK products with the dS^T tile writes.  Group barriers fix
+    // that interleave (one product, then up to seven vector instructions).
+    // ---- S + bias/scale = Q K^T + init: 32 queries x 32 keys ----------------------------------
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) sacc = mfma32(opq[s], kreg[s], sacc);
+    __builtin_amdgcn_sched_barrier(0);
+    // the transposing reads of the dV/dK operands do not depend on P or dS: issue them now
     i16x4 trg[2][D / 32][2], trq[2][D / 32][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int t0 = (gbuf ^ (dt << 5)) + ks * 16 * D, t1 = ((gbuf ^ (dt << 5)) + 8 * D) ^ kG1Xor;
-        trg[ks][dt][0] = lds_read_tr16(&sm.g[0][t0]);
-        trg[ks][dt][1] = lds_read_tr16(&sm.g[0][t1 + ks * 16 * D]);
-        trq[ks][dt][0] = lds_read_tr16(&sm.q[0][t0]);
-        trq[ks][dt][1] = lds_read_tr16(&sm.q[0][t1 + ks * 16 * D]);
+        trg[ks][dt][0] = lds_read_tr16(&sm.g[B][goffs[dt][0] + ks * 16 * D]);
+        trg[ks][dt][1] = lds_read_tr16(&sm.g[B][goffs[dt][1] + ks * 16 * D]);
+        trq[ks][dt][0] = lds_read_tr16(&sm.q[B][goffs[dt][0] + ks * 16 * D]);
+        trq[ks][dt][1] = lds_read_tr16(&sm.q[B][goffs[dt][1] + ks * 16 * D]);
       }
     __builtin_amdgcn_sched_barrier(0);
-    // ---- P = exp2(scale2 * S' - lse log2 e), dS = P (dP - D) -----------------------------------
+    // ---- dP - D = dO V^T - D, and between its products P = exp2(scale2 * S' - lse log2 e) ----
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const f32x4 nl = *reinterpret_cast<const f32x4*>(&sm.nl2[B][gi * 8 + hi * 4]);
+    for (int s = 0; s < D / 16; ++s) pacc = mfma32(opg[s], vreg[s], pacc);
+    f32x16 pv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = gi * 4 + e;
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale2, nl[e]));
-        const float ds = pv * pacc[i];
-        sacc[i] = pv;
-        pacc[i] = ds;
-        dbacc[i] += ds;
-      }
-    }
-    // ---- dV += P^T dO, dK += dS^T Q: two k-steps of 16 queries ----------------------------
-    const int swb = swoff0 + B * Smem::kSTile;
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pv[gi * 4 + e] = __builtin_amdgcn_exp2f(fmaf(sacc[gi * 4 + e], scale2, nl[gi][e]));
+    bf16x8 ap[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u32x4 pw, sw2;
+      u32x4 pw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pw[e] = pack_bf16x2(sacc[ks * 8 + 2 * e], sacc[ks * 8 + 2 * e + 1]);
-        sw2[e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
-      }
-      const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw2);
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(pv[ks * 8 + 2 * e], pv[ks * 8 + 2 * e + 1]);
+      ap[ks] = __builtin_bit_cast(bf16x8, pw);
+    }
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dv[dt] = mfma32(ap, join_bf16x8(trg[ks][dt][0], trg[ks][dt][1]), dv[dt]);
+    for (int s = 0; s < D / 16; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // then seven vector instructions
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- dV += P^T dO, and between its products dS = P (dP - D) ------------------------------
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        dv[dt] = mfma32(ap[ks], join_bf16x8(trg[ks][dt][0], trg[ks][dt][1]), dv[dt]);
+    u32x4 sw[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float ds = pv[i] * pacc[i];
+      pacc[i] = ds;
+      dbacc[i] += ds;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sw[ks][e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- dK += dS^T Q, and between its products the dS^T tile writes ----------------------------
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 as = __builtin_bit_cast(bf16x8, sw[ks]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
         dk[dt] = mfma32(as, join_bf16x8(trq[ks][dt][0], trq[ks][dt][1]), dk[dt]);
-      }
       // the same bf16 pairs (rows gi*4 + 2e', + 1 of the S layout) form the dS^T rows below
       u32x2 lo2, hi2;
-      lo2[0] = sw2[0];
-      lo2[1] = sw2[1];
-      hi2[0] = sw2[2];
-      hi2[1] = sw2[3];
-      *reinterpret_cast<u32x2*>(&sm.s[0][swb ^ ((2 * ks) << 3)]) = lo2;
-      *reinterpret_cast<u32x2*>(&sm.s[0][swb ^ ((2 * ks + 1) << 3)]) = hi2;
+      lo2[0] = sw[ks][0];
+      lo2[1] = sw[ks][1];
+      hi2[0] = sw[ks][2];
+      hi2[1] = sw[ks][3];
+      *reinterpret_cast<u32x2*>(&sm.s[B][swoffs[2 * ks]]) = lo2;
+      *reinterpret_cast<u32x2*>(&sm.s[B][swoffs[2 * ks + 1]]) = hi2;
     }
     dma_barrier();  // dS^T complete; the next item's buffers are loaded; this item's are free
 

@@ -14,6 +14,7 @@ constexpr int kMaskDense = 0, kMaskRanges = 1, kMaskBits = 2;
 constexpr int kBitsPerBlock = kBlock * kBlock / 8;  // bytes of one block's bits: row r at bytes 8r .. 8r+7
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -44,8 +45,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
 }
+// Two fp32 values -> bf16 pair, as one v_cvt_pk_bf16_f32 (the same rounding as f32_to_bf16);
+// converting the halves one by one costs a shift and a merge on top of two conversions.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2 h = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, h);
 }
 // Two fp32 values -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
