@@ -100,6 +100,8 @@ int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !lse || !aligned16(o) || !aligned16(lse)) return DMA_ERR_INVALID_ARGUMENT;
+  // the scores are carried as q.k + bias / |scale|: scale must be finite and nonzero
+  if (!(scale != 0.f) || !std::isfinite(scale)) return DMA_ERR_INVALID_ARGUMENT;
   dma::AttnArgs a = {};
   a.q = q;
   a.k = k;

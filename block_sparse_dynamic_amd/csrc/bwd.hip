@@ -47,6 +47,8 @@
 // chunks as B, so a result lane holds one query row.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace dma {
@@ -480,10 +482,13 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   lds_barrier();     // buffers zeroed
   int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
   int rh = 0, hh = 0;
-  int buf = 0;
   if (qb >= 0) issue(0, qb, 0, 0, cs0, cs1);
+  // first dS tile pair of the current query block, kept as read from LDS (uniform): the next
+  // block's value is read when the walk reaches it and taken into scalars one item later
+  int64_t pbv = qb >= 0 ? sm.pb[qb - cache_lo] : 0;
   dma_barrier();
 
+  int buf = 0;
   while (qb >= 0) {
     // The loop-carried accumulators and K/V operands sit in accumulation registers at both ends
     // of the item: pinned at the end only, the allocator parks some of them in vector registers
@@ -496,7 +501,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     const int i0 = qb * kBlock + rh * kRows;
     const int rows_left = min(kRows, (int)p.lq - i0);
     const uint8_t my_st = half ? cs1 : cs0;
-    const int64_t pbc = sm.pb[qb - cache_lo];  // read before the walk below may move the cache
+    const int64_t pbc = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)pbv)) |
+                                  ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pbv >> 32)) << 32));
 
     // ---- start loading the next item ------------------------------------------------
     int nqb = qb, nrh = rh, nhh = hh + 1;
@@ -507,6 +513,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       if (nrh == 2 || i0 + kRows >= p.lq) {
         nrh = 0;
         nqb = next_qb(qb - 1, ns0, ns1);
+        if (nqb >= 0) pbv = sm.pb[nqb - cache_lo];  // the walk leaves nqb in the cache
       }
     }
     if (nqb >= 0) issue(B ^ 1, nqb, nrh, nhh, ns0, ns1);

@@ -14,19 +14,24 @@
 //
 // Per key block (64 keys):
 //   1. the workgroup copies K and V (row-major, [key][d]) and the *effective*
-//      bias into LDS.  The effective bias is bias where the position is valid
-//      and -inf elsewhere: mask, causality and the ragged matrix edge are
-//      folded in once here (PARTIAL blocks only), so the score epilogue is one
-//      fma per element for every head.  FULL blocks copy the bias alone.
-//   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
-//      wave's Q rows held in registers for the whole kernel.  The result's
-//      lane l holds query l%32 and 16 keys of each 32-key half, so a row's
-//      64 scores live in lanes l and l^32.
+//      bias into LDS.  The effective bias is bias / |scale| in fp32 where the
+//      position is valid and -inf elsewhere: mask, causality and the ragged
+//      matrix edge are folded in once here for all HC heads.  The tiles of
+//      the next non-SKIP block are loaded into registers meanwhile, by buffer
+//      loads whose per-thread offsets are fixed for the kernel (the block's
+//      corner and its valid extent go into the buffer resource, so keys past
+//      lk and rows past lq read as zeros).
+//   2. y = S^T / |scale| + bias / |scale| = K Q^T + the staged tile, on
+//      v_mfma_f32_32x32x16_bf16: the accumulators start from the effective
+//      bias, A = K rows from LDS, B = the wave's Q rows held in registers for
+//      the whole kernel (negated for a negative scale, which is exact).  The
+//      result's lane l holds query l%32 and 16 keys of each 32-key half, so a
+//      row's 64 scores live in lanes l and l^32.  The score is x = |scale| y.
 //   3. online softmax in fp32: row max over the lane pair (v_permlane32_swap),
-//      exp2 with log2(e) folded in; the reference maximum (and with it the
-//      running output) moves only when a row maximum exceeds it by more than
-//      2^8 in weight, so weights stay in [0, 256] and the rescale runs rarely
-//      (the wave skips it when no row needs it).
+//      exp2 with |scale| log2(e) folded into one fma per element; the reference
+//      maximum (and with it the running output) moves only when a row maximum
+//      exceeds it by more than 2^8 in weight, so weights stay in [0, 256] and
+//      the rescale runs rarely (the wave skips it when no row needs it).
 //   4. O^T += V^T P^T on v_mfma_f32_32x32x16_f16: P^T goes from the accumulator
 //      registers straight into the B operand as fp16 (the key order inside a
 //      k-step only has to agree between A and B); V^T comes out of the
@@ -64,10 +69,10 @@ constexpr uint16_t kBf16NegInf = 0xFF80u;
 template <int D>
 struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay single 16-byte LDS accesses
   static constexpr int kRow = tile_row<D>();  // row (elements) of the K and V tiles (tile_off layout)
-  static constexpr int kBRow = kBlock + 8;
+  static constexpr int kBRow = kBlock + 4;  // fp32 row: 272 bytes, so 8 consecutive rows hit distinct banks
   uint16_t k[kBlock * kRow];
   uint16_t v[kBlock * kRow];
-  uint16_t b[kBlock * kBRow];  // effective bias, bf16 bits
+  float b[kBlock * kBRow];  // effective bias / |scale| (-inf where invalid): the S accumulators' start
   uint8_t st[kStateChunkF];    // block states of this query block's row, a chunk at a time
   int32_t rs[2][kBlock];       // column ranges of the current and the next key block (range input)
   int32_t re[2][kBlock];
@@ -104,6 +109,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     for (int s = 0; s < D / 16; ++s) {
       u32x4 w4 = {0u, 0u, 0u, 0u};
       if (row < p.lq) w4 = *reinterpret_cast<const u32x4*>(qp + s * 16);
+      if (p.scale < 0.f) w4 ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};  // exact
       qreg[s] = __builtin_bit_cast(bf16x8, w4);
     }
   }
@@ -121,6 +127,8 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   const uint16_t* vbase = p.v + (bidx * p.lk * p.hkv + g) * D;
   const int64_t plane_off = (int64_t)plane * p.lq * p.lk;
   const bool has_bias = p.bias != nullptr, has_mask = p.mask != nullptr;
+  // scores are carried as y = x / |scale| (Q negated above for a negative scale)
+  const float as = fabsf(p.scale), inv_as = 1.f / as, as_l2e = as * kLog2e;
 
   // Block states of this row are cached in LDS a chunk at a time, so skipping a SKIP block
   // costs an LDS read instead of a dependent global load.
@@ -150,32 +158,53 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   const uint8_t* mb_row = MK == kMaskBits ? p.mbits + ((int64_t)plane * p.nqb + qb) * p.nkb * kBitsPerBlock : nullptr;
   const int32_t* rs_plane = MK == kMaskRanges ? p.rstart + (int64_t)plane * p.lk : nullptr;
   const int32_t* re_plane = MK == kMaskRanges ? p.rend + (int64_t)plane * p.lk : nullptr;
+  // Per-thread byte offsets of the tile loads inside a block (the same for every block); the
+  // block's corner and the bytes it may read go into buffer resources, whose range checks
+  // return zeros for keys past lk and rows past lq.
+  uint32_t kvo[KN], bo[BN];
+#pragma unroll
+  for (int n = 0; n < KN; ++n) {
+    const int task = tid + n * NT;
+    kvo[n] = (uint32_t)((task / (D / 8)) * p.hkv * D + (task % (D / 8)) * 8) * 2u;
+  }
+#pragma unroll
+  for (int n = 0; n < BN; ++n) {
+    const int task = tid + n * NT;
+    bo[n] = (uint32_t)(task >> 3) * (uint32_t)(p.lk * 2) + (uint32_t)(task & 7) * 16u;
+  }
+  const int q_rows = (int)min((int64_t)kBlock, p.lq - (int64_t)qb * kBlock);
   auto prefetch = [&](int kb, uint8_t st) {
     if constexpr (MK == kMaskRanges) {  // first, so that waiting for them never waits for the tiles below
       const int64_t j = min((int64_t)kb * kBlock + (tid & 63), p.lk - 1);
       prs = rs_plane[j];
       pre = re_plane[j];
     }
+    const int k_rows = (int)min((int64_t)kBlock, p.lk - (int64_t)kb * kBlock);  // >= 1
+    const int64_t kv0 = (int64_t)kb * kBlock * p.hkv * D;
+    const uint32_t kvbytes = (uint32_t)k_rows * (uint32_t)(p.hkv * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(const_cast<uint16_t*>(kbase + kv0), kvbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(const_cast<uint16_t*>(vbase + kv0), kvbytes);
 #pragma unroll
     for (int n = 0; n < KN; ++n) {
-      const int task = tid + n * NT;
-      const int r = task / (D / 8), c = task % (D / 8);
-      const int64_t key = (int64_t)kb * kBlock + r;
-      const int64_t off = (key < p.lk ? key : (int64_t)kb * kBlock) * p.hkv * D + c * 8;  // key kb*64 < lk
-      pk[n] = *reinterpret_cast<const u32x4*>(kbase + off);
-      pv[n] = *reinterpret_cast<const u32x4*>(vbase + off);
+      pk[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)kvo[n], 0, 0));
+      pv[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)kvo[n], 0, 0));
     }
-    const int64_t corner = (int64_t)qb * kBlock * p.lk + (int64_t)kb * kBlock;  // (qb*64, kb*64): in bounds
+    // rows past lq and, in the last row, keys past lk fall outside the range (zeros); keys past
+    // lk in earlier rows read the next row's values, which the staging replaces
+    const int64_t corner = plane_off + (int64_t)qb * kBlock * p.lk + (int64_t)kb * kBlock;
+    const uint32_t bbytes = (uint32_t)(q_rows - 1) * (uint32_t)(p.lk * 2) + (uint32_t)k_rows * 2u;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(const_cast<uint16_t*>(has_bias ? p.bias + corner : p.q), has_bias ? bbytes : 0u);
+    const __amdgpu_buffer_rsrc_t rm =
+        make_rsrc(const_cast<uint16_t*>(has_mask ? p.mask + corner : p.q), (has_mask && st != kFull) ? bbytes : 0u);
 #pragma unroll
     for (int n = 0; n < BN; ++n) {
-      const int task = tid + n * NT;
-      const int r = task >> 3, c = task & 7;
-      const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
-      const int64_t off = (i < p.lq && j0 < p.lk) ? i * p.lk + j0 : corner;
-      pb[n] = *reinterpret_cast<const u32x4*>(has_bias ? p.bias + plane_off + off : p.q);
+      pb[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)bo[n], 0, 0));
       if constexpr (MK == kMaskDense)
-        pm[n] = *reinterpret_cast<const u32x4*>((has_mask && st != kFull) ? p.mask + plane_off + off : p.q);
-      if constexpr (MK == kMaskBits) pmb[n] = mb_row[(int64_t)kb * kBitsPerBlock + r * 8 + c];
+        pm[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, (int)bo[n], 0, 0));
+      if constexpr (MK == kMaskBits) {
+        const int task = tid + n * NT;
+        pmb[n] = mb_row[(int64_t)kb * kBitsPerBlock + (task >> 3) * 8 + (task & 7)];
+      }
     }
   };
 
@@ -212,24 +241,26 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     for (int n = 0; n < KN; ++n) {
       const int task = tid + n * NT;
       const int r = task / (D / 8), c = task % (D / 8);
-      const bool in = (int64_t)kb * kBlock + r < p.lk;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = in ? pk[n] : z;
+      // rows past lk were loaded as zeros
+      *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = pk[n];
       u32x4 vh;  // V in fp16 for the P V product
 #pragma unroll
       for (int e = 0; e < 4; ++e) vh[e] = bf16x2_to_f16x2(pv[n][e]);
-      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = in ? vh : z;
+      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = vh;
     }
-    if (has_bias || !full) {
+    {
 #pragma unroll
       for (int n = 0; n < BN; ++n) {
         const int task = tid + n * NT;
         const int r = task >> 3, c = task & 7;
         const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
-        const bool inside = i < p.lq && j0 < p.lk;
-        u32x4 bw = (has_bias && inside) ? pb[n] : u32x4{0u, 0u, 0u, 0u};
+        // columns j0 + e of this chunk are inside the matrix and causal for e <= emax
+        int64_t lim = p.lk - 1 - j0;
+        if (p.causal) lim = min(lim, i + shift - j0);
+        const int emax = (i < p.lq) ? (int)max((int64_t)-1, min(lim, (int64_t)7)) : -1;
+        const u32x4 bw = pb[n];  // zeros without a bias
+        u32x4 mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
         if (!full) {
-          u32x4 mw;
           if constexpr (MK == kMaskRanges) {  // attends iff start <= i < end of the key's column
             const int4 s0 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8]);
             const int4 s1 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8 + 4]);
@@ -248,19 +279,26 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
             for (int e = 0; e < 4; ++e)
               mw[e] = (((pmb[n] >> (2 * e)) & 1u) ? 0x3F80u : 0u) | (((pmb[n] >> (2 * e + 1)) & 1u) ? 0x3F800000u : 0u);
           } else {
-            mw = has_mask ? pm[n] : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t j = j0 + 2 * e;
-            const bool v0 = inside && attends_lo(mw[e]) && (!p.causal || j <= i + shift);
-            const bool v1 = inside && attends_hi(mw[e]) && (!p.causal || j + 1 <= i + shift);
-            const uint32_t lo = v0 ? (bw[e] & 0xFFFFu) : kBf16NegInf;
-            const uint32_t hi16 = v1 ? (bw[e] >> 16) : kBf16NegInf;
-            bw[e] = lo | (hi16 << 16);
+            if (has_mask) mw = pm[n];
           }
         }
-        *reinterpret_cast<u32x4*>(&sm.b[r * BR + c * 8]) = bw;
+        f32x4 y0, y1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool v0 = 2 * e <= emax && attends_lo(mw[e]);
+          const bool v1 = 2 * e + 1 <= emax && attends_hi(mw[e]);
+          const float lo = v0 ? bf16_lo(bw[e]) * inv_as : -INFINITY;
+          const float hi16 = v1 ? bf16_hi(bw[e]) * inv_as : -INFINITY;
+          if (e < 2) {
+            y0[2 * e] = lo;
+            y0[2 * e + 1] = hi16;
+          } else {
+            y1[2 * e - 4] = lo;
+            y1[2 * e - 3] = hi16;
+          }
+        }
+        *reinterpret_cast<f32x4*>(&sm.b[r * BR + c * 8]) = y0;
+        *reinterpret_cast<f32x4*>(&sm.b[r * BR + c * 8 + 4]) = y1;
       }
     }
     lds_barrier();
@@ -269,8 +307,16 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     const uint8_t st_next = kb_next < p.nkb ? sm.st[kb_next - cache_lo] : kSkip;
     if (kb_next < p.nkb) prefetch(kb_next, st_next);
 
-    // ---- S^T = K Q^T --------------------------------------------------------
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // ---- y = S^T / |scale| + effective bias / |scale| = K Q^T + the staged tile ----------------
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.b[rloc * BR + kt * 32 + gi * 8 + hi * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[kt][gi * 4 + e] = y[e];
+      }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
@@ -279,35 +325,13 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
       }
     }
-    // ---- scores: x = scale * s + effective bias ---------------------------
+    // ---- row maximum of the scores x = |scale| y ------------------------------------
     float mx = -INFINITY;
-    if (has_bias || !full) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const u32x2 bw = *reinterpret_cast<const u32x2*>(&sm.b[rloc * BR + kt * 32 + gi * 8 + hi * 4]);
-          const float bb[4] = {bf16_lo(bw[0]), bf16_hi(bw[0]), bf16_lo(bw[1]), bf16_hi(bw[1])};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = fmaf(sacc[kt][gi * 4 + e], p.scale, bb[e]);
-            sacc[kt][gi * 4 + e] = x;
-            mx = fmaxf(mx, x);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = sacc[kt][i] * p.scale;
-          sacc[kt][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-    }
-    mx = max_with_half_swap(mx);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+    mx = max_with_half_swap(mx) * as;
     // ---- online softmax ----------------------------------------------------------
     // The reference maximum moves only when a row's maximum exceeds it by more than
     // kRescaleMargin (8 in log2 units): below that the weights exp(x - m_ref) stay under 256,
@@ -329,7 +353,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], kLog2e, -mb));
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], as_l2e, -mb));
         sacc[kt][i] = pv;
         rs += pv;
       }

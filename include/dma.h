@@ -101,7 +101,9 @@ int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq,
  *               including the row maximum, +inf for rows with no valid key
  * Supported: d in {64, 128}; hq % hkv == 0 with hq / hkv in {1, 2, 4, 8, 16}.
  * Errors: DMA_ERR_INVALID_ARGUMENT (NULL q/k/v/o/lse/block_state, sizes < 1,
- * misalignment, lk % 8 != 0 with mask or bias), DMA_ERR_UNSUPPORTED (d, group).
+ * misalignment, lk % 8 != 0 with mask or bias, a scale that is zero or not
+ * finite: the kernel carries scores as q.k + bias / |scale|),
+ * DMA_ERR_UNSUPPORTED (d, group).
  */
 int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
                  const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,

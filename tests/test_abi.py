@@ -113,6 +113,12 @@ def test_fwd_ragged_lk_allowed_without_mask_and_bias(lib):
     assert fwd(lib, lk=100, mask=None, bias=None, d=96) == UNSUPPORTED
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.0, float("inf"), float("-inf"), float("nan")])
+def test_fwd_rejects_scale(lib, scale):
+    # the forward carries scores as q.k + bias / |scale|
+    assert fwd(lib, scale=scale) == INVALID
+
+
 @pytest.mark.parametrize("kw,want", [
     (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dk=None), INVALID), (dict(dv=None), INVALID),
     (dict(ws=None), INVALID), (dict(lse=P + 4), INVALID), (dict(db=P + 2), INVALID),
