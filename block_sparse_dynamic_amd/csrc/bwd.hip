@@ -527,29 +527,49 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       const bool partial = my_st == kPartial;
       // causal: row r of the item is valid for this key when r >= key - (lk - lq) - i0
       const int64_t cfirst = p.causal ? key_abs - shift - i0 : (int64_t)INT32_MIN;
-      const int first_r = (int)max((int64_t)INT32_MIN, min(cfirst, (int64_t)kRows));
+      const int first_r = (int)max((int64_t)0, min(cfirst, (int64_t)kRows));
+      // rows [lo, up) are in range (and causal on a PARTIAL block) for this lane's key, as a
+      // mask shifted so that bit gi*8 + e stands for row gi*8 + hi*4 + e
+      const int lo = partial ? first_r : 0, up = key_ok ? rows_left : 0;
+      const uint32_t below_up = up >= 32 ? 0xFFFFFFFFu : (1u << up) - 1u;
+      const uint32_t below_lo = lo >= 32 ? 0xFFFFFFFFu : (1u << lo) - 1u;
+      const uint32_t rv = (below_up & ~below_lo) >> (hi * 4);
       // bit input: row r's bits of this lane's key are bit l32 of dword r*2 + (wave & 1) of its block
       const uint32_t* mrow = reinterpret_cast<const uint32_t*>(&sm.m[B][0]) + half * 64 + (wave & 1);
+      // the mask is read on PARTIAL blocks only (uniform across the wave)
+      auto init = [&](auto use_mask) {
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        // 8 rows down the row term of the swizzle flips chunk bit 1 (element bit 4)
-        const int bo = (boff0 + gi * 8 * 128) ^ ((gi & 1) << 4);
-        const i16x4 xb = lds_read_tr16(&sm.b[B][bo]);
-        i16x4 xm = {0, 0, 0, 0};
-        if constexpr (MK == kMaskDense) xm = lds_read_tr16(&sm.m[B][bo]);
-        f32x4 iv;
+        for (int gi = 0; gi < 4; ++gi) {
+          // 8 rows down the row term of the swizzle flips chunk bit 1 (element bit 4)
+          const int bo = (boff0 + gi * 8 * 128) ^ ((gi & 1) << 4);
+          const i16x4 xb = lds_read_tr16(&sm.b[B][bo]);
+          i16x4 xm = {0, 0, 0, 0};
+          if constexpr (decltype(use_mask)::value && MK == kMaskDense) xm = lds_read_tr16(&sm.m[B][bo]);
+          f32x4 iv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = gi * 8 + hi * 4 + e;
-          bool attends = !has_mask || (xm[e] & 0x7FFF) != 0;
-          if constexpr (MK == kMaskRanges) attends = krs <= i0 + r && i0 + r < kre;
-          if constexpr (MK == kMaskBits) attends = ((mrow[r * 2] >> l32) & 1u) != 0;
-          const bool pv = attends && r >= first_r;
-          const bool v = key_ok && r < rows_left && (!partial || pv);
-          iv[e] = v ? __uint_as_float((uint32_t)(uint16_t)xb[e] << 16) * inv_scale : neg_inf_s;
+          for (int e = 0; e < 4; ++e) {
+            const int idx = gi * 8 + e;
+            // all ones where the row is valid, else zero (a sign-extended one-bit field)
+            const uint32_t rm = (uint32_t)((int32_t)(rv << (31 - idx)) >> 31);
+            bool v;
+            if constexpr (!decltype(use_mask)::value) {
+              v = rm != 0u;
+            } else if constexpr (MK == kMaskDense) {
+              v = ((uint32_t)(uint16_t)xm[e] & 0x7FFFu & rm) != 0u;
+            } else if constexpr (MK == kMaskRanges) {
+              const int r = gi * 8 + hi * 4 + e;
+              v = rm != 0u && krs <= i0 + r && i0 + r < kre;
+            } else {
+              const int r = gi * 8 + hi * 4 + e;
+              v = rm != 0u && ((mrow[r * 2] >> l32) & 1u) != 0;
+            }
+            iv[e] = v ? __uint_as_float((uint32_t)(uint16_t)xb[e] << 16) * inv_scale : neg_inf_s;
+          }
+          sm.beff[wave][gi][lane] = iv;
         }
-        sm.beff[wave][gi][lane] = iv;
-      }
+      };
+      if (partial && (MK != kMaskDense || has_mask)) init(std::true_type{});
+      else init(std::false_type{});
       dbacc = f32x16{};
     }
 
