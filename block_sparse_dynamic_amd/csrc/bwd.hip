@@ -16,17 +16,18 @@
 //                     classification blocks); four wavefronts own 32 keys each.
 //                     Work items are (query block, 32-row half, head), heads
 //                     innermost.
-//                     K and V of the keys sit in LDS / registers for the whole kernel
+//                     K and V of the keys sit in registers for the whole kernel
 //                     and dK/dV accumulate in registers over every non-SKIP query
 //                     block and every head of the group, so they are written
-//                     once, without atomics.  Per query block the effective bias
-//                     (bias where valid, -inf elsewhere) is staged once and
-//                     serves all G heads; dBias of the block is summed over the
-//                     heads in registers and stored once.  SKIP blocks get zeros
-//                     and no loads.  The Q/dO tiles (and the bias/mask of a new
-//                     query block) of the next item are loaded into registers
-//                     while the current item computes.  Each item's dS (bf16) goes
-//                     to the workspace in the order the dQ kernel consumes it.
+//                     once, without atomics.  Per query block and 32-row half the
+//                     initial S values (bias / scale where valid, -inf elsewhere)
+//                     are formed once and serve all G heads; dBias of the rows is
+//                     summed over the heads in registers and stored once.  SKIP
+//                     blocks get zeros and no loads.  The Q/dO tiles (and the
+//                     bias/mask rows of a new query block) of the next item are
+//                     loaded straight into LDS while the current item computes.
+//                     Each item's dS (bf16) goes to the workspace in the order the
+//                     dQ kernel consumes it.
 //   dq_kernel         dQ = scale dS K: one workgroup per (batch, g, 64-row query block,
 //                     heads), summing over the live key pairs in registers and
 //                     writing bf16 dQ once.
