@@ -2,7 +2,8 @@
 
 Cases span several 64x64 tiles with ragged tails, all three block classes, NULL
 mask and bias, lq != lk (bottom-right causal alignment, rows with no valid key),
-group sizes 1..16, head dims 64 and 128, and NaN stored in masked bias entries.
+group sizes 1..16, head dims 64 and 128, NaN stored in masked bias entries, and a
+negative and a large scale.
 """
 import numpy as np
 import pytest
@@ -30,6 +31,9 @@ SMALL = [
     Case("doc_small", 21, 1, 1000, 1000, 4, 1, 128, True, "doc", doc_min=64, doc_max=300, bias_std=0.5,
          fill="lowest"),
     Case("all_ones_mask", 22, 1, 192, 192, 4, 1, 128, False, "ones"),
+    # the forward carries scores as q.k + bias/|scale| and negates Q for a negative scale
+    Case("negative_scale", 23, 1, 200, 200, 4, 2, 128, True, "blocks", scale=-0.09),
+    Case("large_scale_d64", 24, 1, 192, 192, 4, 2, 64, True, "topk", 64, scale=0.5),
 ]
 
 
