@@ -2,7 +2,11 @@
 
 One step = one pass of the whole path over one batch of synthetic input already
 resident in HBM: block classification, forward (O, LSE) and backward (dQ, dK, dV,
-dBias), each through the C ABI on the current stream.
+dBias), through the C ABI on the current stream.  By default the classification runs
+fused into the forward (dma_attn_fwd_classify: each live block's mask tile is read once,
+reduced to its class and applied); --separate-classify times dma_block_classify +
+dma_attn_fwd instead.  The other path is timed in the same run (``classify_other``;
+left out with --no-next).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config headline]
 
@@ -39,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-classify", action="store_true",
+                    help="time dma_block_classify + dma_attn_fwd instead of the fused dma_attn_fwd_classify")
     ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements (top-k construction)")
     ap.add_argument("--cpu-blocks", type=int, default=16, help="query-row blocks the oracle times")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -221,6 +227,20 @@ def time_ranges(args, dma, synth, np):
     return out
 
 
+def time_classify_other(c, dma, np, torch, classify_forward, fused, t_bwd, reps=5):
+    """Classification + forward by the path the step does not use (run with `not fused`)."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    classify_forward(fused)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        classify_forward(fused, ev[r])
+    torch.cuda.synchronize()
+    po = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev]).mean(axis=0)
+    return {"path": "separate dma_block_classify + dma_attn_fwd" if fused else "fused dma_attn_fwd_classify",
+            "classify_ms": round(float(po[0]), 4), "fwd_ms": round(float(po[1]), 4),
+            "classify_fwd_ms": round(float(po.sum()), 4), "step_ms_with_it": round(float(po.sum()) + t_bwd, 4)}
+
+
 def time_bits(c, dma, np, q, k, v, do, mask, bias, o, lse, dq, dk, dv, dbias, ws, stream, dense_ms):
     import torch
 
@@ -287,15 +307,24 @@ def main():
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
-    def step(timed=None):
+    fused = not args.separate_classify
+
+    def classify_forward(separate, timed=None):
         if timed is not None:
             timed[0].record(stream)
-        dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, state, stream)
+        if separate:
+            dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, state, stream)
         if timed is not None:
             timed[1].record(stream)
-        dma.dma_attn_fwd(q, k, v, mask, bias, state, c.scale_f32, c.causal, o, lse, stream)
+        if separate:
+            dma.dma_attn_fwd(q, k, v, mask, bias, state, c.scale_f32, c.causal, o, lse, stream)
+        else:
+            dma.dma_attn_fwd_classify(q, k, v, mask, bias, c.scale_f32, c.causal, state, o, lse, stream)
         if timed is not None:
             timed[2].record(stream)
+
+    def step(timed=None):
+        classify_forward(not fused, timed)
         dma.dma_attn_bwd(q, k, v, mask, bias, state, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws,
                          stream)
         if timed is not None:
@@ -324,6 +353,13 @@ def main():
         per[s] = [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
     t_cls, t_fwd, t_bwd = per.mean(axis=0)  # ms
     ms_step = wall / args.steps * 1e3
+
+    # the other classification path (separate pass or fused), outside the step, same inputs
+    # (left out of counter and trace runs, --no-next, which must hold the step's kernels only)
+    classify_other = None
+    if not args.no_next and args.calibrate_copy_mib == 0:
+        classify_other = time_classify_other(c, dma, np, torch, classify_forward, fused, t_bwd)
+
 
     # Next-row measurement, outside the step: the top-k mask construction (dma_topk_mask) on
     # a fresh N(0,1) bf16 bias of the workload's shape, k = the workload's top-k.
@@ -373,7 +409,9 @@ def main():
     live = (kb * 64 <= np.minimum(qb * 64 + 63, c.lq - 1) + (c.lk - c.lq)) if c.causal else np.ones((nqb, nkb), bool)
     n_live = int(live.sum()) * c.b * c.hkv
     has_mask = mask is not None
-    b_cls = 2.0 * 64 * 64 * n_live if has_mask else 0.0
+    # a separate classification reads the mask of every causally live block once more; fused,
+    # the forward's own mask reads classify
+    b_cls = 2.0 * 64 * 64 * n_live if (has_mask and not fused) else 0.0
     b_fwd = 2.0 * 64 * 64 * (2 * n_p + n_f)
     b_bwd = b_fwd + 2.0 * c.b * c.hkv * c.lq * c.lk
     tflops = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
@@ -381,7 +419,8 @@ def main():
 
     # dominant launch: the one with the largest share of the step
     phases = {"bwd": (t_bwd, f_bwd, "dma_attn_bwd (bwd_pre + kt + pair_base + bwd_main + dq)"),
-              "fwd": (t_fwd, f_fwd, "dma_attn_fwd (fwd_kernel)")}
+              "fwd": (t_fwd, f_fwd, "dma_attn_fwd_classify (fwd_kernel, classification fused)" if fused else
+                      "dma_attn_fwd (fwd_kernel)")}
     dom = max(phases, key=lambda k: phases[k][0])
     t_dom, f_dom, dom_name = phases[dom]
     achieved = f_dom / (t_dom * 1e-3) / 1e12
@@ -414,13 +453,15 @@ def main():
                    "b": c.b, "seq_len": c.lq, "hq": c.hq, "hkv": c.hkv, "d": c.d,
                    "blocks_nonskip": n_ns, "blocks_partial": n_p, "blocks_full": n_f, "blocks_skip": n_skip},
         "hbm_gbs_mandatory": round(gbs, 1),
+        "classify_fused": fused,
         "phases_ms": {"classify": round(t_cls, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
         "phases_tflops": {"fwd": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
                           "bwd": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2)},
-        "phases_gbs_mandatory": {"classify": round(b_cls / (t_cls * 1e-3) / 1e9, 1),
+        "phases_gbs_mandatory": {"classify": round(b_cls / (t_cls * 1e-3) / 1e9, 1) if b_cls > 0 else None,
                                  "fwd": round(b_fwd / (t_fwd * 1e-3) / 1e9, 1),
                                  "bwd": round(b_bwd / (t_bwd * 1e-3) / 1e9, 1)},
         "roofline": roofline,
+        "classify_other": classify_other,
         "next_rows": next_rows,
     }
     if not args.no_cpu_baseline:

@@ -43,6 +43,9 @@ _lib.dma_block_classify.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp]
 _lib.dma_attn_fwd.restype = _i32
 _lib.dma_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _i32, _vp, _vp,
                               _vp]
+_lib.dma_attn_fwd_classify.restype = _i32
+_lib.dma_attn_fwd_classify.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _i32, _vp,
+                                       _vp, _vp, _vp]
 _lib.dma_attn_bwd_workspace_size.restype = _sz
 _lib.dma_attn_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32]
 _lib.dma_attn_bwd.restype = _i32
@@ -139,6 +142,19 @@ def dma_attn_fwd(q, k, v, mask, bias, block_state, scale: float, is_causal: bool
                            int(bool(is_causal)), _ptr(o, "o", torch.bfloat16), _ptr(lse, "lse", torch.float32),
                            _stream(stream))
     _check("dma_attn_fwd", st)
+
+
+def dma_attn_fwd_classify(q, k, v, mask, bias, scale: float, is_causal: bool, block_state, o, lse,
+                          stream=None) -> None:
+    """Forward that also writes the block classification (block_state is an output)."""
+    b, lq, hq, d = q.shape
+    lk, hkv = k.shape[1], k.shape[2]
+    st = _lib.dma_attn_fwd_classify(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                    _ptr(v, "v", torch.bfloat16), _ptr(mask, "mask", torch.bfloat16),
+                                    _ptr(bias, "bias", torch.bfloat16), b, lq, lk, hq, hkv, d, float(scale),
+                                    int(bool(is_causal)), _ptr(block_state, "block_state", torch.uint8),
+                                    _ptr(o, "o", torch.bfloat16), _ptr(lse, "lse", torch.float32), _stream(stream))
+    _check("dma_attn_fwd_classify", st)
 
 
 def dma_attn_bwd_workspace_size(b: int, lq: int, lk: int, hq: int, hkv: int, d: int, is_causal: bool) -> int:

@@ -96,7 +96,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const int32_t* rstart,
                   const int32_t* rend, const uint8_t* mbits, const uint16_t* bias, const uint8_t* block_state,
                   int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal,
-                  uint16_t* o, float* lse, void* stream) {
+                  uint16_t* o, float* lse, void* stream, uint8_t* state_out = nullptr) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !lse || !aligned16(o) || !aligned16(lse)) return DMA_ERR_INVALID_ARGUMENT;
@@ -111,7 +111,8 @@ int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.rend = rend;
   a.mbits = mbits;
   a.bias = bias;
-  a.state = block_state;
+  a.state = state_out ? nullptr : block_state;  // the fused classification writes the bitmap instead
+  a.state_out = state_out;
   a.o_out = o;
   a.lse_out = lse;
   a.b = b;
@@ -133,6 +134,14 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  float scale, int is_causal, uint16_t* o, float* lse, void* stream) {
   return attn_fwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, b, lq, lk, hq, hkv, d, scale,
                        is_causal, o, lse, stream);
+}
+
+int dma_attn_fwd_classify(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,
+                          const uint16_t* bias, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                          float scale, int is_causal, uint8_t* block_state, uint16_t* o, float* lse, void* stream) {
+  if (o == nullptr || (void*)o == (void*)block_state || (void*)lse == (void*)block_state) return DMA_ERR_INVALID_ARGUMENT;
+  return attn_fwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, b, lq, lk, hq, hkv, d, scale,
+                       is_causal, o, lse, stream, block_state);
 }
 
 int dma_block_classify_ranges(const int32_t* start_row, const int32_t* end_row, int64_t b, int64_t hkv, int64_t lq,

@@ -11,6 +11,8 @@ constexpr uint8_t kSkip = 0, kPartial = 1, kFull = 2;
 // How the attention kernels learn which (query, key) pairs attend: a dense bf16 mask (or none),
 // per-key row intervals, or the bit-packed PARTIAL blocks written by the classification.
 constexpr int kMaskDense = 0, kMaskRanges = 1, kMaskBits = 2;
+// The forward with a dense mask that also classifies the blocks it visits (no input bitmap).
+constexpr int kMaskDenseClassify = 3;
 constexpr int kBitsPerBlock = kBlock * kBlock / 8;  // bytes of one block's bits: row r at bytes 8r .. 8r+7
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -159,6 +161,7 @@ struct AttnArgs {
   const uint8_t* mbits;  // bit-packed PARTIAL blocks instead of the mask, see launch_classify
   const uint16_t* bias;
   const uint8_t* state;
+  uint8_t* state_out;  // the forward's classification output (dense mask, no input bitmap)
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse_in;

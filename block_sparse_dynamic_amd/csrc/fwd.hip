@@ -53,6 +53,7 @@ struct FwdParams {
   const uint8_t* mbits;   // bit-packed PARTIAL blocks (instead of the mask)
   const uint16_t* bias;
   const uint8_t* state;
+  uint8_t* state_out;  // classification output of the fused mode
   uint16_t* o;
   float* lse;
   int64_t lq, lk, hq, hkv;
@@ -76,6 +77,7 @@ struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay s
   uint8_t st[kStateChunkF];    // block states of this query block's row, a chunk at a time
   int32_t rs[2][kBlock];       // column ranges of the current and the next key block (range input)
   int32_t re[2][kBlock];
+  int32_t cls[2][8];           // per-wave any / all of the staged block's validity (fused classification)
 };
 
 template <int D, int HC, int MK>
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
   float m_ref = -INFINITY, l_part = 0.f;
 
-  const uint8_t* st_row = p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
+  const uint8_t* st_row = MK == kMaskDenseClassify ? nullptr : p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
   const uint16_t* kbase = p.k + (bidx * p.lk * p.hkv + g) * D;
   const uint16_t* vbase = p.v + (bidx * p.lk * p.hkv + g) * D;
   const int64_t plane_off = (int64_t)plane * p.lq * p.lk;
@@ -133,7 +135,15 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   // Block states of this row are cached in LDS a chunk at a time, so skipping a SKIP block
   // costs an LDS read instead of a dependent global load.
   int cache_lo = -kStateChunkF;  // cached key blocks: [cache_lo, cache_lo + kStateChunkF)
+  // fused classification: the blocks not wholly excluded by causality are [0, kb_end)
+  constexpr bool kCls = MK == kMaskDenseClassify;
+  int kb_end = p.nkb;
+  if (kCls && p.causal) {
+    const int64_t last = min((int64_t)qb * kBlock + kBlock - 1, p.lq - 1) + shift;  // largest visible key
+    kb_end = last < 0 ? 0 : (int)min((int64_t)p.nkb, last / kBlock + 1);
+  }
   auto next_kb = [&](int from) -> int {
+    if constexpr (kCls) return from < kb_end ? from : p.nkb;
     for (int kb = from; kb < p.nkb; ++kb) {
       if (kb >= cache_lo + kStateChunkF) {
         lds_barrier();  // every reader of the previous chunk is done
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int n = 0; n < BN; ++n) {
       pb[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)bo[n], 0, 0));
-      if constexpr (MK == kMaskDense)
+      if constexpr (MK == kMaskDense || MK == kMaskDenseClassify)
         pm[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, (int)bo[n], 0, 0));
       if constexpr (MK == kMaskBits) {
         const int task = tid + n * NT;
@@ -224,7 +234,8 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   }
 
   int kb = next_kb(0);
-  uint8_t st = kb < p.nkb ? sm.st[kb - cache_lo] : kSkip;
+  // the fused classification reads the mask of every visited block (as for a PARTIAL one)
+  uint8_t st = kb < p.nkb ? (kCls ? kPartial : sm.st[kb - cache_lo]) : kSkip;
   if (kb < p.nkb) prefetch(kb, st);
   int rpar = 0;  // which of the two range buffers holds the current block's ranges
   if constexpr (MK == kMaskRanges) {
@@ -248,6 +259,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       for (int e = 0; e < 4; ++e) vh[e] = bf16x2_to_f16x2(pv[n][e]);
       *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = vh;
     }
+    bool any_v = false, all_v = true;  // fused classification: this thread's positions of the block
     {
 #pragma unroll
       for (int n = 0; n < BN; ++n) {
@@ -287,6 +299,10 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         for (int e = 0; e < 4; ++e) {
           const bool v0 = 2 * e <= emax && attends_lo(mw[e]);
           const bool v1 = 2 * e + 1 <= emax && attends_hi(mw[e]);
+          if constexpr (kCls) {
+            any_v = any_v || v0 || v1;
+            all_v = all_v && v0 && v1;
+          }
           const float lo = v0 ? bf16_lo(bw[e]) * inv_as : -INFINITY;
           const float hi16 = v1 ? bf16_hi(bw[e]) * inv_as : -INFINITY;
           if (e < 2) {
@@ -301,12 +317,37 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         *reinterpret_cast<f32x4*>(&sm.b[r * BR + c * 8 + 4]) = y1;
       }
     }
+    if constexpr (kCls) {
+      // the block is SKIP without a valid position, FULL when all 4096 are valid (rows past lq
+      // and keys past lk count as invalid), PARTIAL otherwise; every thread holds 8 positions
+      const bool wany = __any(any_v), wall = __all(all_v);
+      if (lane == 0) {
+        sm.cls[0][wave] = wany;
+        sm.cls[1][wave] = wall;
+      }
+    }
     lds_barrier();
+    uint8_t bst = kPartial;
+    if constexpr (kCls) {
+      bool a = false, f = true;
+#pragma unroll
+      for (int w2 = 0; w2 < NT / 64; ++w2) {
+        a = a || sm.cls[0][w2] != 0;
+        f = f && sm.cls[1][w2] != 0;
+      }
+      bst = a ? (f ? kFull : kPartial) : kSkip;
+      if (chunk == 0 && tid == 0) p.state_out[((int64_t)plane * p.nqb + qb) * p.nkb + kb] = bst;
+    }
     // ---- start loading the next non-SKIP block ------------------------------
     const int kb_next = next_kb(kb + 1);
-    const uint8_t st_next = kb_next < p.nkb ? sm.st[kb_next - cache_lo] : kSkip;
+    const uint8_t st_next = kb_next < p.nkb ? (kCls ? kPartial : sm.st[kb_next - cache_lo]) : kSkip;
     if (kb_next < p.nkb) prefetch(kb_next, st_next);
 
+    if (kCls && bst == kSkip) {  // nothing valid in the block: no products (its state is written)
+      kb = kb_next;
+      st = st_next;
+      continue;
+    }
     // ---- y = S^T / |scale| + effective bias / |scale| = K Q^T + the staged tile ----------------
     f32x16 sacc[2];
 #pragma unroll
@@ -391,6 +432,11 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     st = st_next;
   }
 
+  if constexpr (kCls) {  // blocks wholly excluded by causality are SKIP without a read
+    if (chunk == 0)
+      for (int kbd = kb_end + tid; kbd < p.nkb; kbd += NT) p.state_out[((int64_t)plane * p.nqb + qb) * p.nkb + kbd] = kSkip;
+  }
+
   // ---- epilogue -----------------------------------------------------------------
   const float l_tot = sum_with_half_swap(l_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -415,6 +461,8 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_kernel<D, HC, kMaskRanges>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
   else if (p.mbits != nullptr)
     hipLaunchKernelGGL((fwd_kernel<D, HC, kMaskBits>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
+  else if (p.state_out != nullptr)
+    hipLaunchKernelGGL((fwd_kernel<D, HC, kMaskDenseClassify>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
   else
     hipLaunchKernelGGL((fwd_kernel<D, HC, kMaskDense>), dim3(p.total_wg), dim3(HC * 128), 0, stream, p);
   return hipGetLastError();
@@ -431,6 +479,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.mbits = a.mbits;
   p.bias = a.bias;
   p.state = a.state;
+  p.state_out = a.state_out;
   p.o = a.o_out;
   p.lse = a.lse_out;
   p.lq = a.lq;

@@ -109,6 +109,28 @@ int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
                  float scale, int is_causal, uint16_t* o, float* lse, void* stream);
 
+/*
+ * Forward pass with the block classification fused in (Flash-DMA README, key
+ * design: the mask's block reduction decides which tiles are computed, and the
+ * same decisions serve the backward; FlashMask README: fully / partially /
+ * unmasked blocks).  Computes o and lse exactly as dma_attn_fwd does after
+ * dma_block_classify, and writes the same block_state bitmap, in one pass: each
+ * visited block's mask tile is read once, reduced to SKIP / PARTIAL / FULL and
+ * applied.  Blocks wholly excluded by causality are written SKIP and never
+ * read; a block whose mask tile is all zero is written SKIP and computes
+ * nothing, but its K, V and bias rows have been fetched with the mask (the
+ * decision needs the tile), so masks with many all-zero blocks are better
+ * served by the separate dma_block_classify.
+ *
+ *   arguments as dma_attn_fwd, except
+ *   block_state out, uint8 [b, hkv, ceil(lq/64), ceil(lk/64)], as written by
+ *               dma_block_classify for the same mask, sizes and is_causal
+ * Errors: as dma_attn_fwd (block_state must not alias o or lse).
+ */
+int dma_attn_fwd_classify(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,
+                          const uint16_t* bias, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                          float scale, int is_causal, uint8_t* block_state, uint16_t* o, float* lse, void* stream);
+
 /* Bytes of device workspace dma_attn_bwd needs for these sizes (0 for invalid
  * sizes): the fp32 row terms -rowsum(dO * O) and -lse log2(e), each
  * [b, hq, lq], K transposed
