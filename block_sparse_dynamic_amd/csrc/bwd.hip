@@ -14,8 +14,10 @@
 //   pair_base_kernel  offsets of each query block's dS tiles (live 128-key pairs before it).
 //   bwd_main_kernel   one workgroup per (batch, kv head g, 128 keys = two
 //                     classification blocks); four wavefronts own 32 keys each.
-//                     Work items are (query block, 32-row half, head), heads
-//                     innermost.
+//                     Work items are (query block, 32-row half, two heads; one
+//                     head when the group size is odd), heads innermost: the
+//                     item's loads, its barrier and its control run once for
+//                     both heads.
 //                     K and V of the keys sit in registers for the whole kernel
 //                     and dK/dV accumulate in registers over every non-SKIP query
 //                     block and every head of the group, so they are written
@@ -176,19 +178,20 @@ constexpr int kKeys = 128;  // keys per workgroup: two classification blocks
 constexpr int kRows = 32;   // query rows per item (half a classification block)
 constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LDS at a time
 
-template <int D>
+template <int D, int HPI>
 struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay single 16-byte LDS accesses
   static constexpr int kTile = kRows * D;       // Q or dO tile [row][d], tile_off<D> layout
   static constexpr int kBTile = kRows * kKeys;  // raw bias or mask tile [row][key], swz128 layout
   static constexpr int kSTile = kKeys * kRows;  // dS^T [key][query], swz32 layout
-  // Two buffers each: the current item's and the next item's, which loads meanwhile.
-  uint16_t q[2][kTile];
-  uint16_t g[2][kTile];
+  // Two buffers each: the current item's and the next item's, which loads meanwhile; an item
+  // covers HPI consecutive heads of the group.
+  uint16_t q[2][HPI][kTile];
+  uint16_t g[2][HPI][kTile];
   uint16_t b[2][kBTile];
   uint16_t m[2][kBTile];  // raw mask tile, or (bit input) the item's rows of the two blocks' bits
-  uint16_t s[2][kSTile];
-  float nl2[2][64];  // -lse * log2(e) of the item's rows (rows 32..63 take the out-of-range lanes of the load)
-  float nd[2][64];   // -D = -rowsum(dO * O)
+  uint16_t s[2][HPI][kSTile];
+  float nl2[2][HPI][64];  // -lse * log2(e) of the item's rows (rows 32..63 take the out-of-range lanes of the load)
+  float nd[2][HPI][64];   // -D = -rowsum(dO * O)
   // Initial values of the S accumulator in the S layout, one slot per lane: bias / scale on
   // valid pairs, -inf (signed so that scale * it is -inf) elsewhere.  Written when a query
   // block starts, read by the same lane for every head of the group.
@@ -229,9 +232,9 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D, int MK>
+template <int D, int MK, int HPI>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
-  using Smem = BwdSmem<D>;
+  using Smem = BwdSmem<D, HPI>;
   constexpr int SR = kRows;
   constexpr int RPL = 512 / D;          // tile rows filled by one wave load (1 KB): 4 or 8
   constexpr int QL = kRows / RPL / 4;   // wave loads per Q (or dO) tile and wave: 2 or 1
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   // for it: zeros, or the earlier contents of a buffer that only ever held loaded data.
   {
     constexpr int kZero = (int)(sizeof(Smem) / 16);
-    u32x4* z = reinterpret_cast<u32x4*>(&sm.q[0][0]);
+    u32x4* z = reinterpret_cast<u32x4*>(&sm.q[0][0][0]);
     for (int i = tid; i < kZero; i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
 
@@ -380,8 +383,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   // LDS byte addresses of the load destinations (buffer B of a tile is B tiles above buffer 0):
   // plain integers, so no generic-to-LDS pointer conversion is redone on every item
   constexpr uint32_t kTileBytes = Smem::kTile * 2, kBTileBytes = Smem::kBTile * 2;
-  const uint32_t lds_q = lds_addr(&sm.q[0][0]), lds_g = lds_addr(&sm.g[0][0]), lds_b = lds_addr(&sm.b[0][0]),
-                 lds_m = lds_addr(&sm.m[0][0]), lds_nl2 = lds_addr(&sm.nl2[0][0]), lds_nd = lds_addr(&sm.nd[0][0]);
+  const uint32_t lds_q = lds_addr(&sm.q[0][0][0]), lds_g = lds_addr(&sm.g[0][0][0]), lds_b = lds_addr(&sm.b[0][0]),
+                 lds_m = lds_addr(&sm.m[0][0]), lds_nl2 = lds_addr(&sm.nl2[0][0][0]), lds_nd = lds_addr(&sm.nd[0][0][0]);
   // Start the loads of an item into buffer B: Q and dO rows, the raw bias and mask rows of a
   // new query block (first head of the group only), and the row terms.
   auto issue = [&](int B, int qb, int rh, int hh, uint8_t s0, uint8_t s1) {
@@ -389,12 +392,15 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     const int rows_left = min(kRows, (int)p.lq - i0);  // >= 1
     const int64_t item = ((int64_t)i0 * p.hq + hh) * D;
     const uint32_t qbytes = (uint32_t)(rows_left - 1) * qrow_bytes + (uint32_t)D * 2u;
-    const u32x4 rq = rsrc_words(q_plane + item, qbytes), rg = rsrc_words(g_plane + item, qbytes);
 #pragma unroll
-    for (int n = 0; n < QL; ++n) {
-      const uint32_t dst = (uint32_t)((wave * QL + n) * 1024);
-      dma_x4(rq, lds_q + (uint32_t)B * kTileBytes + dst, qv[n]);
-      dma_x4(rg, lds_g + (uint32_t)B * kTileBytes + dst, qv[n]);
+    for (int h2 = 0; h2 < HPI; ++h2) {
+      const u32x4 rq = rsrc_words(q_plane + item + h2 * D, qbytes), rg = rsrc_words(g_plane + item + h2 * D, qbytes);
+#pragma unroll
+      for (int n = 0; n < QL; ++n) {
+        const uint32_t dst = (uint32_t)((B * HPI + h2) * kTileBytes + (wave * QL + n) * 1024);
+        dma_x4(rq, lds_q + dst, qv[n]);
+        dma_x4(rg, lds_g + dst, qv[n]);
+      }
     }
     if (hh == 0) {
       const uint32_t bbytes = (uint32_t)(rows_left - 1) * (uint32_t)p.lk * 2u + krange;
@@ -424,9 +430,14 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         }
       }
     }
-    const int64_t ridx = (int64_t)hh * p.lq + i0;
-    if (wave == 0) dma_x1(rsrc_words(nl2_plane + ridx, (uint32_t)rows_left * 4u), lds_nl2 + (uint32_t)B * 256u, (uint32_t)lane * 4u);
-    if (wave == 1) dma_x1(rsrc_words(nd_plane + ridx, (uint32_t)rows_left * 4u), lds_nd + (uint32_t)B * 256u, (uint32_t)lane * 4u);
+    // row terms of head hh + h2: wave 2 h2 fetches -lse log2 e, wave 2 h2 + 1 fetches -D
+#pragma unroll
+    for (int h2 = 0; h2 < HPI; ++h2) {
+      const int64_t ridx = (int64_t)(hh + h2) * p.lq + i0;
+      const uint32_t rdst = (uint32_t)((B * HPI + h2) * 256);
+      if (wave == 2 * h2) dma_x1(rsrc_words(nl2_plane + ridx, (uint32_t)rows_left * 4u), lds_nl2 + rdst, (uint32_t)lane * 4u);
+      if (wave == 2 * h2 + 1) dma_x1(rsrc_words(nd_plane + ridx, (uint32_t)rows_left * 4u), lds_nd + rdst, (uint32_t)lane * 4u);
+    }
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -506,7 +517,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
                                   ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pbv >> 32)) << 32));
 
     // ---- start loading the next item ------------------------------------------------
-    int nqb = qb, nrh = rh, nhh = hh + 1;
+    int nqb = qb, nrh = rh, nhh = hh + HPI;
     uint8_t ns0 = cs0, ns1 = cs1;
     if (nhh == p.G) {
       nhh = 0;
@@ -578,111 +589,120 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     // dS are exactly zero and it adds nothing (a branch here would make the compiler shuttle
     // the dK/dV accumulators between register files on every item).
     // ---- S + bias/scale = Q K^T + init and dP - D = dO V^T - D: 32 queries x 32 keys -----------
-    f32x16 sacc, pacc;
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const f32x4 iv = sm.beff[wave][gi][lane];
-      const f32x4 nd = *reinterpret_cast<const f32x4*>(&sm.nd[B][gi * 8 + hi * 4]);
+    for (int h2 = 0; h2 < HPI; ++h2) {
+      if (h2 > 0) {  // the loop-carried registers stay in the accumulation file between heads
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sacc[gi * 4 + e] = iv[e];
-        pacc[gi * 4 + e] = nd[e];
+        for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(kreg[s]), "+a"(vreg[s]));
       }
-    }
-    // Every operand read is issued before the first product (a scheduling barrier keeps
-    // them there), so the products wait on LDS once instead of once per k-step.
-    bf16x8 opq[D / 16], opg[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      opq[s] = *reinterpret_cast<const bf16x8*>(&sm.q[B][aoffs[s]]);
-      opg[s] = *reinterpret_cast<const bf16x8*>(&sm.g[B][aoffs[s]]);
-    }
-    f32x4 nl[4];
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) nl[gi] = *reinterpret_cast<const f32x4*>(&sm.nl2[B][gi * 8 + hi * 4]);
-    __builtin_amdgcn_sched_barrier(0);
-    // The wave issues in order and is the only one on its SIMD, so the vector work of the item
-    // only overlaps the matrix products if it sits between them: S first; then the dP products
-    // with P = exp2(...) of the finished S between them; the dV products (they need P only)
-    // with dS = P (dP - D); the dK products with the dS^T tile writes.  Group barriers fix
-    // that interleave (one product, then up to seven vector instructions).
-    // ---- S + bias/scale = Q K^T + init: 32 queries x 32 keys ----------------------------------
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) sacc = mfma32(opq[s], kreg[s], sacc);
-    __builtin_amdgcn_sched_barrier(0);
-    // the transposing reads of the dV/dK operands do not depend on P or dS: issue them now
-    i16x4 trg[2][D / 32][2], trq[2][D / 32][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        trg[ks][dt][0] = lds_read_tr16(&sm.g[B][goffs[dt][0] + ks * 16 * D]);
-        trg[ks][dt][1] = lds_read_tr16(&sm.g[B][goffs[dt][1] + ks * 16 * D]);
-        trq[ks][dt][0] = lds_read_tr16(&sm.q[B][goffs[dt][0] + ks * 16 * D]);
-        trq[ks][dt][1] = lds_read_tr16(&sm.q[B][goffs[dt][1] + ks * 16 * D]);
+      f32x16 sacc, pacc;
+  #pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 iv = sm.beff[wave][gi][lane];
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(&sm.nd[B][h2][gi * 8 + hi * 4]);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sacc[gi * 4 + e] = iv[e];
+          pacc[gi * 4 + e] = nd[e];
+        }
       }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- dP - D = dO V^T - D, and between its products P = exp2(scale2 * S' - lse log2 e) ----
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) pacc = mfma32(opg[s], vreg[s], pacc);
-    f32x16 pv;
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pv[gi * 4 + e] = __builtin_amdgcn_exp2f(fmaf(sacc[gi * 4 + e], scale2, nl[gi][e]));
-    bf16x8 ap[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 pw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(pv[ks * 8 + 2 * e], pv[ks * 8 + 2 * e + 1]);
-      ap[ks] = __builtin_bit_cast(bf16x8, pw);
-    }
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // then seven vector instructions
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- dV += P^T dO, and between its products dS = P (dP - D) ------------------------------
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        dv[dt] = mfma32(ap[ks], join_bf16x8(trg[ks][dt][0], trg[ks][dt][1]), dv[dt]);
-    u32x4 sw[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float ds = pv[i] * pacc[i];
-      pacc[i] = ds;
-      dbacc[i] += ds;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sw[ks][e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- dK += dS^T Q, and between its products the dS^T tile writes ----------------------------
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 as = __builtin_bit_cast(bf16x8, sw[ks]);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        dk[dt] = mfma32(as, join_bf16x8(trq[ks][dt][0], trq[ks][dt][1]), dk[dt]);
-      // the same bf16 pairs (rows gi*4 + 2e', + 1 of the S layout) form the dS^T rows below
-      u32x2 lo2, hi2;
-      lo2[0] = sw[ks][0];
-      lo2[1] = sw[ks][1];
-      hi2[0] = sw[ks][2];
-      hi2[1] = sw[ks][3];
-      *reinterpret_cast<u32x2*>(&sm.s[B][swoffs[2 * ks]]) = lo2;
-      *reinterpret_cast<u32x2*>(&sm.s[B][swoffs[2 * ks + 1]]) = hi2;
+      // Every operand read is issued before the first product (a scheduling barrier keeps
+      // them there), so the products wait on LDS once instead of once per k-step.
+      bf16x8 opq[D / 16], opg[D / 16];
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        opq[s] = *reinterpret_cast<const bf16x8*>(&sm.q[B][h2][aoffs[s]]);
+        opg[s] = *reinterpret_cast<const bf16x8*>(&sm.g[B][h2][aoffs[s]]);
+      }
+      f32x4 nl[4];
+  #pragma unroll
+      for (int gi = 0; gi < 4; ++gi) nl[gi] = *reinterpret_cast<const f32x4*>(&sm.nl2[B][h2][gi * 8 + hi * 4]);
+      __builtin_amdgcn_sched_barrier(0);
+      // The wave issues in order and is the only one on its SIMD, so the vector work of the item
+      // only overlaps the matrix products if it sits between them: S first; then the dP products
+      // with P = exp2(...) of the finished S between them; the dV products (they need P only)
+      // with dS = P (dP - D); the dK products with the dS^T tile writes.  Group barriers fix
+      // that interleave (one product, then up to seven vector instructions).
+      // ---- S + bias/scale = Q K^T + init: 32 queries x 32 keys ----------------------------------
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s) sacc = mfma32(opq[s], kreg[s], sacc);
+      __builtin_amdgcn_sched_barrier(0);
+      // the transposing reads of the dV/dK operands do not depend on P or dS: issue them now
+      i16x4 trg[2][D / 32][2], trq[2][D / 32][2];
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          trg[ks][dt][0] = lds_read_tr16(&sm.g[B][h2][goffs[dt][0] + ks * 16 * D]);
+          trg[ks][dt][1] = lds_read_tr16(&sm.g[B][h2][goffs[dt][1] + ks * 16 * D]);
+          trq[ks][dt][0] = lds_read_tr16(&sm.q[B][h2][goffs[dt][0] + ks * 16 * D]);
+          trq[ks][dt][1] = lds_read_tr16(&sm.q[B][h2][goffs[dt][1] + ks * 16 * D]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- dP - D = dO V^T - D, and between its products P = exp2(scale2 * S' - lse log2 e) ----
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s) pacc = mfma32(opg[s], vreg[s], pacc);
+      f32x16 pv;
+  #pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+  #pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pv[gi * 4 + e] = __builtin_amdgcn_exp2f(fmaf(sacc[gi * 4 + e], scale2, nl[gi][e]));
+      bf16x8 ap[2];
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 pw;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(pv[ks * 8 + 2 * e], pv[ks * 8 + 2 * e + 1]);
+        ap[ks] = __builtin_bit_cast(bf16x8, pw);
+      }
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // then seven vector instructions
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- dV += P^T dO, and between its products dS = P (dP - D) ------------------------------
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          dv[dt] = mfma32(ap[ks], join_bf16x8(trg[ks][dt][0], trg[ks][dt][1]), dv[dt]);
+      u32x4 sw[2];
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float ds = pv[i] * pacc[i];
+        pacc[i] = ds;
+        dbacc[i] += ds;
+      }
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) sw[ks][e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- dK += dS^T Q, and between its products the dS^T tile writes ----------------------------
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 as = __builtin_bit_cast(bf16x8, sw[ks]);
+  #pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          dk[dt] = mfma32(as, join_bf16x8(trq[ks][dt][0], trq[ks][dt][1]), dk[dt]);
+        // the same bf16 pairs (rows gi*4 + 2e', + 1 of the S layout) form the dS^T rows below
+        u32x2 lo2, hi2;
+        lo2[0] = sw[ks][0];
+        lo2[1] = sw[ks][1];
+        hi2[0] = sw[ks][2];
+        hi2[1] = sw[ks][3];
+        *reinterpret_cast<u32x2*>(&sm.s[B][h2][swoffs[2 * ks]]) = lo2;
+        *reinterpret_cast<u32x2*>(&sm.s[B][h2][swoffs[2 * ks + 1]]) = hi2;
+      }
     }
     dma_barrier();  // dS^T complete; the next item's buffers are loaded; this item's are free
 
@@ -691,20 +711,21 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     // writes chunks tid and tid + 256: transposing reads of the dS^T tile give it those 8
     // keys of its query (k-steps wave and wave + 4, rows hi*8 of the step), and consecutive
     // lanes store consecutive chunks.
-    {
-      uint16_t* tile = p.ds + ((((int64_t)plane * p.npairs + pbc + KB) * p.G + hh) * 2 + rh) * (kRows * kKeys);
+#pragma unroll
+    for (int h2 = 0; h2 < HPI; ++h2) {
+      uint16_t* tile = p.ds + ((((int64_t)plane * p.npairs + pbc + KB) * p.G + hh + h2) * 2 + rh) * (kRows * kKeys);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int ks = wave + 4 * hf;
         const int sofs = (ks >> 1) * 32 * SR;
-        const i16x4 a0 = lds_read_tr16(&sm.s[B][sq[ks & 1][0] + sofs]);
-        const i16x4 a1 = lds_read_tr16(&sm.s[B][sq[ks & 1][1] + sofs]);
+        const i16x4 a0 = lds_read_tr16(&sm.s[B][h2][sq[ks & 1][0] + sofs]);
+        const i16x4 a1 = lds_read_tr16(&sm.s[B][h2][sq[ks & 1][1] + sofs]);
         *reinterpret_cast<bf16x8*>(tile + (tid + 256 * hf) * 8) = join_bf16x8(a0, a1);
       }
     }
 
     // ---- dBias of the item's rows, summed over the group: store after the last head -------------
-    if (hh == p.G - 1 && p.dbias != nullptr) {
+    if (hh + HPI == p.G && p.dbias != nullptr) {
       // rows at or past rows_left fall outside the resource; a lane whose key is past lk
       // takes an offset beyond it, so its stores are dropped as well
       const uint32_t rbytes = (uint32_t)p.lk * 2u;
@@ -948,15 +969,21 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.causal = a.causal;
   const int MK = a.rstart != nullptr ? kMaskRanges : a.mbits != nullptr ? kMaskBits : kMaskDense;
   auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(p.total_wg), dim3(256), 0, stream, p); };
-  if (a.d == 64) {
-    if (MK == kMaskRanges) launch_main(bwd_main_kernel<64, kMaskRanges>);
-    else if (MK == kMaskBits) launch_main(bwd_main_kernel<64, kMaskBits>);
-    else launch_main(bwd_main_kernel<64, kMaskDense>);
-  } else {
-    if (MK == kMaskRanges) launch_main(bwd_main_kernel<128, kMaskRanges>);
-    else if (MK == kMaskBits) launch_main(bwd_main_kernel<128, kMaskBits>);
-    else launch_main(bwd_main_kernel<128, kMaskDense>);
-  }
+  // an item covers two heads when the group size is even
+  auto launch_d = [&](auto dconst) {
+    constexpr int D = decltype(dconst)::value;
+    if (p.G % 2 == 0) {
+      if (MK == kMaskRanges) launch_main(bwd_main_kernel<D, kMaskRanges, 2>);
+      else if (MK == kMaskBits) launch_main(bwd_main_kernel<D, kMaskBits, 2>);
+      else launch_main(bwd_main_kernel<D, kMaskDense, 2>);
+    } else {
+      if (MK == kMaskRanges) launch_main(bwd_main_kernel<D, kMaskRanges, 1>);
+      else if (MK == kMaskBits) launch_main(bwd_main_kernel<D, kMaskBits, 1>);
+      else launch_main(bwd_main_kernel<D, kMaskDense, 1>);
+    }
+  };
+  if (a.d == 64) launch_d(std::integral_constant<int, 64>{});
+  else launch_d(std::integral_constant<int, 128>{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
