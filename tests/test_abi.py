@@ -27,6 +27,7 @@ def lib():
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.dma_block_classify.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp]
     L.dma_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp]
+    L.dma_attn_fwd_classify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp, vp]
     L.dma_attn_bwd_workspace_size.restype = sz
     L.dma_attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     L.dma_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, vp, vp, vp,
@@ -82,6 +83,26 @@ def fwd(lib, **kw):
     a.update(kw)
     return lib.dma_attn_fwd(a["q"], a["k"], a["v"], a["mask"], a["bias"], a["st"], a["b"], a["lq"], a["lk"], a["hq"],
                             a["hkv"], a["d"], a["scale"], a["causal"], a["o"], a["lse"], a["stream"])
+
+
+def fwd_cls(lib, **kw):
+    a = dict(q=P, k=P, v=P, mask=P, bias=P, b=1, lq=128, lk=128, hq=4, hkv=2, d=128, scale=0.1, causal=1, st=P,
+             o=P, lse=P, stream=None)
+    a.update(kw)
+    return lib.dma_attn_fwd_classify(a["q"], a["k"], a["v"], a["mask"], a["bias"], a["b"], a["lq"], a["lk"],
+                                     a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["st"], a["o"], a["lse"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(st=None), INVALID), (dict(o=None), INVALID), (dict(lse=None), INVALID),
+    (dict(st=P + 0x10000, o=P + 0x10000), INVALID), (dict(b=0), INVALID), (dict(mask=P + 8), INVALID),
+    (dict(lk=100), INVALID), (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(causal=2), INVALID), (dict(d=96), UNSUPPORTED), (dict(hq=6, hkv=2), UNSUPPORTED),
+])
+def test_fwd_classify_rejects(lib, kw, want):
+    # validation runs before anything is enqueued, so the stand-in pointers are never touched
+    assert fwd_cls(lib, **kw) == want
 
 
 def bwd(lib, **kw):
