@@ -86,8 +86,8 @@ def fwd(lib, **kw):
 
 
 def fwd_cls(lib, **kw):
-    a = dict(q=P, k=P, v=P, mask=P, bias=P, b=1, lq=128, lk=128, hq=4, hkv=2, d=128, scale=0.1, causal=1, st=P,
-             o=P, lse=P, stream=None)
+    a = dict(q=P, k=P, v=P, mask=P, bias=P, b=1, lq=128, lk=128, hq=4, hkv=2, d=128, scale=0.1, causal=1, st=P + 0x100,
+             o=P + 0x200, lse=P + 0x300, stream=None)
     a.update(kw)
     return lib.dma_attn_fwd_classify(a["q"], a["k"], a["v"], a["mask"], a["bias"], a["b"], a["lq"], a["lk"],
                                      a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["st"], a["o"], a["lse"],
