@@ -628,8 +628,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       // ---- S + bias/scale = Q K^T + init: 32 queries x 32 keys ----------------------------------
   #pragma unroll
       for (int s = 0; s < D / 16; ++s) sacc = mfma32(opq[s], kreg[s], sacc);
-      __builtin_amdgcn_sched_barrier(0);
-      // the transposing reads of the dV/dK operands do not depend on P or dS: issue them now
+      // the transposing reads of the dV/dK operands do not depend on P or dS: they issue between
+      // the S products (one product, then four reads), whose dependent chain leaves the wave idle
       i16x4 trg[2][D / 32][2], trq[2][D / 32][2];
   #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -640,6 +640,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
           trq[ks][dt][0] = lds_read_tr16(&sm.q[B][h2][goffs[dt][0] + ks * 16 * D]);
           trq[ks][dt][1] = lds_read_tr16(&sm.q[B][h2][goffs[dt][1] + ks * 16 * D]);
         }
+  #pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // ---- dP - D = dO V^T - D, and between its products P = exp2(scale2 * S' - lse log2 e) ----
   #pragma unroll
