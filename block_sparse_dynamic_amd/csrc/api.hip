@@ -178,9 +178,10 @@ namespace {
 //   rows       fp32 2 x [b, hq, lq]                -rowsum(dO * O), then -lse * log2(e)
 //   pair_base  int64 [nqb + 1]                     first dS tile pair of each query block
 //   kt         bf16 [b, hkv, d, nkb2 * 128]        K transposed
-//   ds         bf16 [b, hkv, npairs, G, 2, 32*128] dS tiles of every live (query block, key pair)
+//   ds         bf16 [b, hkv, npairs, G, 2, 32*128] dS tile slots of every live (query block, key pair)
+//   dsmap      u64  [b, hkv, npairs, G, 2, 8]      which 16-byte chunks of each slot are stored
 struct WsLayout {
-  size_t rows, pair_base, kt, ds, total;
+  size_t rows, pair_base, kt, ds, dsmap, total;
   int64_t npairs;
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -194,7 +195,8 @@ WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, i
   w.pair_base = w.rows + up256((size_t)2 * b * hq * lq * sizeof(float));
   w.kt = w.pair_base + up256((size_t)(nqb + 1) * sizeof(int64_t));
   w.ds = w.kt + up256((size_t)b * hkv * d * nkb2 * 128 * sizeof(uint16_t));
-  w.total = w.ds + up256((size_t)b * hq * np * 2 * 32 * 128 * sizeof(uint16_t));
+  w.dsmap = w.ds + up256((size_t)b * hq * np * 2 * 32 * 128 * sizeof(uint16_t));
+  w.total = w.dsmap + up256((size_t)b * hq * np * 2 * 8 * sizeof(uint64_t));
   return w;
 }
 }  // namespace
@@ -251,6 +253,7 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.pair_base = reinterpret_cast<int64_t*>(ws + wl.pair_base);
   a.kt = reinterpret_cast<uint16_t*>(ws + wl.kt);
   a.ds = reinterpret_cast<uint16_t*>(ws + wl.ds);
+  a.dsmap = reinterpret_cast<uint64_t*>(ws + wl.dsmap);
   a.npairs = wl.npairs;
   a.b = b;
   a.lq = lq;

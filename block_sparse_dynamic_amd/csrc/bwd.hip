@@ -29,7 +29,7 @@
 //                     bias/mask rows of a new query block) of the next item are
 //                     loaded straight into LDS while the current item computes.
 //                     Each item's dS (bf16) goes to the workspace in the order the
-//                     dQ kernel consumes it.
+//                     dQ kernel consumes it, nonzero 16-byte chunks only.
 //   dq_kernel         dQ = scale dS K: one workgroup per (batch, g, 64-row query block,
 //                     heads), summing over the live key pairs in registers and
 //                     writing bf16 dQ once.
@@ -39,7 +39,10 @@
 // pattern.  Adding each item's dS K into a dQ accumulator costs one add per (query, d,
 // 128-key pair): 4.3e9 adds, ~12.7 ms, at L = 16384 with causal top-k, more than all the
 // matrix work of the backward.  Writing dS (one bf16 per query, key and head) and reading
-// it back once is ~17 GB of plain traffic and no atomics; dQ also becomes deterministic.
+// it back once is plain traffic and no atomics, and dQ becomes deterministic.  Only the
+// nonzero 16-byte chunks (8 keys of one query row) travel: with sparse masks most are zero
+// (at top-k 1024 of 16384 keys, 60% of them), which cuts the round trip from ~17 GB to ~7 GB
+// at L = 16384.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 for all five products.  S = Q K^T puts one key
 // per lane (lane l%32) and 16 query rows per lane, which is the A-operand layout
@@ -164,6 +167,7 @@ struct BwdParams {
   const float* nd;   // -D, fp32 [b, hq, lq]
   const int64_t* pair_base;
   uint16_t* ds;
+  uint64_t* dsmap;
   int64_t npairs;
   uint16_t* dk;
   uint16_t* dv;
@@ -711,22 +715,45 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     }
     dma_barrier();  // dS^T complete; the next item's buffers are loaded; this item's are free
 
-    // ---- dS of the item to the workspace, in the order the dQ kernel reads it --------------
+    // ---- dS of the item to the workspace: its nonzero chunks only, in dQ-kernel order --------
     // 16-byte chunk c holds keys (c/64)*16 + ((c/32)%2)*8 .. +7 of query row c%32.  This lane
-    // writes chunks tid and tid + 256: transposing reads of the dS^T tile give it those 8
-    // keys of its query (k-steps wave and wave + 4, rows hi*8 of the step), and consecutive
-    // lanes store consecutive chunks.
+    // owns chunks tid and tid + 256: transposing reads of the dS^T tile give it those 8 keys of
+    // its query (k-steps wave and wave + 4, rows hi*8 of the step).  dS is zero wherever P is
+    // (masked, SKIP or non-causal keys), so with sparse masks most chunks are zero: each wave
+    // packs its nonzero chunks (half 0 in lane order, then half 1) at the start of its own
+    // quarter of the slot, and records which lanes stored one in two 64-bit masks.  A chunk of
+    // zeros (either sign) is read back as +0, which leaves every dQ sum unchanged.
 #pragma unroll
     for (int h2 = 0; h2 < HPI; ++h2) {
-      uint16_t* tile = p.ds + ((((int64_t)plane * p.npairs + pbc + KB) * p.G + hh + h2) * 2 + rh) * (kRows * kKeys);
+      const int64_t slot = (((int64_t)plane * p.npairs + pbc + KB) * p.G + hh + h2) * 2 + rh;
+      uint16_t* seg = p.ds + slot * (kRows * kKeys) + wave * (2 * 64 * 8);
+      bf16x8 ch[2];
+      bool nz[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int ks = wave + 4 * hf;
         const int sofs = (ks >> 1) * 32 * SR;
         const i16x4 a0 = lds_read_tr16(&sm.s[B][h2][sq[ks & 1][0] + sofs]);
         const i16x4 a1 = lds_read_tr16(&sm.s[B][h2][sq[ks & 1][1] + sofs]);
-        *reinterpret_cast<bf16x8*>(tile + (tid + 256 * hf) * 8) = join_bf16x8(a0, a1);
+        ch[hf] = join_bf16x8(a0, a1);
+        const u32x4 w = __builtin_bit_cast(u32x4, ch[hf]);
+        nz[hf] = ((w[0] | w[1] | w[2] | w[3]) & 0x7FFF7FFFu) != 0u;
       }
+      const uint64_t m0 = __ballot(nz[0]), m1 = __ballot(nz[1]);
+      const int r0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u));
+      const int r1 = __popcll(m0) +
+                     (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u));
+      // no branches in the loop: a chunk that is not stored, and the mask stores of lanes past
+      // 1, take offsets past their buffer range, which drops them
+      const __amdgpu_buffer_rsrc_t rseg = make_rsrc(seg, 2 * 64 * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[0]), rseg, nz[0] ? (uint32_t)r0 * 16u : kOutOfRange, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[1]), rseg, nz[1] ? (uint32_t)r1 * 16u : kOutOfRange, 0, 0);
+      const __amdgpu_buffer_rsrc_t rmap = make_rsrc(p.dsmap + slot * 8 + wave, 5 * 8);
+      const uint64_t mw = lane ? m1 : m0;
+      u32x2 mv;
+      mv[0] = (uint32_t)mw;
+      mv[1] = (uint32_t)(mw >> 32);
+      __builtin_amdgcn_raw_buffer_store_b64(mv, rmap, lane < 2 ? (uint32_t)lane * 32u : kOutOfRange, 0, 0);
     }
 
     // ---- dBias of the item's rows, summed over the group: store after the last head -------------
@@ -781,12 +808,17 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
 //   A = K^T rows d (staged once per pair for all heads, swizzled 128-key rows),
 //   B = the dS chunks the backward main kernel stored in fragment order (lane l reads
 //       chunk ks*64 + l of its tile: query l%32, keys ks*16 + (l/32)*8 .. +7),
-// so the result lane holds one query row and 4-element runs of d for the store.
+// so the result lane holds one query row and 4-element runs of d for the store.  Only the
+// nonzero chunks are stored: chunk ks*64 + l was owned by lane l of writer wave ks%4 (half
+// ks/4), and sits at that wave's quarter of the slot + its rank among the stored chunks; the
+// slot's 8 chunk masks (read before the previous pair's chunks) give presence and rank, and an
+// absent chunk takes an offset past the slot, which the buffer load returns as zeros.
 struct DqParams {
   const uint8_t* state;
   const int64_t* pair_base;
   const uint16_t* kt;
   const uint16_t* ds;
+  const uint64_t* dsmap;
   uint16_t* dq;
   int64_t lq, lk, hq, hkv, npairs, ktrow;
   int G, chunks, nqb, nkb, total_wg;
@@ -808,7 +840,8 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   const int qb = p.nqb - 1 - (t % p.nqb);
   const int plane = unit / p.chunks, chunk = unit % p.chunks;
   const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int hh = chunk * HC + (wave >> 1), rh = wave & 1;
   const int64_t head = g * p.G + hh;
@@ -817,10 +850,9 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   const int64_t pbase = p.pair_base[qb];
   const uint8_t* st_row = p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
   const uint16_t* ktp = p.kt + (int64_t)plane * D * p.ktrow;
-  // the tile of pair KB for this wave: + (pbase + KB) * G * 2 * 4096
-  const uint16_t* dsp = p.ds + (((int64_t)plane * p.npairs + pbase) * p.G + hh) * 2 * (kRows * kKeys) +
-                        (int64_t)rh * (kRows * kKeys);
-  const int64_t pair_stride = (int64_t)p.G * 2 * (kRows * kKeys);
+  // the slot of pair KB for this wave: slot0 + KB * G * 2
+  const int64_t slot0 = (((int64_t)plane * p.npairs + pbase) * p.G + hh) * 2 + rh;
+  const int64_t slot_stride = (int64_t)p.G * 2;
 
   // The block states of this query block's row are cached in LDS a chunk of pairs at a time:
   // the pair walk then waits on LDS only, never on a global load that would also wait for the
@@ -844,22 +876,55 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
     return npair;
   };
 
-  // K^T chunks of a pair (staged into LDS one pair later) and this wave's dS fragments of a
-  // pair (eight 16-byte chunks per lane, consumed one pair later), both loaded a pair ahead so
-  // that their latency hides behind a pair of products.  A pair past the last is replaced by
-  // the current one: the loads stay unconditional and in bounds.
+  // The pair walk runs three pairs ahead of the products: the K^T chunks of a pair load one pair
+  // before it is staged into LDS, this wave's dS chunks two pairs before their products, and the
+  // pair's chunk masks three pairs before (ahead of the chunk loads of the pair before it, so
+  // that waiting for them never waits for chunk loads).  The SKIP halves of a pair are taken
+  // when the walk finds it.  A pair past the last is replaced by the current one: every load
+  // stays unconditional and in bounds.
+  struct Pair {
+    int kb;
+    bool d0, d1;  // halves that are SKIP
+  };
+  auto walk = [&](int from) -> Pair {
+    Pair r;
+    r.kb = from < npair ? (int)next_pair(from) : (int)npair;
+    r.kb = __builtin_amdgcn_readfirstlane(r.kb);
+    r.d0 = r.kb < npair && state(r.kb, 0) == kSkip;
+    r.d1 = r.kb < npair && state(r.kb, 1) == kSkip;
+    return r;
+  };
+  // a pair's 8 masks arrive as 16 words in lanes 0..15 of one register (a vector load, counted
+  // in order with the chunk loads) and are taken into scalars where the chunk offsets need them
+  auto load_maps = [&](int kb) -> uint32_t {
+    const uint32_t* mp = reinterpret_cast<const uint32_t*>(p.dsmap + (slot0 + (int64_t)kb * slot_stride) * 8);
+    return mp[lane & 15];
+  };
   u32x4 pkt[KT];
-  bf16x8 bfr[8], bnx[8];
-  auto prefetch = [&](int64_t kb2, bf16x8* dst) {
+  auto load_kt = [&](int kb) {
 #pragma unroll
     for (int n = 0; n < KT; ++n) {
       const int task = tid + n * NT;
       const int r = task >> 4, c = task & 15;
-      pkt[n] = *reinterpret_cast<const u32x4*>(ktp + (int64_t)r * p.ktrow + kb2 * 128 + c * 8);
+      pkt[n] = *reinterpret_cast<const u32x4*>(ktp + (int64_t)r * p.ktrow + (int64_t)kb * 128 + c * 8);
     }
-    const uint16_t* tile = dsp + kb2 * pair_stride;
+  };
+  auto load_chunks = [&](int kb, uint32_t mv, bf16x8* dst) {
+    uint64_t mk[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) dst[ks] = *reinterpret_cast<const bf16x8*>(tile + (ks * 64 + lane) * 8);
+    for (int i = 0; i < 8; ++i)
+      mk[i] = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mv, 2 * i) |
+              ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mv, 2 * i + 1) << 32);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(const_cast<uint16_t*>(p.ds + (slot0 + (int64_t)kb * slot_stride) * (kRows * kKeys)), kRows * kKeys * 2);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint64_t m = mk[ks];
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) +
+                            (ks >= 4 ? (uint32_t)__popcll(mk[ks - 4]) : 0u);
+      const uint32_t off = ((m >> lane) & 1u) ? ((uint32_t)(ks & 3) * (2 * 64 * 8) + rank * 8u) * 2u : kOutOfRange;
+      dst[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+    }
   };
 
   f32x16 acc[D / 32];
@@ -869,25 +934,44 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) aoff[dt] = swz128(dt * 32 + l32, hi * 8);
 
-  int64_t kb2 = next_pair(0);
-  if (kb2 < npair) prefetch(kb2, bfr);
-  while (kb2 < npair) {
+  // Pair n's dS chunks sit in B[n % 3] and its masks in M[n % 3]; the loop is unrolled three
+  // times so that the stages rotate by name: a register copy between stages would wait for the
+  // loads in flight.
+  bf16x8 B[3][8];
+  uint32_t M[3] = {0u, 0u, 0u};
+  Pair p0 = walk(0);
+  Pair p1 = walk(p0.kb + 1);
+  Pair p2 = walk(p1.kb + 1);
+  if (p0.kb < npair) {  // the loads in the loop's order: K^T of a pair, then masks, then chunks
+    M[0] = load_maps(p0.kb);
+    M[1] = load_maps(p1.kb < npair ? p1.kb : p0.kb);
+    load_chunks(p0.kb, M[0], B[0]);
+    load_kt(p0.kb);
+    M[2] = load_maps(p2.kb < npair ? p2.kb : p0.kb);
+    asm volatile("" ::: "memory");
+    load_chunks(p1.kb < npair ? p1.kb : p0.kb, M[1], B[1]);
+    asm volatile("" ::: "memory");
+  }
+  auto step = [&](auto rc) -> bool {
+    constexpr int r = decltype(rc)::value;  // n % 3
+    if (p0.kb >= npair) return false;
     // a key block that is SKIP for this query block has dS = 0 and may hold any K rows (they
     // are never loaded elsewhere): its half of the tile is staged as zeros
-    const bool dead0 = state(kb2, 0) == kSkip;
-    const bool dead1 = state(kb2, 1) == kSkip;
     lds_barrier();  // every read of the previous K^T tile is done
 #pragma unroll
     for (int n = 0; n < KT; ++n) {
       const int task = tid + n * NT;
-      const int r = task >> 4, c = task & 15;
-      const bool dead = (c < 8) ? dead0 : dead1;
-      *reinterpret_cast<u32x4*>(&ktile[swz128(r, c * 8)]) = dead ? u32x4{0u, 0u, 0u, 0u} : pkt[n];
+      const int rr = task >> 4, c = task & 15;
+      const bool dead = (c < 8) ? p0.d0 : p0.d1;
+      *reinterpret_cast<u32x4*>(&ktile[swz128(rr, c * 8)]) = dead ? u32x4{0u, 0u, 0u, 0u} : pkt[n];
     }
     lds_barrier();
-    const int64_t kb2n = next_pair(kb2 + 1);
-    prefetch(kb2n < npair ? kb2n : kb2, bnx);
-    asm volatile("" ::: "memory");  // keep the prefetch here: the compiler would sink it below the products
+    const Pair p3 = walk(p2.kb + 1);
+    load_kt(p1.kb < npair ? p1.kb : p0.kb);
+    M[r] = load_maps(p3.kb < npair ? p3.kb : p0.kb);  // pair n + 3
+    asm volatile("" ::: "memory");  // the masks of pair n + 3 load before the chunks of pair n + 2
+    load_chunks(p2.kb < npair ? p2.kb : p0.kb, M[(r + 2) % 3], B[(r + 2) % 3]);
+    asm volatile("" ::: "memory");  // keep the loads here: the compiler would sink them below the products
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
@@ -895,12 +979,16 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
         // keys ks*16 + hi*8 are 16-byte chunk 2*ks + hi; swz128 XORs the chunk index, so the
         // k-step flips bits 4..6 of the per-lane offset
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(&ktile[aoff[dt] ^ (ks << 4)]);
-        acc[dt] = mfma32(av, bfr[ks], acc[dt]);
+        acc[dt] = mfma32(av, B[r][ks], acc[dt]);
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bfr[ks] = bnx[ks];
-    kb2 = kb2n;
+    p0 = p1;
+    p1 = p2;
+    p2 = p3;
+    return true;
+  };
+  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{}) &&
+         step(std::integral_constant<int, 2>{})) {
   }
 
   // ---- dQ rows qb*64 + rh*32 + l32, d = dt*32 + gi*8 + hi*4 .. +3 ------------------------
@@ -957,6 +1045,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.nd = a.nd;
   p.pair_base = a.pair_base;
   p.ds = a.ds;
+  p.dsmap = a.dsmap;
   p.npairs = a.npairs;
   p.dk = a.dk;
   p.dv = a.dv;
@@ -997,6 +1086,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   q.pair_base = a.pair_base;
   q.kt = a.kt;
   q.ds = a.ds;
+  q.dsmap = a.dsmap;
   q.dq = a.dq;
   q.lq = a.lq;
   q.lk = a.lk;

@@ -175,7 +175,9 @@ struct AttnArgs {
   float* nl2;         // fp32 [b, hq, lq]: -lse * log2(e)
   int64_t* pair_base; // [nqb + 1]: index of query block qb's first dS tile pair (live pairs before it)
   uint16_t* kt;       // bf16 [b, hkv, d, nkb2 * 128]: K transposed, zero past lk
-  uint16_t* ds;       // bf16 dS tiles, see bwd_ds_tile
+  uint16_t* ds;       // bf16 dS tiles: per (plane, live pair, head, 32-row half) a slot of 32 x 128 values
+                      // holding only the tile's nonzero 16-byte chunks, packed per writing wave
+  uint64_t* dsmap;    // per slot 8 masks: which chunks of each (wave, half) of the writer are stored
   int64_t npairs;     // live key-block pairs of one plane (pair_base[nqb])
   int64_t b, lq, lk, hq, hkv, d;
   float scale;

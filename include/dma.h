@@ -134,10 +134,12 @@ int dma_attn_fwd_classify(const uint16_t* q, const uint16_t* k, const uint16_t* 
 /* Bytes of device workspace dma_attn_bwd needs for these sizes (0 for invalid
  * sizes): the fp32 row terms -rowsum(dO * O) and -lse log2(e), each
  * [b, hq, lq], K transposed
- * (bf16), and the bf16 dS tile of every (query head, 64-row query block, 128-key
- * pair of classification blocks) that causality leaves live, from which dQ is
- * formed without atomics (FlashMask README: deterministic backward).  With
- * is_causal the count of live pairs is about half of all pairs. */
+ * (bf16), and a slot for the bf16 dS tile of every (query head, 64-row query
+ * block, 128-key pair of classification blocks) that causality leaves live, from
+ * which dQ is formed without atomics (FlashMask README: deterministic backward),
+ * with 128 bytes per slot that record which of its 16-byte chunks are nonzero
+ * (only those are written and read back).  With is_causal the count of live
+ * pairs is about half of all pairs. */
 size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
                                    int is_causal);
 
