@@ -830,7 +830,9 @@ template <int D, int HC>
 __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   constexpr int NT = HC * 128;
   constexpr int KT = D * 16 / NT;  // 16-byte chunks of the K^T tile each thread stages
-  __shared__ __attribute__((aligned(16))) uint16_t ktile[D * 128];  // [d][128 keys], swz128 rows
+  // two K^T tiles [d][128 keys] (swz128 rows), used by alternate pairs: a pair's tile is written
+  // while a slower wave may still read the previous pair's, so one barrier per pair suffices
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[2 * D * 128];
   constexpr int kPairChunk = 2048;
   __shared__ uint8_t srow[2 * kPairChunk];  // block states of the query block's row, pairs [cache_lo, + kPairChunk)
 
@@ -952,18 +954,20 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
     load_chunks(p1.kb < npair ? p1.kb : p0.kb, M[1], B[1]);
     asm volatile("" ::: "memory");
   }
+  int kbo = 0;  // element offset of this pair's K^T tile: 0 or D * 128, alternating
   auto step = [&](auto rc) -> bool {
     constexpr int r = decltype(rc)::value;  // n % 3
     if (p0.kb >= npair) return false;
     // a key block that is SKIP for this query block has dS = 0 and may hold any K rows (they
-    // are never loaded elsewhere): its half of the tile is staged as zeros
-    lds_barrier();  // every read of the previous K^T tile is done
+    // are never loaded elsewhere): its half of the tile is staged as zeros.  The tile written
+    // here was last read two pairs ago, and every wave has passed the barrier of the pair
+    // between after those reads.
 #pragma unroll
     for (int n = 0; n < KT; ++n) {
       const int task = tid + n * NT;
       const int rr = task >> 4, c = task & 15;
       const bool dead = (c < 8) ? p0.d0 : p0.d1;
-      *reinterpret_cast<u32x4*>(&ktile[swz128(rr, c * 8)]) = dead ? u32x4{0u, 0u, 0u, 0u} : pkt[n];
+      *reinterpret_cast<u32x4*>(&ktile[kbo + swz128(rr, c * 8)]) = dead ? u32x4{0u, 0u, 0u, 0u} : pkt[n];
     }
     lds_barrier();
     const Pair p3 = walk(p2.kb + 1);
@@ -978,13 +982,14 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
       for (int dt = 0; dt < D / 32; ++dt) {
         // keys ks*16 + hi*8 are 16-byte chunk 2*ks + hi; swz128 XORs the chunk index, so the
         // k-step flips bits 4..6 of the per-lane offset
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&ktile[aoff[dt] ^ (ks << 4)]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&ktile[kbo + (aoff[dt] ^ (ks << 4))]);
         acc[dt] = mfma32(av, B[r][ks], acc[dt]);
       }
     }
     p0 = p1;
     p1 = p2;
     p2 = p3;
+    kbo ^= D * 128;
     return true;
   };
   while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{}) &&
