@@ -723,10 +723,15 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     // packs its nonzero chunks (half 0 in lane order, then half 1) at the start of its own
     // quarter of the slot, and records which lanes stored one in two 64-bit masks.  A chunk of
     // zeros (either sign) is read back as +0, which leaves every dQ sum unchanged.
+    // One buffer range per item over its heads' slots (head h2 of the item is 2 slots further:
+    // the two 32-row halves interleave), for the chunks and for the masks; the head and the
+    // wave go into the per-lane offsets.
+    const int64_t slot_a = (((int64_t)plane * p.npairs + pbc + KB) * p.G + hh) * 2 + rh;
+    const __amdgpu_buffer_rsrc_t rds =
+        make_rsrc(p.ds + slot_a * (kRows * kKeys), (uint32_t)((2 * HPI - 1) * kRows * kKeys * 2));
+    const __amdgpu_buffer_rsrc_t rmp = make_rsrc(p.dsmap + slot_a * 8, (uint32_t)((2 * HPI - 1) * 8 * 8));
 #pragma unroll
     for (int h2 = 0; h2 < HPI; ++h2) {
-      const int64_t slot = (((int64_t)plane * p.npairs + pbc + KB) * p.G + hh + h2) * 2 + rh;
-      uint16_t* seg = p.ds + slot * (kRows * kKeys) + wave * (2 * 64 * 8);
       bf16x8 ch[2];
       bool nz[2];
 #pragma unroll
@@ -744,16 +749,15 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
       const int r1 = __popcll(m0) +
                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u));
       // no branches in the loop: a chunk that is not stored, and the mask stores of lanes past
-      // 1, take offsets past their buffer range, which drops them
-      const __amdgpu_buffer_rsrc_t rseg = make_rsrc(seg, 2 * 64 * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[0]), rseg, nz[0] ? (uint32_t)r0 * 16u : kOutOfRange, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[1]), rseg, nz[1] ? (uint32_t)r1 * 16u : kOutOfRange, 0, 0);
-      const __amdgpu_buffer_rsrc_t rmap = make_rsrc(p.dsmap + slot * 8 + wave, 5 * 8);
+      // 1, take offsets past the buffer range, which drops them
+      const uint32_t seg = (uint32_t)(h2 * 2 * kRows * kKeys * 2 + wave * (2 * 64 * 16));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[0]), rds, nz[0] ? seg + (uint32_t)r0 * 16u : kOutOfRange, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[1]), rds, nz[1] ? seg + (uint32_t)r1 * 16u : kOutOfRange, 0, 0);
       const uint64_t mw = lane ? m1 : m0;
       u32x2 mv;
       mv[0] = (uint32_t)mw;
       mv[1] = (uint32_t)(mw >> 32);
-      __builtin_amdgcn_raw_buffer_store_b64(mv, rmap, lane < 2 ? (uint32_t)lane * 32u : kOutOfRange, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(mv, rmp, lane < 2 ? (uint32_t)(h2 * 16 + wave + 4 * lane) * 8u : kOutOfRange, 0, 0);
     }
 
     // ---- dBias of the item's rows, summed over the group: store after the last head -------------
