@@ -115,11 +115,42 @@ def block_state_shape(b: int, hkv: int, lq: int, lk: int):
     return (b, hkv, (lq + n - 1) // n, (lk + n - 1) // n)
 
 
+def _shapes(fn: str, q, k, v, planes=(), qlike=(), kvlike=(), lse=None, ranges=(), state=None):
+    """Sizes (b, lq, lk, hq, hkv, d) from q [b, lq, hq, d] and k [b, lk, hkv, d], after checking
+    that every other tensor has exactly the shape the C ABI reads or writes through it
+    (the library takes plain pointers: a broadcast or mis-shaped tensor would be read or
+    written past its end)."""
+    def want(name, t, shape):
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{fn}: {name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError(f"{fn}: q must be [b, lq, hq, d] and k [b, lk, hkv, d]")
+    b, lq, hq, d = q.shape
+    lk, hkv = k.shape[1], k.shape[2]
+    want("k", k, (b, lk, hkv, d))
+    want("v", v, (b, lk, hkv, d))
+    for name, t in planes:
+        want(name, t, (b, hkv, lq, lk))
+    for name, t in qlike:
+        want(name, t, (b, lq, hq, d))
+    for name, t in kvlike:
+        want(name, t, (b, lk, hkv, d))
+    want("lse", lse, (b, hq, lq))
+    for name, t in ranges:
+        want(name, t, (b, hkv, lk))
+    want("block_state", state, block_state_shape(b, hkv, lq, lk))
+    return b, lq, lk, hq, hkv, d
+
+
 def dma_topk_mask(bias: torch.Tensor, k: int, mask_out: torch.Tensor, bias_out: torch.Tensor, stream=None) -> None:
     """Keep the k largest bias values of each row (last dimension): mask_out 1 there, and
     bias_out the bias there and the smallest bf16 elsewhere.  bias_out may be bias itself."""
     lk = bias.shape[-1]
     rows = bias.numel() // lk
+    for name, t in (("mask_out", mask_out), ("bias_out", bias_out)):
+        if tuple(t.shape) != tuple(bias.shape):
+            raise ValueError(f"dma_topk_mask: {name} must have the bias's shape {tuple(bias.shape)}")
     st = _lib.dma_topk_mask(_ptr(bias, "bias", torch.bfloat16), rows, lk, int(k),
                             _ptr(mask_out, "mask_out", torch.bfloat16), _ptr(bias_out, "bias_out", torch.bfloat16),
                             _stream(stream))
@@ -128,14 +159,18 @@ def dma_topk_mask(bias: torch.Tensor, k: int, mask_out: torch.Tensor, bias_out: 
 
 def dma_block_classify(mask: Optional[torch.Tensor], b: int, hkv: int, lq: int, lk: int, is_causal: bool,
                        block_state: torch.Tensor, stream=None) -> None:
+    if mask is not None and tuple(mask.shape) != (b, hkv, lq, lk):
+        raise ValueError(f"dma_block_classify: mask must have shape {(b, hkv, lq, lk)}, got {tuple(mask.shape)}")
+    if tuple(block_state.shape) != block_state_shape(b, hkv, lq, lk):
+        raise ValueError(f"dma_block_classify: block_state must have shape {block_state_shape(b, hkv, lq, lk)}")
     st = _lib.dma_block_classify(_ptr(mask, "mask", torch.bfloat16), b, hkv, lq, lk, int(bool(is_causal)),
                                  _ptr(block_state, "block_state", torch.uint8), _stream(stream))
     _check("dma_block_classify", st)
 
 
 def dma_attn_fwd(q, k, v, mask, bias, block_state, scale: float, is_causal: bool, o, lse, stream=None) -> None:
-    b, lq, hq, d = q.shape
-    lk, hkv = k.shape[1], k.shape[2]
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_fwd", q, k, v, planes=(("mask", mask), ("bias", bias)),
+                                    qlike=(("o", o),), lse=lse, state=block_state)
     st = _lib.dma_attn_fwd(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
                            _ptr(mask, "mask", torch.bfloat16), _ptr(bias, "bias", torch.bfloat16),
                            _ptr(block_state, "block_state", torch.uint8), b, lq, lk, hq, hkv, d, float(scale),
@@ -147,8 +182,8 @@ def dma_attn_fwd(q, k, v, mask, bias, block_state, scale: float, is_causal: bool
 def dma_attn_fwd_classify(q, k, v, mask, bias, scale: float, is_causal: bool, block_state, o, lse,
                           stream=None) -> None:
     """Forward that also writes the block classification (block_state is an output)."""
-    b, lq, hq, d = q.shape
-    lk, hkv = k.shape[1], k.shape[2]
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_fwd_classify", q, k, v, planes=(("mask", mask), ("bias", bias)),
+                                    qlike=(("o", o),), lse=lse, state=block_state)
     st = _lib.dma_attn_fwd_classify(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
                                     _ptr(v, "v", torch.bfloat16), _ptr(mask, "mask", torch.bfloat16),
                                     _ptr(bias, "bias", torch.bfloat16), b, lq, lk, hq, hkv, d, float(scale),
@@ -163,8 +198,9 @@ def dma_attn_bwd_workspace_size(b: int, lq: int, lk: int, hq: int, hkv: int, d: 
 
 def dma_attn_bwd(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq, dk, dv, dbias,
                  workspace, stream=None) -> None:
-    b, lq, hq, d = q.shape
-    lk, hkv = k.shape[1], k.shape[2]
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_bwd", q, k, v, planes=(("mask", mask), ("bias", bias), ("dbias", dbias)),
+                                    qlike=(("o", o), ("dout", dout), ("dq", dq)), kvlike=(("dk", dk), ("dv", dv)),
+                                    lse=lse, state=block_state)
     st = _lib.dma_attn_bwd(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16), _ptr(v, "v", torch.bfloat16),
                            _ptr(mask, "mask", torch.bfloat16), _ptr(bias, "bias", torch.bfloat16),
                            _ptr(block_state, "block_state", torch.uint8), _ptr(o, "o", torch.bfloat16),
@@ -179,6 +215,11 @@ def dma_attn_bwd(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, i
 def dma_block_classify_ranges(start_row, end_row, b: int, hkv: int, lq: int, lk: int, is_causal: bool, block_state,
                               stream=None) -> None:
     """Block classes from column ranges: key j of plane (b, g) attends rows start_row <= i < end_row."""
+    for name, t in (("start_row", start_row), ("end_row", end_row)):
+        if tuple(t.shape) != (b, hkv, lk):
+            raise ValueError(f"dma_block_classify_ranges: {name} must have shape {(b, hkv, lk)}")
+    if tuple(block_state.shape) != block_state_shape(b, hkv, lq, lk):
+        raise ValueError(f"dma_block_classify_ranges: block_state must have shape {block_state_shape(b, hkv, lq, lk)}")
     st = _lib.dma_block_classify_ranges(_ptr(start_row, "start_row", torch.int32), _ptr(end_row, "end_row", torch.int32),
                                         b, hkv, lq, lk, int(bool(is_causal)),
                                         _ptr(block_state, "block_state", torch.uint8), _stream(stream))
@@ -187,8 +228,9 @@ def dma_block_classify_ranges(start_row, end_row, b: int, hkv: int, lq: int, lk:
 
 def dma_attn_fwd_ranges(q, k, v, start_row, end_row, bias, block_state, scale: float, is_causal: bool, o, lse,
                         stream=None) -> None:
-    b, lq, hq, d = q.shape
-    lk, hkv = k.shape[1], k.shape[2]
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_fwd_ranges", q, k, v, planes=(("bias", bias),), qlike=(("o", o),),
+                                    lse=lse, ranges=(("start_row", start_row), ("end_row", end_row)),
+                                    state=block_state)
     st = _lib.dma_attn_fwd_ranges(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
                                   _ptr(v, "v", torch.bfloat16), _ptr(start_row, "start_row", torch.int32),
                                   _ptr(end_row, "end_row", torch.int32), _ptr(bias, "bias", torch.bfloat16),
@@ -200,8 +242,10 @@ def dma_attn_fwd_ranges(q, k, v, start_row, end_row, bias, block_state, scale: f
 
 def dma_attn_bwd_ranges(q, k, v, start_row, end_row, bias, block_state, o, dout, lse, scale: float, is_causal: bool,
                         dq, dk, dv, dbias, workspace, stream=None) -> None:
-    b, lq, hq, d = q.shape
-    lk, hkv = k.shape[1], k.shape[2]
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_bwd_ranges", q, k, v, planes=(("bias", bias), ("dbias", dbias)),
+                                    qlike=(("o", o), ("dout", dout), ("dq", dq)), kvlike=(("dk", dk), ("dv", dv)),
+                                    lse=lse, ranges=(("start_row", start_row), ("end_row", end_row)),
+                                    state=block_state)
     st = _lib.dma_attn_bwd_ranges(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
                                   _ptr(v, "v", torch.bfloat16), _ptr(start_row, "start_row", torch.int32),
                                   _ptr(end_row, "end_row", torch.int32), _ptr(bias, "bias", torch.bfloat16),
@@ -214,6 +258,12 @@ def dma_attn_bwd_ranges(q, k, v, start_row, end_row, bias, block_state, o, dout,
     _check("dma_attn_bwd_ranges", st)
 
 
+def _bits_size(fn: str, mask_bits, b, hkv, lq, lk):
+    need = dma_mask_bits_size(b, hkv, lq, lk)
+    if mask_bits.numel() * mask_bits.element_size() < need:
+        raise ValueError(f"{fn}: mask_bits must hold at least {need} bytes")
+
+
 def dma_mask_bits_size(b: int, hkv: int, lq: int, lk: int) -> int:
     """Bytes of the bit-packed PARTIAL-block mask: 512 per 64 x 64 block."""
     return int(_lib.dma_mask_bits_size(b, hkv, lq, lk))
@@ -222,6 +272,11 @@ def dma_mask_bits_size(b: int, hkv: int, lq: int, lk: int) -> int:
 def dma_block_classify_bits(mask, b: int, hkv: int, lq: int, lk: int, is_causal: bool, block_state, mask_bits,
                             stream=None) -> None:
     """dma_block_classify plus, in the same pass, the mask bits of every PARTIAL block."""
+    if mask is not None and tuple(mask.shape) != (b, hkv, lq, lk):
+        raise ValueError(f"dma_block_classify_bits: mask must have shape {(b, hkv, lq, lk)}")
+    if tuple(block_state.shape) != block_state_shape(b, hkv, lq, lk):
+        raise ValueError(f"dma_block_classify_bits: block_state must have shape {block_state_shape(b, hkv, lq, lk)}")
+    _bits_size("dma_block_classify_bits", mask_bits, b, hkv, lq, lk)
     st = _lib.dma_block_classify_bits(_ptr(mask, "mask", torch.bfloat16), b, hkv, lq, lk, int(bool(is_causal)),
                                       _ptr(block_state, "block_state", torch.uint8),
                                       _ptr(mask_bits, "mask_bits", torch.uint8), _stream(stream))
@@ -230,8 +285,9 @@ def dma_block_classify_bits(mask, b: int, hkv: int, lq: int, lk: int, is_causal:
 
 def dma_attn_fwd_bits(q, k, v, mask_bits, bias, block_state, scale: float, is_causal: bool, o, lse,
                       stream=None) -> None:
-    b, lq, hq, d = q.shape
-    lk, hkv = k.shape[1], k.shape[2]
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_fwd_bits", q, k, v, planes=(("bias", bias),), qlike=(("o", o),),
+                                    lse=lse, state=block_state)
+    _bits_size("dma_attn_fwd_bits", mask_bits, b, hkv, lq, lk)
     st = _lib.dma_attn_fwd_bits(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
                                 _ptr(v, "v", torch.bfloat16), _ptr(mask_bits, "mask_bits", torch.uint8),
                                 _ptr(bias, "bias", torch.bfloat16), _ptr(block_state, "block_state", torch.uint8), b,
@@ -242,8 +298,10 @@ def dma_attn_fwd_bits(q, k, v, mask_bits, bias, block_state, scale: float, is_ca
 
 def dma_attn_bwd_bits(q, k, v, mask_bits, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq, dk, dv,
                       dbias, workspace, stream=None) -> None:
-    b, lq, hq, d = q.shape
-    lk, hkv = k.shape[1], k.shape[2]
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_bwd_bits", q, k, v, planes=(("bias", bias), ("dbias", dbias)),
+                                    qlike=(("o", o), ("dout", dout), ("dq", dq)), kvlike=(("dk", dk), ("dv", dv)),
+                                    lse=lse, state=block_state)
+    _bits_size("dma_attn_bwd_bits", mask_bits, b, hkv, lq, lk)
     st = _lib.dma_attn_bwd_bits(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
                                 _ptr(v, "v", torch.bfloat16), _ptr(mask_bits, "mask_bits", torch.uint8),
                                 _ptr(bias, "bias", torch.bfloat16), _ptr(block_state, "block_state", torch.uint8),

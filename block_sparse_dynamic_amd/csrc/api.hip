@@ -37,12 +37,28 @@ int check_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const ui
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DMA_OK : DMA_ERR_HIP; }
 
+// Longest query or key length the attention kernels take: their per-thread offsets inside a
+// tile row range (64 rows of lk bf16 values) are 32-bit.
+constexpr int64_t kMaxLen = int64_t(1) << 24;
+
+// |scale| in [2^-100, 2^100]: the kernels carry scores as q.k + bias / |scale| with the bias
+// clamped to +-2^12 and fold |scale| log2(e) into one product, all of which stay finite there.
+bool scale_in_range(float scale) {
+  const float a = std::fabs(scale);
+  return a >= 0x1p-100f && a <= 0x1p100f;
+}
+
 }  // namespace
 
 extern "C" {
 
+// The block of the skip decisions (Flash-DMA README, key design: a block's mask is OR-reduced
+// to decide whether it is computed; FlashMask README, Key Features: fully / partially /
+// unmasked blocks).  The pages leave its size to the kernel; this library fixes 64 x 64.
 int dma_block_size(void) { return dma::kBlock; }
 
+// Text of the status codes of this C ABI (the pages define no error interface; the Python
+// binding raises with this text).
 const char* dma_status_string(int status) {
   switch (status) {
     case DMA_OK:
@@ -50,7 +66,8 @@ const char* dma_status_string(int status) {
     case DMA_ERR_INVALID_ARGUMENT:
       return "invalid argument";
     case DMA_ERR_UNSUPPORTED:
-      return "unsupported configuration (d must be 64 or 128, hq/hkv in {1,2,4,8,16})";
+      return "unsupported configuration (d must be 64 or 128, hq/hkv in {1,2,4,8,16}, lq and lk at most 2^24, "
+             "|scale| in [2^-100, 2^100])";
     case DMA_ERR_WORKSPACE_TOO_SMALL:
       return "workspace too small";
     case DMA_ERR_HIP:
@@ -102,6 +119,9 @@ int attn_fwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   if (!o || !lse || !aligned16(o) || !aligned16(lse)) return DMA_ERR_INVALID_ARGUMENT;
   // the scores are carried as q.k + bias / |scale|: scale must be finite and nonzero
   if (!(scale != 0.f) || !std::isfinite(scale)) return DMA_ERR_INVALID_ARGUMENT;
+  if (!scale_in_range(scale)) return DMA_ERR_UNSUPPORTED;
+  // per-thread byte offsets of the bias and mask tiles inside a 64 x 64 block are 32-bit
+  if (lk > kMaxLen || lq > kMaxLen) return DMA_ERR_UNSUPPORTED;
   dma::AttnArgs a = {};
   a.q = q;
   a.k = k;
@@ -226,8 +246,9 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   if (dbias && lk % 8 != 0) return DMA_ERR_INVALID_ARGUMENT;
   // the scores are carried as S + bias / scale: scale must be finite and nonzero
   if (!(scale != 0.f) || !std::isfinite(scale)) return DMA_ERR_INVALID_ARGUMENT;
+  if (!scale_in_range(scale)) return DMA_ERR_UNSUPPORTED;
   // per-row byte ranges of dbias and row indices must stay within 32-bit offsets
-  if (lk > (int64_t(1) << 24) || lq > (int64_t(1) << 24)) return DMA_ERR_UNSUPPORTED;
+  if (lk > kMaxLen || lq > kMaxLen) return DMA_ERR_UNSUPPORTED;
   const WsLayout wl = ws_layout(b, lq, lk, hq, hkv, d, is_causal);
   if (workspace_bytes < wl.total) return DMA_ERR_WORKSPACE_TOO_SMALL;
   dma::AttnArgs a = {};

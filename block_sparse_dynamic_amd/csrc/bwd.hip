@@ -325,7 +325,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     for (int t = tid; t < 2 * kStateChunk; t += 256) {
       const int hf = t / kStateChunk, j = t % kStateChunk, qb = lo + j;
       uint8_t v = kSkip;
-      if (qb <= qb_hi && (hf == 0 || has_kb1)) v = st_col[(int64_t)qb * p.nkb + hf];
+      // A pair that causality leaves no valid position for this query block (KB at or past its
+      // live pairs) owns no dS slot: it is SKIP whatever the bitmap says, so a bitmap classified
+      // without causality cannot send a dS store past the block's slots.
+      if (qb <= qb_hi && (hf == 0 || has_kb1) && KB < live_pairs(qb, p.lq, p.lk, p.causal))
+        v = st_col[(int64_t)qb * p.nkb + hf];
       sm.st[hf][j] = v;
       if (hf == 0 && qb <= qb_hi) sm.pb[j] = p.pair_base[qb];
     }
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
               const int r = gi * 8 + hi * 4 + e;
               v = rm != 0u && ((mrow[r * 2] >> l32) & 1u) != 0;
             }
-            iv[e] = v ? __uint_as_float((uint32_t)(uint16_t)xb[e] << 16) * inv_scale : neg_inf_s;
+            iv[e] = v ? clamp_bias(__uint_as_float((uint32_t)(uint16_t)xb[e] << 16)) * inv_scale : neg_inf_s;
           }
           sm.beff[wave][gi][lane] = iv;
         }

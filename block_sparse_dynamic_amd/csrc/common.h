@@ -17,8 +17,6 @@ constexpr int kBitsPerBlock = kBlock * kBlock / 8;  // bytes of one block's bits
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -42,6 +40,19 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ bool attends_lo(uint32_t w) { return (w & 0x7FFFu) != 0; }
 __device__ __forceinline__ bool attends_hi(uint32_t w) { return (w & 0x7FFF0000u) != 0; }
 
+// Bias values at valid positions are clamped to [-kBiasClamp, kBiasClamp] before use, in the
+// forward and the backward alike.  Scores are fp32, so a score of magnitude M carries a rounding
+// of about M 2^-24 (M 2^-24 / |scale| in the units the kernels carry it in), and the fp32
+// log-sum-exp handed from the forward to the backward has a spacing of M 2^-23.  At 2^12 these
+// cost O at most about 1e-3 of the output tolerance and the backward's P = exp(S - lse) about
+// 1e-3 relative; at the smallest bf16 that the pages' recipe writes into masked bias entries
+// (-3.39e38, which a caller may pass without the mask) nothing of the q.k term or of the
+// normaliser would be left.  A clamped entry still weighs exp(-2^12) = 0 against every
+// unclamped score of its row, and equal entries stay equal, so only a row whose valid keys all
+// carry distinct biases beyond the clamp is changed (its weights no longer favour the larger).
+constexpr float kBiasClamp = 4096.f;
+__device__ __forceinline__ float clamp_bias(float b) { return __builtin_amdgcn_fmed3f(b, -kBiasClamp, kBiasClamp); }
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = static_cast<__bf16>(f);
@@ -53,13 +64,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2 h = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, h);
 }
-// Two fp32 values -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const f16x2 h = {(_Float16)lo, (_Float16)hi};
-  return __builtin_bit_cast(uint32_t, h);
-}
-// A bf16 pair -> the same two values as an fp16 pair (exact for |x| in [2^-14, 65504]).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return pack_f16x2(bf16_lo(w), bf16_hi(w)); }
 
 // LDS tile layouts.  A [rows][D] bf16 tile stores the 16-byte chunk c of row r at chunk
 // c ^ tile_xor<D>(r), rows unpadded.  For D = 128 the XOR is 4*(r%4) + (r/4)%4: a 128-bit
@@ -134,9 +138,6 @@ __device__ __forceinline__ bf16x8 join_bf16x8(i16x4 a, i16x4 b) {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma32_f16(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -13,10 +13,11 @@
 // wavefront owns 32 query rows of one head.
 //
 // Per key block (64 keys):
-//   1. the workgroup copies K and V (row-major, [key][d]) and the *effective*
-//      bias into LDS.  The effective bias is bias / |scale| in fp32 where the
-//      position is valid and -inf elsewhere: mask, causality and the ragged
-//      matrix edge are folded in once here for all HC heads.  The tiles of
+//   1. the workgroup copies K and V (row-major, [key][d], bf16 as loaded) and
+//      the *effective* bias into LDS.  The effective bias is bias / |scale| in
+//      fp32 where the position is valid and -inf elsewhere: mask, causality and
+//      the ragged matrix edge are folded in once here for all HC heads.  The
+//      bias is first clamped to [-2^12, 2^12] (see kBiasClamp).  The tiles of
 //      the next non-SKIP block are loaded into registers meanwhile, by buffer
 //      loads whose per-thread offsets are fixed for the kernel (the block's
 //      corner and its valid extent go into the buffer resource, so keys past
@@ -32,11 +33,13 @@
 //      maximum (and with it the running output) moves only when a row maximum
 //      exceeds it by more than 2^8 in weight, so weights stay in [0, 256] and
 //      the rescale runs rarely (the wave skips it when no row needs it).
-//   4. O^T += V^T P^T on v_mfma_f32_32x32x16_f16: P^T goes from the accumulator
-//      registers straight into the B operand as fp16 (the key order inside a
-//      k-step only has to agree between A and B); V^T comes out of the
-//      row-major V tile, staged in fp16 (bf16 values convert exactly for
-//      magnitudes in [2^-14, 65504]), by ds_read_b64_tr_b16.
+//   4. O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, with V in bf16 exactly as
+//      given and the weights P split into two bf16 parts, P = P_hi + P_lo
+//      (P_hi = P truncated to bf16, P_lo = the remainder rounded to bf16): two
+//      products per k-step give P to about 16 significant bits over the whole
+//      bf16 range of V.  P^T goes from the accumulator registers straight into
+//      the B operand (the key order inside a k-step only has to agree between
+//      A and B); V^T comes out of the row-major V tile by ds_read_b64_tr_b16.
 #include <math.h>
 
 #include "common.h"
@@ -254,10 +257,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       const int r = task / (D / 8), c = task % (D / 8);
       // rows past lk were loaded as zeros
       *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = pk[n];
-      u32x4 vh;  // V in fp16 for the P V product
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vh[e] = bf16x2_to_f16x2(pv[n][e]);
-      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = vh;
+      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = pv[n];
     }
     bool any_v = false, all_v = true;  // fused classification: this thread's positions of the block
     {
@@ -303,8 +303,8 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
             any_v = any_v || v0 || v1;
             all_v = all_v && v0 && v1;
           }
-          const float lo = v0 ? bf16_lo(bw[e]) * inv_as : -INFINITY;
-          const float hi16 = v1 ? bf16_hi(bw[e]) * inv_as : -INFINITY;
+          const float lo = v0 ? clamp_bias(bf16_lo(bw[e])) * inv_as : -INFINITY;
+          const float hi16 = v1 ? clamp_bias(bf16_hi(bw[e])) * inv_as : -INFINITY;
           if (e < 2) {
             y0[2 * e] = lo;
             y0[2 * e + 1] = hi16;
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     // ---- online softmax ----------------------------------------------------------
     // The reference maximum moves only when a row's maximum exceeds it by more than
     // kRescaleMargin (8 in log2 units): below that the weights exp(x - m_ref) stay under 256,
-    // which fp32 sums and fp16 P hold without loss, and the rescale of the accumulators
+    // which fp32 sums and the two-part bf16 P hold without loss, and the rescale of the accumulators
     // (64 multiplies per lane) runs a few times per row instead of on most key blocks.
     if (__any(mx > m_ref + kRescaleMargin)) {
       const float m_new = fmaxf(m_ref, mx);
@@ -399,25 +399,32 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         rs += pv;
       }
     l_part += rs;
-    // ---- O^T += V^T P^T -------------------------------------------------------
-    // P and V enter in fp16 (V converted exactly when staged): P in [0, 1] keeps 11
-    // significant bits, against 8 in bf16, whose rounding (2^-9 relative) could move O by more
-    // than the 1e-2 the output tolerance leaves after bf16 storage.
+    // ---- O^T += V^T P_hi^T + V^T P_lo^T ------------------------------------------------
+    // P in [0, 256] as two bf16 parts: P_hi keeps the upper half of each fp32 weight
+    // (truncation, one byte permute per pair), P_lo = P - P_hi rounded to bf16, so P_hi + P_lo
+    // is within 2^-15 of P.  A single bf16 P (relative rounding 2^-8) would move O by more than
+    // the 1e-2 the output tolerance leaves after bf16 storage of O.
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        u32x4 pw;
+        u32x4 ph, pl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pw[e] = pack_f16x2(sacc[kt][hh * 8 + 2 * e], sacc[kt][hh * 8 + 2 * e + 1]);
-        const f16x8 ph = __builtin_bit_cast(f16x8, pw);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t a = __float_as_uint(sacc[kt][hh * 8 + 2 * e]), b = __float_as_uint(sacc[kt][hh * 8 + 2 * e + 1]);
+          ph[e] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // upper halves of a (low) and b (high)
+          pl[e] = pack_bf16x2(__uint_as_float(a) - __uint_as_float(a & 0xFFFF0000u),
+                              __uint_as_float(b) - __uint_as_float(b & 0xFFFF0000u));
+        }
+        const bf16x8 bh = __builtin_bit_cast(bf16x8, ph), bl = __builtin_bit_cast(bf16x8, pl);
         const int rbase = (kt * 32 + hh * 16) * KR;  // rows of this k-step, a compile-time offset
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const i16x4 a0 = lds_read_tr16(&sm.v[voff0[dt] + rbase]);
           const i16x4 a1 = lds_read_tr16(&sm.v[voff1[dt] + rbase]);
-          const f16x8 av = __builtin_bit_cast(f16x8, join_bf16x8(a0, a1));
-          oacc[dt] = mfma32_f16(av, ph, oacc[dt]);
+          const bf16x8 av = join_bf16x8(a0, a1);
+          oacc[dt] = mfma32(av, bh, oacc[dt]);
+          oacc[dt] = mfma32(av, bl, oacc[dt]);
         }
       }
     }

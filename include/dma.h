@@ -60,10 +60,15 @@ enum {
 
 enum { DMA_BLOCK_SKIP = 0, DMA_BLOCK_PARTIAL = 1, DMA_BLOCK_FULL = 2 };
 
-/* Side of the square classification block: 64 (query rows = key columns). */
+/* Side of the square classification block: 64 (query rows = key columns).  The
+ * block is the unit of the skip decision (Flash-DMA README, key design: a
+ * block's mask is OR-reduced to decide whether it is computed; FlashMask
+ * README, Key Features: fully / partially / unmasked blocks); the pages leave
+ * its size to the kernel. */
 int dma_block_size(void);
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL).  The pages define no error
+ * interface; this is the library's own, and the Python binding raises with it. */
 const char* dma_status_string(int status);
 
 /*
@@ -89,21 +94,36 @@ int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq,
  * valid scores scaled, bias added; softmax; times V).
  *
  *   q           bf16 [b, lq, hq, d]
- *   k, v        bf16 [b, lk, hkv, d]; the P V product takes v in fp16, exact
- *               for magnitudes in [2^-14, 65504] (larger ones saturate there)
+ *   k, v        bf16 [b, lk, hkv, d]; v enters the P V product in bf16 as
+ *               given (the weights P as two bf16 parts, about 16 significant
+ *               bits), so every finite bf16 value of v is taken exactly
  *   mask, bias  bf16 [b, hkv, lq, lk]; either may be NULL (no mask: every key
  *               attends; no bias: zero).  bias entries at masked positions
  *               are never read into the result (they may hold NaN or inf).
+ *               Bias values at valid positions are clamped to [-4096, 4096]
+ *               (fp32 scores and log-sum-exp resolve the softmax only up to
+ *               such magnitudes); a clamped entry still weighs exp(-4096) = 0
+ *               against any unclamped score of its row, so only a row whose
+ *               valid keys all hold distinct biases beyond the clamp differs
+ *               from the unclamped formula.  The bf16 minimum that the
+ *               Flash-DMA README's recipe writes at masked entries is thus
+ *               safe to pass without the mask.
  *   block_state from dma_block_classify with the same mask, sizes and is_causal
- *   scale       multiplies q.k (callers usually pass 1/sqrt(d))
+ *   scale       multiplies q.k (callers usually pass 1/sqrt(d)); |scale| in
+ *               [2^-100, 2^100]
  *   o           out, bf16 [b, lq, hq, d]
  *   lse         out, fp32 [b, hq, lq]: natural log of the softmax denominator
  *               including the row maximum, +inf for rows with no valid key
- * Supported: d in {64, 128}; hq % hkv == 0 with hq / hkv in {1, 2, 4, 8, 16}.
+ * Supported: d in {64, 128}; hq % hkv == 0 with hq / hkv in {1, 2, 4, 8, 16};
+ * lq, lk <= 2^24.
  * Errors: DMA_ERR_INVALID_ARGUMENT (NULL q/k/v/o/lse/block_state, sizes < 1,
  * misalignment, lk % 8 != 0 with mask or bias, a scale that is zero or not
  * finite: the kernel carries scores as q.k + bias / |scale|),
- * DMA_ERR_UNSUPPORTED (d, group).
+ * DMA_ERR_UNSUPPORTED (d, group, lq or lk above 2^24: 32-bit offsets inside a
+ * tile row range; |scale| outside [2^-100, 2^100]).
+ * The block_state must come from dma_block_classify with the same mask, sizes
+ * and is_causal: a bitmap that marks blocks FULL which the call's causality
+ * cuts gives wrong results (never an access outside the buffers).
  */
 int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
                  const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
@@ -158,10 +178,9 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq
  *               NULL: then the bias gradient is not produced.
  *   workspace   device scratch of at least dma_attn_bwd_workspace_size() bytes,
  *               16-byte aligned, owned by the caller, contents on entry ignored
- * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL,
- *   DMA_ERR_INVALID_ARGUMENT for a scale that is zero or not finite (the kernel
- *   carries scores as q.k + bias / scale), and DMA_ERR_UNSUPPORTED for lq or lk
- *   above 2^24 (32-bit row offsets).
+ * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL.  A key pair that
+ *   the call's causality leaves no valid position for a query block is taken as
+ *   SKIP whatever block_state says (such a pair owns no dS slot).
  * dq is deterministic: the same inputs give bit-identical outputs.
  */
 int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,

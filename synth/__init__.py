@@ -129,6 +129,7 @@ class Case:
     doc_max: int = 8192
     seed: int = 0
     scale: Optional[float] = None  # None: fp32(1/sqrt(d))
+    v_std: float = 1.0  # standard deviation of V
 
     @property
     def G(self) -> int:
@@ -174,7 +175,8 @@ def k(c: Case) -> np.ndarray:
 
 
 def v(c: Case) -> np.ndarray:
-    return dense(c, TAG_V, (c.b, c.lk, c.hkv, c.d)).reshape(c.b, c.lk, c.hkv, c.d)
+    n = c.b * c.lk * c.hkv * c.d
+    return normal_bf16(_tensor_key(c, TAG_V), 0, n, std=c.v_std).reshape(c.b, c.lk, c.hkv, c.d)
 
 
 def do(c: Case) -> np.ndarray:

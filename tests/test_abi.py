@@ -269,3 +269,63 @@ def test_bits_reject(lib):
     assert g(*bargs[:3], None, *bargs[4:]) == INVALID
     assert g(*bargs[:14], 80, *bargs[15:]) == UNSUPPORTED
     assert g(*bargs[:15], 0.0, *bargs[16:]) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(lk=(1 << 24) + 64), dict(lq=(1 << 24) + 64)])
+def test_fwd_rejects_lengths_past_32bit_tile_offsets(lib, kw):
+    # the forward's per-thread offsets inside a tile row range are 32-bit, as the backward's
+    assert fwd(lib, **kw) == UNSUPPORTED
+    assert fwd_cls(lib, **kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("scale", [1e-31, -1e-31, 1e31, -1e31])
+def test_scale_outside_supported_range(lib, scale):
+    # |scale| must lie in [2^-100, 2^100]: bias / |scale| and |scale| log2(e) stay finite
+    assert fwd(lib, scale=scale) == UNSUPPORTED
+    assert bwd(lib, scale=scale) == UNSUPPORTED
+    assert fwd(lib, scale=2.0 ** -100, d=96) == UNSUPPORTED  # in range: validation goes on to d
+    assert fwd(lib, scale=2.0 ** 100, d=96) == UNSUPPORTED
+
+
+def _cpu_bf16(*shape):
+    import torch
+
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("what", ["bias_broadcast", "mask_broadcast", "v_shape", "dbias_shape", "lse_shape",
+                                  "state_shape", "dq_shape"])
+def test_binding_rejects_mismatched_shapes(what):
+    """The binding hands plain pointers to the library, so every tensor must have exactly the
+    shape the kernels read or write through it; a broadcast [b, 1, lq, lk] bias, or a v whose
+    shape differs from k's, is refused before any call (no GPU is touched)."""
+    import torch
+
+    import block_sparse_dynamic_amd as dma
+
+    b, lq, lk, hq, hkv, d = 1, 128, 128, 4, 2, 64
+    q, k, v = _cpu_bf16(b, lq, hq, d), _cpu_bf16(b, lk, hkv, d), _cpu_bf16(b, lk, hkv, d)
+    mask, bias = _cpu_bf16(b, hkv, lq, lk), _cpu_bf16(b, hkv, lq, lk)
+    st = torch.zeros(dma.block_state_shape(b, hkv, lq, lk), dtype=torch.uint8)
+    o, lse = _cpu_bf16(b, lq, hq, d), torch.zeros((b, hq, lq), dtype=torch.float32)
+    dq, dk, dv, db = _cpu_bf16(b, lq, hq, d), _cpu_bf16(b, lk, hkv, d), _cpu_bf16(b, lk, hkv, d), _cpu_bf16(b, hkv, lq, lk)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    if what == "bias_broadcast":
+        bias = _cpu_bf16(b, 1, lq, lk)
+    elif what == "mask_broadcast":
+        mask = _cpu_bf16(b, 1, lq, lk)
+    elif what == "v_shape":
+        v = _cpu_bf16(b, lk, hkv, d // 2)
+    elif what == "dbias_shape":
+        db = _cpu_bf16(b, 1, lq, lk)
+    elif what == "lse_shape":
+        lse = torch.zeros((b, lq, hq), dtype=torch.float32)
+    elif what == "state_shape":
+        st = torch.zeros((b, hkv, 1, 1), dtype=torch.uint8)
+    elif what == "dq_shape":
+        dq = _cpu_bf16(b, lq, hq, d + 8)
+    with pytest.raises(ValueError):
+        if what in ("dbias_shape", "dq_shape"):
+            dma.dma_attn_bwd(q, k, v, mask, bias, st, o, o, lse, 0.125, True, dq, dk, dv, db, ws)
+        else:
+            dma.dma_attn_fwd(q, k, v, mask, bias, st, 0.125, True, o, lse)

@@ -1,7 +1,8 @@
 """Bit-packed PARTIAL-block mask (dma_*_bits): the classification writes, for every PARTIAL
 block, exactly the packed form of the mask (the oracle's attends(), one bit per element, zero
 past lq and lk), leaves every other block's bytes untouched, and the attention passes that read
-those bits return the dense entry points' results bit for bit.
+those bits return the dense entry points' results bit for bit; those outputs are compared with
+the fp64 oracle as well (the tolerances of gpu_harness).
 
 Cases: ragged sizes, lq < lk and lq > lk (rows without keys), head dims 64 and 128, group sizes
 1..8, block/top-k/document/all-ones masks, causal and not, a mask without a bias; at full size
@@ -62,6 +63,8 @@ def run_both(c: Case):
                           dbias, ws)
     torch.cuda.synchronize()
     out = [H.bits(t) for t in (o, dq, dk, dv, dbias)] + [lse.cpu().numpy()]
+    H.compare_with_oracle(f"{c.name} (bits)", c, dc.q_h, dc.k_h, dc.v_h, dc.mask_h, dc.bias_h, dc.do_h, o, lse, dq,
+                          dk, dv, dbias)
     return dc, st_b.cpu().numpy(), mb.cpu().numpy(), dense, out
 
 
@@ -93,6 +96,16 @@ def test_bits_equal_packed_mask_and_dense_results(c):
     print(c.name, "PARTIAL blocks:", int(part.sum()), "of", part.size, flush=True)
     for name, a, b in zip(("o", "dq", "dk", "dv", "dbias", "lse"), dense, out):
         assert np.array_equal(a, b), f"{c.name}: {name} differs between the bit and the dense path"
+
+
+@pytest.mark.timeout(1200)
+def test_headline_full_size_oracle():
+    """The Top-k headline workload at full size through the bit entry points, against the
+    oracle: whole bitmap, 64 sampled query blocks of O / LSE / dQ / dBias, sampled-row dK / dV."""
+    import gpu_harness as H
+
+    H.check_full_case(synth.CASES["headline"], n_blocks=64, path="bits")
+    torch.cuda.empty_cache()
 
 
 def test_headline_full_size_equal_dense():

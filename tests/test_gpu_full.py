@@ -25,3 +25,12 @@ def test_full_size_sampled_parity(name):
 
     H.check_full_case(synth.CASES[name], n_blocks=64)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(1200)
+def test_headline_fused_classify_sampled_parity():
+    """The timed step's forward (classification fused in) at the Headline workload, against the oracle."""
+    import gpu_harness as H
+
+    H.check_full_case(synth.CASES["headline"], n_blocks=64, path="fused")
+    torch.cuda.empty_cache()

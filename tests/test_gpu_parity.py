@@ -3,7 +3,11 @@
 Cases span several 64x64 tiles with ragged tails, all three block classes, NULL
 mask and bias, lq != lk (bottom-right causal alignment, rows with no valid key),
 group sizes 1..16, head dims 64 and 128, NaN stored in masked bias entries, and a
-negative and a large scale.
+negative and a large scale.  The value range: the pages' top-k-filled bias passed
+without its mask (valid keys holding the smallest bf16, rows whose every valid key
+holds it), the largest and smallest bf16 as bias at valid positions, large but
+unclamped biases, V of standard deviation 1e-6 and 1e4, and V beyond the fp16 range
+at keys that are masked for some rows of a PARTIAL block.
 """
 import numpy as np
 import pytest
@@ -179,3 +183,107 @@ def test_memory_after_inputs_is_never_read():
     got = [H.bits(t) for t in (dc.o, dc.dq, dc.dk, dc.dv, dc.dbias)] + [dc.lse.cpu().numpy()]
     for name, a, b in zip(("o", "dq", "dk", "dv", "dbias", "lse"), ref, got):
         assert np.array_equal(a, b), f"{name} changed"
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bits, round to nearest even through fp32 (test input construction only)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _valid(dc):
+    c = dc.c
+    v = np.ones((c.b, c.hkv, c.lq, c.lk), bool) if dc.mask_h is None else oracle.attends(dc.mask_h)
+    if c.causal:
+        v &= np.arange(c.lk)[None, :] <= np.arange(c.lq)[:, None] + c.lk - c.lq
+    return v
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_topk_filled_bias_without_mask(d):
+    """The Flash-DMA README recipe's bias (top-k kept, the smallest bf16 elsewhere) passed with
+    attn_mask=None: every causal key is valid, the filled ones with a score of about -3.4e38.
+    Early causal rows have only filled keys, or one of them."""
+    import gpu_harness as H
+
+    c = Case(f"topk_fill_nomask_d{d}", 30 + d // 64, 1, 320, 320, 4, 2, d, True, "topk", 48)
+
+    def prep(dc):
+        assert (dc.bias_h == 0xFF7F).any()
+        dc.mask_h = None
+
+    dc, _ = H.check_small_case(c, prepare=prep)
+    lse = dc.lse.cpu().numpy()
+    assert np.all(np.isfinite(lse)), "every causal row has a valid key without a mask"
+
+
+def test_extreme_bias_values_with_mask():
+    """+-largest bf16 at valid positions (single-valued per sign within a row), and rows whose
+    every valid key holds the smallest bf16."""
+    import gpu_harness as H
+
+    c = Case("extreme_bias", 33, 1, 256, 256, 4, 2, 128, True, "blocks")
+
+    def prep(dc):
+        rng = np.random.default_rng(33)
+        b = dc.bias_h.copy()
+        valid = _valid(dc)
+        pick = rng.random(b.shape)
+        b[valid & (pick < 0.02)] = 0x7F7F  # +3.39e38
+        b[valid & (pick > 0.97)] = 0xFF7F  # -3.39e38
+        b[0, 1, 130:150, :] = 0xFF7F  # whole rows at the smallest bf16
+        dc.bias_h = b
+
+    H.check_small_case(c, prepare=prep)
+
+
+def test_large_unclamped_bias():
+    """Biases around -3000 (inside the clamp): scores far from zero, every term kept."""
+    import gpu_harness as H
+
+    c = Case("large_bias", 34, 1, 256, 256, 4, 2, 128, True, "topk", 64)
+
+    def prep(dc):
+        f = oracle.bf16_to_f64(dc.bias_h)
+        f = np.where(f > -1e30, f - 3000.0, f)
+        dc.bias_h = _bf16_bits(f)
+
+    H.check_small_case(c, prepare=prep)
+
+
+@pytest.mark.parametrize("v_std", [1e-6, 1e4])
+def test_v_magnitudes(v_std):
+    """V far below and far above 1: the P V product keeps bf16 V exactly (no fp16 range)."""
+    import gpu_harness as H
+
+    c = Case(f"v_std_{v_std:g}", 35, 1, 256, 256, 4, 2, 128, True, "blocks", v_std=v_std)
+    H.check_small_case(c)
+
+
+def test_v_beyond_fp16_range_at_masked_keys():
+    """V rows of 7e4 and -1e5 (beyond the fp16 range) at keys whose mask column is zero for every
+    row, inside key blocks that stay PARTIAL: those keys meet a zero weight in every product, and
+    0 * V must stay 0 (an fp16 copy of V would hold inf there and turn the rows to NaN)."""
+    import gpu_harness as H
+
+    c = Case("v_spikes", 36, 1, 256, 256, 4, 2, 128, True, "blocks")
+
+    def prep(dc):
+        st = oracle.classify(dc.mask_h, c.b, c.hkv, c.lq, c.lk, c.causal)
+        m, v = dc.mask_h.copy(), dc.v_h.copy()
+        n = 0
+        for kb in range(st.shape[3]):
+            # a key block PARTIAL for some query block in both planes (K and V rows are shared by
+            # the query heads of a plane only, so both planes' masks lose the column)
+            if not all((st[0, g, :, kb] == oracle.PARTIAL).any() for g in range(c.hkv)):
+                continue
+            for j, val in ((kb * 64 + 5, 7.0e4), (kb * 64 + 40, -1.0e5)):
+                m[0, :, :, j] = 0
+                v[0, j, :, :] = _bf16_bits(np.full((c.hkv, c.d), val))
+                n += 1
+        assert n >= 4
+        dc.mask_h, dc.v_h = m, v
+
+    dc, _ = H.check_small_case(c, prepare=prep)
+    st = dc.state.cpu().numpy()
+    assert (st == oracle.PARTIAL).any()

@@ -1,5 +1,6 @@
-"""Column-range mask input (dma_*_ranges): every result equals the dense entry point's on the
-expanded mask, bit for bit, and the bitmap equals the oracle's classification of that mask.
+"""Column-range mask input (dma_*_ranges): every output is compared with the fp64 oracle on the
+expanded mask (the tolerances of gpu_harness), equals the dense entry point's on that mask bit
+for bit, and the bitmap equals the oracle's classification of that mask.
 
 Ranges: random intervals per key column (empty ones, and bounds below 0 and past lq included),
 document-packed intervals ([j, end of j's document), the pages' column-wise form), causal and
@@ -30,12 +31,9 @@ def random_ranges(rng, c):
 
 
 def doc_ranges(c):
-    bounds = synth.doc_bounds(c)
-    j = np.arange(c.lk)
-    end = bounds[np.searchsorted(bounds, j, side="right")]
-    s = np.broadcast_to(j, (c.b, c.hkv, c.lk)).astype(np.int32)
-    e = np.broadcast_to(end, (c.b, c.hkv, c.lk)).astype(np.int32)
-    return np.ascontiguousarray(s), np.ascontiguousarray(e)
+    import gpu_harness as H
+
+    return H.doc_ranges(c)
 
 
 def expand(s, e, lq):
@@ -70,6 +68,9 @@ def run_both(c, s, e):
                             dbias, ws)
     torch.cuda.synchronize()
     rng_out = [H.bits(t) for t in (o, dq, dk, dv, dbias)] + [lse.cpu().numpy()]
+    # the range path's own outputs against the oracle on the expanded mask
+    H.compare_with_oracle(f"{c.name} (ranges)", c, dc.q_h, dc.k_h, dc.v_h, mask_h, dc.bias_h, dc.do_h, o, lse, dq, dk,
+                          dv, dbias)
     return dc, mask_h, st_r.cpu().numpy(), dense, rng_out
 
 
@@ -105,8 +106,16 @@ def test_doc_ranges_equal_dense_and_oracle():
     assert np.array_equal(st_r, st_ref)
     for name, a, b in zip(("o", "dq", "dk", "dv", "dbias", "lse"), dense, rng_out):
         assert np.array_equal(a, b), f"{name} differs between the range and the dense path"
-    o_ref, lse_ref = oracle.forward(dc.q_h, dc.k_h, dc.v_h, mask_h, dc.bias_h, c.scale_f32, c.causal)
-    H.check_o(oracle.bf16_to_f64(rng_out[0].reshape(dc.q_h.shape)), o_ref)
+
+
+@pytest.mark.timeout(1200)
+def test_doc_packed_full_size_oracle():
+    """The Doc-packed workload at full size through the range entry points, against the oracle:
+    whole bitmap, 64 sampled query blocks of O / LSE / dQ / dBias, sampled-row dK / dV."""
+    import gpu_harness as H
+
+    H.check_full_case(synth.CASES["docpacked"], n_blocks=64, path="ranges")
+    torch.cuda.empty_cache()
 
 
 def test_doc_packed_full_size_equal_dense():
