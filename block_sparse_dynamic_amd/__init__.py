@@ -69,6 +69,10 @@ _lib.dma_attn_fwd_bits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i6
 _lib.dma_attn_bwd_bits.restype = _i32
 _lib.dma_attn_bwd_bits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                    _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dma_attn_bwd_noalloc.restype = _i32
+_lib.dma_attn_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                      _f32, _i32, _vp, _vp, _vp, _vp, _vp]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DMA_NOALLOC_SCRATCH_BYTES of include/dma.h
 _lib.dma_topk_mask.restype = _i32
 _lib.dma_topk_mask.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
 
@@ -210,6 +214,25 @@ def dma_attn_bwd(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, i
                            _ptr(dbias, "dbias", torch.bfloat16), _ptr(workspace, "workspace"),
                            workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dma_attn_bwd", st)
+
+
+def dma_attn_bwd_noalloc(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq, dk, dv,
+                         dbias, stream=None) -> None:
+    """dma_attn_bwd with the library's own fixed scratch array instead of a workspace (nothing is
+    allocated); calls on one GPU must not overlap."""
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_bwd_noalloc", q, k, v,
+                                    planes=(("mask", mask), ("bias", bias), ("dbias", dbias)),
+                                    qlike=(("o", o), ("dout", dout), ("dq", dq)), kvlike=(("dk", dk), ("dv", dv)),
+                                    lse=lse, state=block_state)
+    st = _lib.dma_attn_bwd_noalloc(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                   _ptr(v, "v", torch.bfloat16), _ptr(mask, "mask", torch.bfloat16),
+                                   _ptr(bias, "bias", torch.bfloat16), _ptr(block_state, "block_state", torch.uint8),
+                                   _ptr(o, "o", torch.bfloat16), _ptr(dout, "dout", torch.bfloat16),
+                                   _ptr(lse, "lse", torch.float32), b, lq, lk, hq, hkv, d, float(scale),
+                                   int(bool(is_causal)), _ptr(dq, "dq", torch.bfloat16),
+                                   _ptr(dk, "dk", torch.bfloat16), _ptr(dv, "dv", torch.bfloat16),
+                                   _ptr(dbias, "dbias", torch.bfloat16), _stream(stream))
+    _check("dma_attn_bwd_noalloc", st)
 
 
 def dma_block_classify_ranges(start_row, end_row, b: int, hkv: int, lq: int, lk: int, is_causal: bool, block_state,
@@ -360,5 +383,6 @@ __all__ = [
     "dma_block_size", "dma_status_string", "dma_block_classify", "dma_attn_fwd", "dma_attn_bwd_workspace_size",
     "dma_attn_bwd", "dma_attention", "block_state_shape", "DMAError", "LIB_PATH", "HEADER_PATH",
     "dma_block_classify_ranges", "dma_attn_fwd_ranges", "dma_attn_bwd_ranges", "dma_topk_mask", "dma_mask_bits_size",
-    "dma_block_classify_bits", "dma_attn_fwd_bits", "dma_attn_bwd_bits",
+    "dma_block_classify_bits", "dma_attn_fwd_bits", "dma_attn_bwd_bits", "dma_attn_bwd_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]

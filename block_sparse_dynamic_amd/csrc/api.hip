@@ -1,6 +1,8 @@
 // C ABI of libdma.so: argument validation and dispatch to the gfx950 kernels.
 // Declarations, layouts and error behaviour are documented in include/dma.h.
 #include <cmath>
+#include <mutex>
+
 #include "../../include/dma.h"
 
 #include "common.h"
@@ -236,7 +238,7 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   const int32_t* rend, const uint8_t* mbits, const uint16_t* bias, const uint8_t* block_state,
                   const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv,
                   int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool validate_only = false) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !dout || !lse || !dq || !dk || !dv || !workspace) return DMA_ERR_INVALID_ARGUMENT;
@@ -251,6 +253,7 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   if (lk > kMaxLen || lq > kMaxLen) return DMA_ERR_UNSUPPORTED;
   const WsLayout wl = ws_layout(b, lq, lk, hq, hkv, d, is_causal);
   if (workspace_bytes < wl.total) return DMA_ERR_WORKSPACE_TOO_SMALL;
+  if (validate_only) return DMA_OK;
   dma::AttnArgs a = {};
   a.q = q;
   a.k = k;
@@ -328,6 +331,56 @@ int dma_topk_mask(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uin
   return dma::launch_topk(bias, rows, lk, k, mask_out, bias_out, static_cast<hipStream_t>(stream)) == hipSuccess
              ? DMA_OK
              : DMA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Backward without allocation: the workspace is this file-scope device array.  In host code
+// `scratch` names a host-side stand-in, not device memory; the device address of each GPU's
+// copy comes from hipGetSymbolAddress, taken once per device with that device current and
+// kept in scratch_ptr.  Every call on a GPU shares that GPU's copy.
+static __device__ __align__(256) unsigned char scratch[DMA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, or nullptr if it cannot be had.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int dma_attn_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,
+                         const uint16_t* bias, const uint8_t* block_state, const uint16_t* o, const uint16_t* dout,
+                         const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                         float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
+                         void* stream) {
+  // every argument first, against a stand-in workspace of the array's size: sizes past the
+  // array get the status of a caller's workspace that is too small
+  const int st = attn_bwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq,
+                               hkv, d, scale, is_causal, dq, dk, dv, dbias, reinterpret_cast<void*>(uintptr_t(256)),
+                               (size_t)DMA_NOALLOC_SCRATCH_BYTES, stream, /*validate_only=*/true);
+  if (st != DMA_OK) return st;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return DMA_ERR_HIP;
+  // every workspace region the kernels read is written earlier in the same call (row terms,
+  // pair offsets, K^T, and the dS chunks and chunk masks of every item the dQ kernel visits),
+  // so nothing has to start at zero
+  return attn_bwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv,
+                       d, scale, is_causal, dq, dk, dv, dbias, ws, (size_t)DMA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -189,6 +189,28 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward pass that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, outputs and errors are
+ * those of dma_attn_bwd without workspace / workspace_bytes.  Its workspace is
+ * one array of DMA_NOALLOC_SCRATCH_BYTES bytes in the library's device memory,
+ * one copy per GPU, held until the process ends; sizes whose
+ * dma_attn_bwd_workspace_size() exceeds it return DMA_ERR_WORKSPACE_TOO_SMALL
+ * before anything is enqueued.  All calls on one GPU share that GPU's copy:
+ * calls that overlap on one GPU (on different streams) race and must not be
+ * issued; calls in stream order are safe (each call writes every workspace byte
+ * it reads, so nothing depends on what an earlier call left there).  The array's
+ * device address is looked up once per device (hipGetSymbolAddress) on the
+ * first call made with that device current.
+ */
+#define DMA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int dma_attn_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,
+                         const uint16_t* bias, const uint8_t* block_state, const uint16_t* o, const uint16_t* dout,
+                         const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                         float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
+                         void* stream);
+
+/*
  * Column-range mask input (FlashMask README, column-wise sparse representation:
  * per key column, the rows that may attend form one interval; O(L) memory).
  * Instead of the dense mask, key column j of plane (b, g) attends exactly the

@@ -329,3 +329,26 @@ def test_binding_rejects_mismatched_shapes(what):
             dma.dma_attn_bwd(q, k, v, mask, bias, st, o, o, lse, 0.125, True, dq, dk, dv, db, ws)
         else:
             dma.dma_attn_fwd(q, k, v, mask, bias, st, 0.125, True, o, lse)
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    """dma_attn_bwd_noalloc: the arguments of dma_attn_bwd without the workspace; every argument,
+    and a workspace need past its fixed array, is rejected before the device is touched."""
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    f = lib.dma_attn_bwd_noalloc
+    f.argtypes = [vp] * 9 + [i64] * 6 + [f32, i32] + [vp] * 5
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, mask=P, bias=P, st=P, o=P, do=P, lse=P, b=1, lq=128, lk=128, hq=4, hkv=2, d=128,
+                 scale=0.1, causal=1, dq=P, dk=P, dv=P, db=P)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["mask"], a["bias"], a["st"], a["o"], a["do"], a["lse"], a["b"], a["lq"],
+                 a["lk"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["dq"], a["dk"], a["dv"], a["db"], None)
+
+    assert call(q=None) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(scale=0.0) == INVALID
+    # the Headline workload needs about 8.8 GB of workspace: far past the 64 MiB array
+    assert call(b=2, lq=16384, lk=16384, hq=16, hkv=4) == WS_SMALL
+    need = lib.dma_attn_bwd_workspace_size(1, 2048, 2048, 16, 4, 128, 1)
+    assert need > 64 << 20 and call(lq=2048, lk=2048, hq=16, hkv=4) == WS_SMALL
