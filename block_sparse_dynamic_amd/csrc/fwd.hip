@@ -42,6 +42,8 @@
 //      A and B); V^T comes out of the row-major V tile by ds_read_b64_tr_b16.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace dma {
@@ -74,13 +76,16 @@ template <int D>
 struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay single 16-byte LDS accesses
   static constexpr int kRow = tile_row<D>();  // row (elements) of the K and V tiles (tile_off layout)
   static constexpr int kBRow = kBlock + 4;  // fp32 row: 272 bytes, so 8 consecutive rows hit distinct banks
-  uint16_t k[kBlock * kRow];
-  uint16_t v[kBlock * kRow];
-  float b[kBlock * kBRow];  // effective bias / |scale| (-inf where invalid): the S accumulators' start
+  // Two buffers of the K and effective-bias tiles and three of V: iteration i reads K, bias and V
+  // of its block and (the waves that defer their P V) the V of the block before, while it
+  // stages K, bias and V of the next block.
+  uint16_t k[2][kBlock * kRow];
+  uint16_t v[3][kBlock * kRow];
+  float b[2][kBlock * kBRow];  // effective bias / |scale| (-inf where invalid): the S accumulators' start
   uint8_t st[kStateChunkF];    // block states of this query block's row, a chunk at a time
-  int32_t rs[2][kBlock];       // column ranges of the current and the next key block (range input)
+  int32_t rs[2][kBlock];       // column ranges of the blocks staged in alternate iterations (range input)
   int32_t re[2][kBlock];
-  int32_t cls[2][8];           // per-wave any / all of the staged block's validity (fused classification)
+  int32_t cls[2][2][8];        // per-wave any / all of a staged block's validity (fused classification)
 };
 
 template <int D, int HC, int MK>
@@ -186,22 +191,23 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     bo[n] = (uint32_t)(task >> 3) * (uint32_t)(p.lk * 2) + (uint32_t)(task & 7) * 16u;
   }
   const int q_rows = (int)min((int64_t)kBlock, p.lq - (int64_t)qb * kBlock);
-  auto prefetch = [&](int kb, uint8_t st) {
-    if constexpr (MK == kMaskRanges) {  // first, so that waiting for them never waits for the tiles below
+  // Loads of a block's K rows, bias and mask (or its column ranges / mask bits), and of a block's
+  // V rows: the software pipeline below stages K and bias one block ahead of V.
+  auto load_ranges = [&](int kb) {
+    if constexpr (MK == kMaskRanges) {
       const int64_t j = min((int64_t)kb * kBlock + (tid & 63), p.lk - 1);
       prs = rs_plane[j];
       pre = re_plane[j];
     }
+  };
+  auto load_kbm = [&](int kb, uint8_t st) {
     const int k_rows = (int)min((int64_t)kBlock, p.lk - (int64_t)kb * kBlock);  // >= 1
     const int64_t kv0 = (int64_t)kb * kBlock * p.hkv * D;
     const uint32_t kvbytes = (uint32_t)k_rows * (uint32_t)(p.hkv * D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(const_cast<uint16_t*>(kbase + kv0), kvbytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(const_cast<uint16_t*>(vbase + kv0), kvbytes);
 #pragma unroll
-    for (int n = 0; n < KN; ++n) {
+    for (int n = 0; n < KN; ++n)
       pk[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)kvo[n], 0, 0));
-      pv[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)kvo[n], 0, 0));
-    }
     // rows past lq and, in the last row, keys past lk fall outside the range (zeros); keys past
     // lk in earlier rows read the next row's values, which the staging replaces
     const int64_t corner = plane_off + (int64_t)qb * kBlock * p.lk + (int64_t)kb * kBlock;
@@ -220,6 +226,100 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       }
     }
   };
+  auto load_v = [&](int kb) {
+    const int k_rows = (int)min((int64_t)kBlock, p.lk - (int64_t)kb * kBlock);
+    const int64_t kv0 = (int64_t)kb * kBlock * p.hkv * D;
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(const_cast<uint16_t*>(vbase + kv0), (uint32_t)k_rows * (uint32_t)(p.hkv * D * 2));
+#pragma unroll
+    for (int n = 0; n < KN; ++n)
+      pv[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)kvo[n], 0, 0));
+  };
+
+  // Stage block kb's K rows and effective bias into buffer `buf` (its column ranges, for the
+  // range input, are in sm.rs[buf]); in the classifying mode also each wave's any / all.
+  auto stage_kb = [&](int buf, int kb, uint8_t st) {
+#pragma unroll
+    for (int n = 0; n < KN; ++n) {
+      const int task = tid + n * NT;
+      const int r = task / (D / 8), c = task % (D / 8);
+      *reinterpret_cast<u32x4*>(&sm.k[buf][tile_off<D>(r, c * 8)]) = pk[n];  // rows past lk are zeros
+    }
+    const bool full = (st == kFull);
+    bool any_v = false, all_v = true;  // fused classification: this thread's positions of the block
+#pragma unroll
+    for (int n = 0; n < BN; ++n) {
+      const int task = tid + n * NT;
+      const int r = task >> 3, c = task & 7;
+      const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
+      // columns j0 + e of this chunk are inside the matrix and causal for e <= emax
+      int64_t lim = p.lk - 1 - j0;
+      if (p.causal) lim = min(lim, i + shift - j0);
+      const int emax = (i < p.lq) ? (int)max((int64_t)-1, min(lim, (int64_t)7)) : -1;
+      const u32x4 bw = pb[n];  // zeros without a bias
+      u32x4 mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+      if (!full) {
+        if constexpr (MK == kMaskRanges) {  // attends iff start <= i < end of the key's column
+          const int4 s0 = *reinterpret_cast<const int4*>(&sm.rs[buf][c * 8]);
+          const int4 s1 = *reinterpret_cast<const int4*>(&sm.rs[buf][c * 8 + 4]);
+          const int4 e0 = *reinterpret_cast<const int4*>(&sm.re[buf][c * 8]);
+          const int4 e1 = *reinterpret_cast<const int4*>(&sm.re[buf][c * 8 + 4]);
+          const int rs8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          const int re8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool a0 = rs8[2 * e] <= i && i < re8[2 * e];
+            const bool a1 = rs8[2 * e + 1] <= i && i < re8[2 * e + 1];
+            mw[e] = (a0 ? 0x3F80u : 0u) | (a1 ? 0x3F800000u : 0u);
+          }
+        } else if constexpr (MK == kMaskBits) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            mw[e] = (((pmb[n] >> (2 * e)) & 1u) ? 0x3F80u : 0u) | (((pmb[n] >> (2 * e + 1)) & 1u) ? 0x3F800000u : 0u);
+        } else {
+          if (has_mask) mw = pm[n];
+        }
+      }
+      f32x4 y0, y1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool v0 = 2 * e <= emax && attends_lo(mw[e]);
+        const bool v1 = 2 * e + 1 <= emax && attends_hi(mw[e]);
+        if constexpr (kCls) {
+          any_v = any_v || v0 || v1;
+          all_v = all_v && v0 && v1;
+        }
+        const float lo = v0 ? clamp_bias(bf16_lo(bw[e])) * inv_as : -INFINITY;
+        const float hi16 = v1 ? clamp_bias(bf16_hi(bw[e])) * inv_as : -INFINITY;
+        if (e < 2) {
+          y0[2 * e] = lo;
+          y0[2 * e + 1] = hi16;
+        } else {
+          y1[2 * e - 4] = lo;
+          y1[2 * e - 3] = hi16;
+        }
+      }
+      *reinterpret_cast<f32x4*>(&sm.b[buf][r * BR + c * 8]) = y0;
+      *reinterpret_cast<f32x4*>(&sm.b[buf][r * BR + c * 8 + 4]) = y1;
+    }
+    if constexpr (kCls) {
+      // the block is SKIP without a valid position, FULL when all 4096 are valid (rows past lq
+      // and keys past lk count as invalid), PARTIAL otherwise; every thread holds 8 positions
+      const bool wany = __any(any_v), wall = __all(all_v);
+      if (lane == 0) {
+        sm.cls[buf][0][wave] = wany;
+        sm.cls[buf][1][wave] = wall;
+      }
+    }
+  };
+  auto stage_v = [&](int buf, bool keep) {
+#pragma unroll
+    for (int n = 0; n < KN; ++n) {
+      const int task = tid + n * NT;
+      const int r = task / (D / 8), c = task % (D / 8);
+      *reinterpret_cast<u32x4*>(&sm.v[buf][tile_off<D>(r, c * 8)]) = keep ? pv[n] : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
   // Per-lane LDS element offsets of the K operand reads and the transposing V reads; the
   // loop adds compile-time row offsets only.  With the swizzled 128-wide layout the XOR of
@@ -236,208 +336,188 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     voff1[dt] = tile_off<D>(hi * 4 + trow + 8, dt * 32 + tcol);
   }
 
-  int kb = next_kb(0);
-  // the fused classification reads the mask of every visited block (as for a PARTIAL one)
-  uint8_t st = kb < p.nkb ? (kCls ? kPartial : sm.st[kb - cache_lo]) : kSkip;
-  if (kb < p.nkb) prefetch(kb, st);
-  int rpar = 0;  // which of the two range buffers holds the current block's ranges
-  if constexpr (MK == kMaskRanges) {
-    if (tid < kBlock) {
-      sm.rs[0][tid] = prs;
-      sm.re[0][tid] = pre;
-    }
-  }
-  while (kb < p.nkb) {
-    const bool full = (st == kFull);
-    lds_barrier();  // the previous block's LDS reads are done
-    // ---- stage K, V (row-major) and the effective bias -------------------
-#pragma unroll
-    for (int n = 0; n < KN; ++n) {
-      const int task = tid + n * NT;
-      const int r = task / (D / 8), c = task % (D / 8);
-      // rows past lk were loaded as zeros
-      *reinterpret_cast<u32x4*>(&sm.k[tile_off<D>(r, c * 8)]) = pk[n];
-      *reinterpret_cast<u32x4*>(&sm.v[tile_off<D>(r, c * 8)]) = pv[n];
-    }
-    bool any_v = false, all_v = true;  // fused classification: this thread's positions of the block
-    {
-#pragma unroll
-      for (int n = 0; n < BN; ++n) {
-        const int task = tid + n * NT;
-        const int r = task >> 3, c = task & 7;
-        const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
-        // columns j0 + e of this chunk are inside the matrix and causal for e <= emax
-        int64_t lim = p.lk - 1 - j0;
-        if (p.causal) lim = min(lim, i + shift - j0);
-        const int emax = (i < p.lq) ? (int)max((int64_t)-1, min(lim, (int64_t)7)) : -1;
-        const u32x4 bw = pb[n];  // zeros without a bias
-        u32x4 mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-        if (!full) {
-          if constexpr (MK == kMaskRanges) {  // attends iff start <= i < end of the key's column
-            const int4 s0 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8]);
-            const int4 s1 = *reinterpret_cast<const int4*>(&sm.rs[rpar][c * 8 + 4]);
-            const int4 e0 = *reinterpret_cast<const int4*>(&sm.re[rpar][c * 8]);
-            const int4 e1 = *reinterpret_cast<const int4*>(&sm.re[rpar][c * 8 + 4]);
-            const int rs8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-            const int re8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool a0 = rs8[2 * e] <= i && i < re8[2 * e];
-              const bool a1 = rs8[2 * e + 1] <= i && i < re8[2 * e + 1];
-              mw[e] = (a0 ? 0x3F80u : 0u) | (a1 ? 0x3F800000u : 0u);
-            }
-          } else if constexpr (MK == kMaskBits) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              mw[e] = (((pmb[n] >> (2 * e)) & 1u) ? 0x3F80u : 0u) | (((pmb[n] >> (2 * e + 1)) & 1u) ? 0x3F800000u : 0u);
-          } else {
-            if (has_mask) mw = pm[n];
-          }
-        }
-        f32x4 y0, y1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool v0 = 2 * e <= emax && attends_lo(mw[e]);
-          const bool v1 = 2 * e + 1 <= emax && attends_hi(mw[e]);
-          if constexpr (kCls) {
-            any_v = any_v || v0 || v1;
-            all_v = all_v && v0 && v1;
-          }
-          const float lo = v0 ? clamp_bias(bf16_lo(bw[e])) * inv_as : -INFINITY;
-          const float hi16 = v1 ? clamp_bias(bf16_hi(bw[e])) * inv_as : -INFINITY;
-          if (e < 2) {
-            y0[2 * e] = lo;
-            y0[2 * e + 1] = hi16;
-          } else {
-            y1[2 * e - 4] = lo;
-            y1[2 * e - 3] = hi16;
-          }
-        }
-        *reinterpret_cast<f32x4*>(&sm.b[r * BR + c * 8]) = y0;
-        *reinterpret_cast<f32x4*>(&sm.b[r * BR + c * 8 + 4]) = y1;
-      }
-    }
-    if constexpr (kCls) {
-      // the block is SKIP without a valid position, FULL when all 4096 are valid (rows past lq
-      // and keys past lk count as invalid), PARTIAL otherwise; every thread holds 8 positions
-      const bool wany = __any(any_v), wall = __all(all_v);
-      if (lane == 0) {
-        sm.cls[0][wave] = wany;
-        sm.cls[1][wave] = wall;
-      }
-    }
-    lds_barrier();
-    uint8_t bst = kPartial;
-    if constexpr (kCls) {
-      bool a = false, f = true;
-#pragma unroll
-      for (int w2 = 0; w2 < NT / 64; ++w2) {
-        a = a || sm.cls[0][w2] != 0;
-        f = f && sm.cls[1][w2] != 0;
-      }
-      bst = a ? (f ? kFull : kPartial) : kSkip;
-      if (chunk == 0 && tid == 0) p.state_out[((int64_t)plane * p.nqb + qb) * p.nkb + kb] = bst;
-    }
-    // ---- start loading the next non-SKIP block ------------------------------
-    const int kb_next = next_kb(kb + 1);
-    const uint8_t st_next = kb_next < p.nkb ? (kCls ? kPartial : sm.st[kb_next - cache_lo]) : kSkip;
-    if (kb_next < p.nkb) prefetch(kb_next, st_next);
-
-    if (kCls && bst == kSkip) {  // nothing valid in the block: no products (its state is written)
-      kb = kb_next;
-      st = st_next;
-      continue;
-    }
-    // ---- y = S^T / |scale| + effective bias / |scale| = K Q^T + the staged tile ----------------
-    f32x16 sacc[2];
+  // O^T += V^T P_hi^T + V^T P_lo^T for the block whose V sits in buffer vb.  P in [0, 256] as two
+  // bf16 parts: P_hi keeps the upper half of each fp32 weight (truncation), P_lo = P - P_hi
+  // rounded to bf16, so P_hi + P_lo is within 2^-15 of P.  A single bf16 P (relative rounding
+  // 2^-8) would move O by more than the 1e-2 the output tolerance leaves after bf16 storage.
+  u32x4 ph[2][2], pl[2][2];  // the weights P_hi, P_lo [32-key half][16-key step]
+  auto pv_products = [&](int vb) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.b[rloc * BR + kt * 32 + gi * 8 + hi * 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[kt][gi * 4 + e] = y[e];
-      }
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[koff[s] + kt * 32 * KR]);
-        sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
-      }
-    }
-    // ---- row maximum of the scores x = |scale| y ------------------------------------
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-    mx = max_with_half_swap(mx) * as;
-    // ---- online softmax ----------------------------------------------------------
-    // The reference maximum moves only when a row's maximum exceeds it by more than
-    // kRescaleMargin (8 in log2 units): below that the weights exp(x - m_ref) stay under 256,
-    // which fp32 sums and the two-part bf16 P hold without loss, and the rescale of the accumulators
-    // (64 multiplies per lane) runs a few times per row instead of on most key blocks.
-    if (__any(mx > m_ref + kRescaleMargin)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_ref - m_new) * kLog2e);
-      m_ref = m_new;
-      l_part *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-    }
-    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * kLog2e;
-    float rs = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], as_l2e, -mb));
-        sacc[kt][i] = pv;
-        rs += pv;
-      }
-    l_part += rs;
-    // ---- O^T += V^T P_hi^T + V^T P_lo^T ------------------------------------------------
-    // P in [0, 256] as two bf16 parts: P_hi keeps the upper half of each fp32 weight
-    // (truncation, one byte permute per pair), P_lo = P - P_hi rounded to bf16, so P_hi + P_lo
-    // is within 2^-15 of P.  A single bf16 P (relative rounding 2^-8) would move O by more than
-    // the 1e-2 the output tolerance leaves after bf16 storage of O.
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        u32x4 ph, pl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a = __float_as_uint(sacc[kt][hh * 8 + 2 * e]), b = __float_as_uint(sacc[kt][hh * 8 + 2 * e + 1]);
-          ph[e] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // upper halves of a (low) and b (high)
-          pl[e] = pack_bf16x2(__uint_as_float(a) - __uint_as_float(a & 0xFFFF0000u),
-                              __uint_as_float(b) - __uint_as_float(b & 0xFFFF0000u));
-        }
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, ph), bl = __builtin_bit_cast(bf16x8, pl);
+        const bf16x8 bh = __builtin_bit_cast(bf16x8, ph[kt][hh]), bl = __builtin_bit_cast(bf16x8, pl[kt][hh]);
         const int rbase = (kt * 32 + hh * 16) * KR;  // rows of this k-step, a compile-time offset
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const i16x4 a0 = lds_read_tr16(&sm.v[voff0[dt] + rbase]);
-          const i16x4 a1 = lds_read_tr16(&sm.v[voff1[dt] + rbase]);
+          const i16x4 a0 = lds_read_tr16(&sm.v[vb][voff0[dt] + rbase]);
+          const i16x4 a1 = lds_read_tr16(&sm.v[vb][voff1[dt] + rbase]);
           const bf16x8 av = join_bf16x8(a0, a1);
           oacc[dt] = mfma32(av, bh, oacc[dt]);
           oacc[dt] = mfma32(av, bl, oacc[dt]);
         }
       }
-    }
-    if constexpr (MK == kMaskRanges) {  // the next block's ranges go to the other buffer, read after the next barrier
+  };
+
+  // ---- the key-block loop, with the two waves of each SIMD in opposite phases ----------------
+  // Waves of the first half (one per SIMD) take a block as S products -> softmax -> P V; the
+  // other waves as S products -> P V of the block before -> softmax, keeping the weights for one
+  // block.  After the S products, which both waves of a SIMD issue together, one wave's softmax
+  // (vector work) runs while the other wave's P V products occupy the matrix core, and the other
+  // way round: the two waves keep each other's idle units busy.  Per block (iteration i, one
+  // barrier): K, bias from buffer i % 2, V of the block from buffer i % 3 and of the block before
+  // from (i - 1) % 3; K, bias and V of the next block are staged into the other buffers.
+  const bool defer = wave >= NT / 128;  // waves 0 .. n/2-1 do not defer, the others do
+  int kbc = next_kb(0);
+  uint8_t stc = kbc < p.nkb ? (kCls ? kPartial : sm.st[kbc - cache_lo]) : kSkip;
+  int kbn = p.nkb;
+  uint8_t stn = kSkip;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) ph[kt][hh] = pl[kt][hh] = u32x4{0u, 0u, 0u, 0u};
+  // the deferring waves' first P V reads buffer 2 with zero weights: clear it
+  for (int t2 = tid; t2 < kBlock * KR / 8; t2 += NT) reinterpret_cast<u32x4*>(&sm.v[2][0])[t2] = u32x4{0u, 0u, 0u, 0u};
+  if (kbc < p.nkb) {
+    load_ranges(kbc);
+    load_kbm(kbc, stc);
+    load_v(kbc);
+    if constexpr (MK == kMaskRanges) {
       if (tid < kBlock) {
-        sm.rs[rpar ^ 1][tid] = prs;
-        sm.re[rpar ^ 1][tid] = pre;
+        sm.rs[0][tid] = prs;
+        sm.re[0][tid] = pre;
       }
-      rpar ^= 1;
+      lds_barrier();
     }
-    kb = kb_next;
-    st = st_next;
+    stage_kb(0, kbc, stc);
+    stage_v(0, true);
+    kbn = next_kb(kbc + 1);
+    stn = kbn < p.nkb ? (kCls ? kPartial : sm.st[kbn - cache_lo]) : kSkip;
+    if (kbn < p.nkb) {
+      load_ranges(kbn);
+      load_kbm(kbn, stn);
+      load_v(kbn);
+    }
   }
+  int vcur = 0;       // V buffer of the current block; the block before's is (vcur + 2) % 3
+  bool prev_ok = false;  // the block before computed (its V and weights are valid)
+  auto iteration = [&](auto parity) {
+    constexpr int buf = decltype(parity)::value;
+    lds_barrier();  // the tiles staged in the iteration before are visible, the buffers it read are free
+    if constexpr (MK == kMaskRanges) {  // the next block's ranges, staged below
+      if (kbn < p.nkb && tid < kBlock) {
+        sm.rs[buf ^ 1][tid] = prs;
+        sm.re[buf ^ 1][tid] = pre;
+      }
+    }
+    bool compute = true;  // a block with no valid position (fused classification) adds nothing
+    if constexpr (kCls) {
+      bool a = false, f = true;
+#pragma unroll
+      for (int w2 = 0; w2 < NT / 64; ++w2) {
+        a = a || sm.cls[buf][0][w2] != 0;
+        f = f && sm.cls[buf][1][w2] != 0;
+      }
+      const uint8_t bst = a ? (f ? kFull : kPartial) : kSkip;
+      if (chunk == 0 && tid == 0) p.state_out[((int64_t)plane * p.nqb + qb) * p.nkb + kbc] = bst;
+      compute = bst != kSkip;
+    }
+    const int vprev = vcur == 0 ? 2 : vcur - 1;
+    if (defer && prev_ok) pv_products(vprev);  // the block before's P V (oacc still in its reference)
+    if (compute) {
+      // ---- y = S^T / |scale| + effective bias / |scale| = K Q^T + the staged tile ----------
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.b[buf][rloc * BR + kt * 32 + gi * 8 + hi * 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[kt][gi * 4 + e] = y[e];
+        }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][koff[s] + kt * 32 * KR]);
+          sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
+        }
+      }
+      // ---- online softmax ----------------------------------------------------------------------
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+      mx = max_with_half_swap(mx) * as;
+      // The reference maximum moves only when a row's maximum exceeds it by more than
+      // kRescaleMargin (8 in log2 units): below that the weights exp(x - m_ref) stay under 256,
+      // which fp32 sums and the two-part bf16 P hold without loss, and the rescale of the
+      // output accumulators (64 multiplies per lane) runs a few times per row instead of on most
+      // key blocks.  It follows every P V of the old reference, whichever order the wave runs.
+      if (__any(mx > m_ref + kRescaleMargin)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f((m_ref - m_new) * kLog2e);
+        m_ref = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      }
+      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * kLog2e;
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pw = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], as_l2e, -mb));
+          sacc[kt][i] = pw;
+          rs += pw;
+        }
+      l_part += rs;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t a = __float_as_uint(sacc[kt][hh * 8 + 2 * e]), b = __float_as_uint(sacc[kt][hh * 8 + 2 * e + 1]);
+            ph[kt][hh][e] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // upper halves of a (low) and b (high)
+            pl[kt][hh][e] = pack_bf16x2(__uint_as_float(a) - __uint_as_float(a & 0xFFFF0000u),
+                                        __uint_as_float(b) - __uint_as_float(b & 0xFFFF0000u));
+          }
+      if (!defer) pv_products(vcur);
+    }
+    prev_ok = compute;
+    // ---- stage the next block's K, bias and V; load the one after -----------------------------
+    if (kbn < p.nkb) {
+      const int vnext = vcur == 2 ? 0 : vcur + 1;  // the buffer of the block two back, read by no one now
+      stage_kb(buf ^ 1, kbn, stn);
+      stage_v(vnext, true);
+      kbc = kbn;
+      stc = stn;
+      kbn = next_kb(kbn + 1);
+      stn = kbn < p.nkb ? (kCls ? kPartial : sm.st[kbn - cache_lo]) : kSkip;
+      if (kbn < p.nkb) {
+        load_ranges(kbn);
+        load_kbm(kbn, stn);
+        load_v(kbn);
+      }
+      vcur = vnext;
+    } else {
+      kbc = p.nkb;
+    }
+  };
+  // The loop is unrolled twice, so the K / bias buffer of every LDS access is a compile-time
+  // constant (an immediate offset instead of an address add per access).
+  while (kbc < p.nkb) {
+    iteration(std::integral_constant<int, 0>{});
+    if (kbc >= p.nkb) break;
+    iteration(std::integral_constant<int, 1>{});
+  }
+  lds_barrier();  // the same barrier count in every wave
+  if (defer && prev_ok) pv_products(vcur);  // the last block's P V
 
   if constexpr (kCls) {  // blocks wholly excluded by causality are SKIP without a read
     if (chunk == 0)
