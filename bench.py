@@ -2,24 +2,36 @@
 
 One step = one pass of the whole path over one batch of synthetic input already
 resident in HBM: block classification, forward (O, LSE) and backward (dQ, dK, dV,
-dBias), through the C ABI on the current stream.  By default the classification runs
-fused into the forward (dma_attn_fwd_classify: each live block's mask tile is read once,
-reduced to its class and applied); --separate-classify times dma_block_classify +
-dma_attn_fwd instead.  The other path is timed in the same run (``classify_other``;
-left out with --no-next).
+dBias), through the C ABI on the current stream.  The classification runs fused
+into the forward (dma_attn_fwd_classify: each live block's mask tile is read once,
+reduced to its class and applied); the backward is called as its three phases
+(dma_attn_bwd_part: prepare, main, dQ, which together are dma_attn_bwd) so that
+HIP events can bracket the main kernel.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config headline]
 
-Prints one JSON line.  ``value`` is the effective fwd+bwd TFLOP/s of the step:
-MMA FLOPs over the non-SKIP 64x64 blocks (4*d per block element per query head
-forward, 10*d backward; FlashMask README, Performance: theoretical FLOPs count
-only the core matrix multiplies) divided by the time of the whole step,
-classification included.
+Prints one JSON line.  ``value`` is the effective fwd+bwd TFLOP/s of the step on
+the Headline workload: MMA FLOPs over the non-SKIP 64x64 blocks (4*d per block
+element per query head forward, 10*d backward; FlashMask README, Performance:
+theoretical FLOPs count only the core matrix multiplies) divided by the wall time
+of K steps (synchronised on both sides), classification included.
 
-``next_rows`` (outside the step, skipped with --no-next): the GPU top-k mask construction on a
-fresh N(0,1) bias of the workload's shape; the step with the bit-packed PARTIAL-block mask
-instead of the bf16 mask, per phase; and one classify + forward + backward of the Doc-packed
-workload with the dense mask and with column ranges.
+Beside it:
+* ``roofline`` for the dominant kernel, the backward main kernel: its algorithmic
+  FLOPs (S, dP, dV, dK products: 8*d per block element per query head) over its
+  mean duration from HIP events around it in the K timed steps;
+* ``method``: the measurement of every workload by the survey's method: 2 warm-up
+  iterations, then 10 timed ones, each preceded by an untimed 512 MiB write (larger
+  than the last-level caches, so mask and bias come from HBM), with HIP events
+  around every call; the mean of the first 3 and the median of 10 per phase,
+  effective TFLOP/s and the mandatory mask / bias / dBias bytes per second, each
+  as a fraction of the bound that applies (bf16 MFMA, or HBM for the document
+  workload);
+* ``measured_peaks``: a 4 GiB device copy's read + write bandwidth beside the
+  spec HBM peak;
+* ``cpu_baseline``: the fp64 oracle on sampled query blocks of the workload;
+* ``next_rows`` (unless --no-next): GPU top-k mask construction, the step with the
+  bit-packed PARTIAL-block mask, the other classification path.
 """
 from __future__ import annotations
 
@@ -34,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+FLUSH_BYTES = 512 << 20
 
 
 def parse():
@@ -43,9 +56,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--separate-classify", action="store_true",
-                    help="time dma_block_classify + dma_attn_fwd instead of the fused dma_attn_fwd_classify")
-    ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements (top-k construction)")
+    ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload method measurements")
+    ap.add_argument("--workloads", default="mid,headline,docpacked,long",
+                    help="workloads measured by the survey's method (comma separated)")
     ap.add_argument("--cpu-blocks", type=int, default=16, help="query-row blocks the oracle times")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps, so that a hardware counter "
@@ -62,9 +76,9 @@ def parse():
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "headline_traffic.json")
 KERNEL_SOURCES = ["classify.hip", "fwd.hip", "bwd.hip", "common.h"]
-# kernels of each C-ABI call, matched by substring of the demangled name
-CALL_KERNELS = {"classify": ["classify_kernel"], "fwd": ["fwd_kernel"],
-                "bwd": ["bwd_pre_kernel", "kt_kernel", "pair_base_kernel", "bwd_main_kernel", "dq_kernel"]}
+# kernels of each measured unit, matched by substring of the demangled name
+CALL_KERNELS = {"fwd": ["fwd_kernel"], "bwd_main": ["bwd_main_kernel"], "bwd_dq": ["dq_kernel"],
+                "bwd_prepare": ["bwd_pre_kernel", "kt_kernel", "pair_base_kernel"], "classify": ["classify_kernel"]}
 
 
 def kernel_source_hash() -> str:
@@ -78,7 +92,7 @@ def kernel_source_hash() -> str:
 
 
 def summarize_traffic(counter_dir: str, out_json: str, copy_mib: int):
-    """HBM bytes per launch of each call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+    """HBM bytes per launch of each kernel group from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
 
     Each counter is scaled by the ratio of known bytes to what it reads for the calibration
     copy (a device copy of --calibrate-copy-mib MiB: that many bytes fetched and written)."""
@@ -88,7 +102,7 @@ def summarize_traffic(counter_dir: str, out_json: str, copy_mib: int):
 
     assert copy_mib > 0, "give the calibration copy's size with --calibrate-copy-mib"
     out = {"source_hash": kernel_source_hash(), "calibration_mib": copy_mib, "counters": {}}
-    per_call = defaultdict(float)
+    per_unit = defaultdict(float)
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         files = glob.glob(os.path.join(counter_dir, "**", f"{counter}_counter_collection.csv"), recursive=True)
         assert len(files) == 1, f"expected one {counter} csv under {counter_dir}, found {files}"
@@ -101,23 +115,165 @@ def summarize_traffic(counter_dir: str, out_json: str, copy_mib: int):
         copy_kib = max(copy)
         factor = copy_mib * 1024.0 / copy_kib
         out["counters"][counter] = {"copy_kib": copy_kib, "factor": factor}
-        for call, subs in CALL_KERNELS.items():
+        for unit, subs in CALL_KERNELS.items():
             for name, vals in per.items():
                 if any(sub in name for sub in subs):
-                    per_call[call] += sum(vals) / len(vals) * 1024.0 * factor
-    out["bytes_per_launch"] = {k: round(v) for k, v in per_call.items()}
+                    per_unit[unit] += sum(vals) / len(vals) * 1024.0 * factor
+    out["bytes_per_launch"] = {k: round(v) for k, v in per_unit.items()}
     with open(out_json, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def block_counts(state):
-    import torch
+def live_blocks(c, np):
+    """Blocks not wholly excluded by causality, summed over (b, kv head)."""
+    nqb, nkb = (c.lq + 63) // 64, (c.lk + 63) // 64
+    qb = np.arange(nqb)[:, None]
+    kb = np.arange(nkb)[None, :]
+    live = (kb * 64 <= np.minimum(qb * 64 + 63, c.lq - 1) + (c.lk - c.lq)) if c.causal else np.ones((nqb, nkb), bool)
+    return int(live.sum()) * c.b * c.hkv
 
-    n_skip = int((state == 0).sum())
+
+def work_of(c, state, np, fused: bool, has_mask: bool, ranges: bool = False):
+    """Algorithmic FLOPs and mandatory mask / bias / dBias bytes of one step (see the module doc)."""
     n_p = int((state == 1).sum())
     n_f = int((state == 2).sum())
-    return n_skip, n_p, n_f
+    n_ns = n_p + n_f
+    G, d = c.hq // c.hkv, c.d
+    w = {"blocks_nonskip": n_ns, "blocks_partial": n_p, "blocks_full": n_f,
+         "f_fwd": 4.0 * d * 4096 * G * n_ns, "f_bwd": 10.0 * d * 4096 * G * n_ns,
+         "f_bwd_main": 8.0 * d * 4096 * G * n_ns, "f_bwd_dq": 2.0 * d * 4096 * G * n_ns}
+    mask_read = 0 if ranges else 2.0 * 4096 * n_p
+    # a separate classification reads the mask of every causally live block once more; fused,
+    # the forward's own mask reads classify; column ranges are 8 bytes per key and plane
+    w["b_cls"] = (8.0 * c.b * c.hkv * c.lk if ranges else
+                  (2.0 * 4096 * live_blocks(c, np) if (has_mask and not fused) else 0.0))
+    w["b_fwd"] = 2.0 * 4096 * n_ns + mask_read
+    w["b_bwd"] = w["b_fwd"] + 2.0 * c.b * c.hkv * c.lq * c.lk
+    return w
+
+
+class Step:
+    """Device inputs, outputs and workspace of one workload, and its step through the C ABI."""
+
+    def __init__(self, c, dma, torch, np, path="fused"):
+        import synth
+        from synth.device import upload_dense, upload_mask_bias
+
+        self.c, self.dma, self.torch, self.path = c, dma, torch, path
+        t0 = time.perf_counter()
+        self.q, self.k, self.v, self.do = upload_dense(c)
+        self.mask, self.bias = upload_mask_bias(c)
+        torch.cuda.synchronize()
+        self.t_gen = time.perf_counter() - t0
+        if path == "ranges":
+            bounds = synth.doc_bounds(c)
+            j = np.arange(c.lk)
+            end = bounds[np.searchsorted(bounds, j, side="right")]
+            self.rs = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(j, (c.b, c.hkv, c.lk)).astype(np.int32))).cuda()
+            self.re = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(end, (c.b, c.hkv, c.lk)).astype(np.int32))).cuda()
+        self.state = torch.empty(dma.block_state_shape(c.b, c.hkv, c.lq, c.lk), dtype=torch.uint8, device="cuda")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.dbias = torch.empty((c.b, c.hkv, c.lq, c.lk), dtype=torch.bfloat16, device="cuda")
+        self.ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal),
+                              dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.current_stream()
+
+    PHASES = ("classify", "fwd", "bwd_prepare", "bwd_main", "bwd_dq")
+
+    def run(self, ev=None):
+        """One step; ev = 6 events recorded between the phases (or None)."""
+        c, dma, s = self.c, self.dma, self.stream
+        rec = (lambda i: ev[i].record(s)) if ev is not None else (lambda i: None)
+        rec(0)
+        if self.path == "ranges":
+            dma.dma_block_classify_ranges(self.rs, self.re, c.b, c.hkv, c.lq, c.lk, c.causal, self.state, s)
+            rec(1)
+            dma.dma_attn_fwd_ranges(self.q, self.k, self.v, self.rs, self.re, self.bias, self.state, c.scale_f32,
+                                    c.causal, self.o, self.lse, s)
+            rec(2)
+            rec(3)
+            # the range backward has no per-phase entry point: its whole time counts as bwd_main
+            dma.dma_attn_bwd_ranges(self.q, self.k, self.v, self.rs, self.re, self.bias, self.state, self.o, self.do,
+                                    self.lse, c.scale_f32, c.causal, self.dq, self.dk, self.dv, self.dbias, self.ws, s)
+            rec(4)
+            rec(5)
+            return
+        if self.path == "separate":
+            dma.dma_block_classify(self.mask, c.b, c.hkv, c.lq, c.lk, c.causal, self.state, s)
+            rec(1)
+            dma.dma_attn_fwd(self.q, self.k, self.v, self.mask, self.bias, self.state, c.scale_f32, c.causal, self.o,
+                             self.lse, s)
+        else:
+            rec(1)
+            dma.dma_attn_fwd_classify(self.q, self.k, self.v, self.mask, self.bias, c.scale_f32, c.causal, self.state,
+                                      self.o, self.lse, s)
+        rec(2)
+        for i, part in enumerate((dma.BWD_PREPARE, dma.BWD_MAIN, dma.BWD_DQ)):
+            dma.dma_attn_bwd_part(part, self.q, self.k, self.v, self.mask, self.bias, self.state, self.o, self.do,
+                                  self.lse, c.scale_f32, c.causal, self.dq, self.dk, self.dv, self.dbias, self.ws, s)
+            rec(3 + i)
+
+    def events(self):
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(6)]
+
+    @staticmethod
+    def phase_ms(ev):
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+
+    def free(self):
+        for name in ("q", "k", "v", "do", "mask", "bias", "state", "o", "lse", "dq", "dk", "dv", "dbias", "ws", "rs",
+                     "re"):
+            if hasattr(self, name):
+                delattr(self, name)
+        self.torch.cuda.empty_cache()
+
+
+def method_measure(st, np, torch, flush, n_warm=2, n_iter=10, bound="mfma"):
+    """The survey's method: warm-ups, then n_iter iterations each after an untimed flush write;
+    per phase the mean of the first 3 and the median of all, and rates against the bound."""
+    c = st.c
+    for _ in range(n_warm):
+        st.run()
+    torch.cuda.synchronize()
+    evs = [st.events() for _ in range(n_iter)]
+    for i in range(n_iter):
+        flush.zero_()  # untimed: outside the events
+        st.run(evs[i])
+    torch.cuda.synchronize()
+    t = np.array([Step.phase_ms(e) for e in evs])  # [iter, phase]
+    first3, med = t[:3].mean(axis=0), np.median(t, axis=0)
+    w = work_of(c, st.state, np, fused=(st.path == "fused"), has_mask=st.mask is not None or st.path == "ranges",
+                ranges=(st.path == "ranges"))
+    out = {"workload": describe(c), "path": st.path, "bound": bound, "iterations": n_iter,
+           "blocks_nonskip": w["blocks_nonskip"], "blocks_partial": w["blocks_partial"], "blocks_full": w["blocks_full"]}
+    for name, stat in (("mean_first3", first3), ("median10", med)):
+        ph = dict(zip(Step.PHASES, stat))
+        t_cls_fwd = ph["classify"] + ph["fwd"]
+        t_bwd = ph["bwd_prepare"] + ph["bwd_main"] + ph["bwd_dq"]
+        t_step = t_cls_fwd + t_bwd
+        mand = w["b_cls"] + w["b_fwd"] + w["b_bwd"]
+        tf = (w["f_fwd"] + w["f_bwd"]) / (t_step * 1e-3) / 1e12
+        gbs = mand / (t_step * 1e-3) / 1e9
+        out[name] = {"phases_ms": {k: round(float(v), 4) for k, v in ph.items()}, "step_ms": round(float(t_step), 4),
+                     "tflops": round(tf, 2), "tflops_fwd": round(w["f_fwd"] / (t_cls_fwd * 1e-3) / 1e12, 2),
+                     "tflops_bwd": round(w["f_bwd"] / (t_bwd * 1e-3) / 1e12, 2),
+                     "mandatory_gbs": round(gbs, 1),
+                     "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        if st.path != "ranges":
+            out[name]["bwd_main_tflops"] = round(w["f_bwd_main"] / (ph["bwd_main"] * 1e-3) / 1e12, 2)
+        else:
+            out[name]["note"] = "the range backward is one call: bwd_main holds all of it, bwd_prepare and bwd_dq are 0"
+    out["mandatory_bytes"] = {"classify": w["b_cls"], "fwd": w["b_fwd"], "bwd": w["b_bwd"]}
+    return out
+
+
+def describe(c) -> str:
+    m = f"top-k {c.topk}" if c.mask == "topk" else ("document" if c.mask == "doc" else c.mask)
+    return (f"{c.name}: b={c.b} L={c.lq} Hq={c.hq} Hkv={c.hkv} d={c.d} {m} mask, "
+            f"{'causal' if c.causal else 'non-causal'}")
 
 
 def cpu_baseline(c, blocks: int, f_total: float):
@@ -161,114 +317,76 @@ def cpu_baseline(c, blocks: int, f_total: float):
     }
 
 
-def time_ranges(args, dma, synth, np):
-    import torch
-    from synth.device import upload_dense, upload_mask_bias
-
-    c = synth.CASES["docpacked"]
-    q, k, v, do = upload_dense(c)
-    mask, bias = upload_mask_bias(c)
-    bounds = synth.doc_bounds(c)
-    j = np.arange(c.lk)
-    end = bounds[np.searchsorted(bounds, j, side="right")]
-    rs = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(j, (c.b, c.hkv, c.lk)).astype(np.int32))).cuda()
-    re = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(end, (c.b, c.hkv, c.lk)).astype(np.int32))).cuda()
-    st = torch.empty(dma.block_state_shape(c.b, c.hkv, c.lq, c.lk), dtype=torch.uint8, device="cuda")
-    o, lse = torch.empty_like(q), torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dbias = torch.empty((c.b, c.hkv, c.lq, c.lk), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8,
-                     device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step(ranges):
-        if ranges:
-            dma.dma_block_classify_ranges(rs, re, c.b, c.hkv, c.lq, c.lk, c.causal, st, stream)
-            dma.dma_attn_fwd_ranges(q, k, v, rs, re, bias, st, c.scale_f32, c.causal, o, lse, stream)
-            dma.dma_attn_bwd_ranges(q, k, v, rs, re, bias, st, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias,
-                                    ws, stream)
-        else:
-            dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, st, stream)
-            dma.dma_attn_fwd(q, k, v, mask, bias, st, c.scale_f32, c.causal, o, lse, stream)
-            dma.dma_attn_bwd(q, k, v, mask, bias, st, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws, stream)
-
-    out = {"workload": f"{c.name}: b={c.b} L={c.lq} Hq={c.hq} Hkv={c.hkv} d={c.d} document mask, causal"}
-    for ranges in (False, True):
-        step(ranges)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 3
-        e0.record(stream)
-        for _ in range(reps):
-            step(ranges)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        out["ranges_ms" if ranges else "dense_ms"] = round(e0.elapsed_time(e1) / reps, 4)
-    n_p = int((st == 1).sum())
-    n_f = int((st == 2).sum())
-    live = int(((st == 1) | (st == 2)).sum())
-    G = c.hq // c.hkv
-    flops = 14.0 * c.d * 64 * 64 * G * (n_p + n_f)
-    # mandatory HBM bytes: bias (+ mask) of non-SKIP blocks in the forward and the backward, the
-    # mask scan of classification, all of dBias; the range path reads 8 B per key and plane
-    n_live_blocks = int(((np.arange((c.lq + 63) // 64)[:, None] * 64 + 63 + (c.lk - c.lq)) >=
-                         (np.arange((c.lk + 63) // 64)[None, :] * 64)).sum()) * c.b * c.hkv
-    bias_b = 2.0 * 64 * 64 * (n_p + n_f)
-    mask_b = 2.0 * 64 * 64 * n_p
-    dbias_b = 2.0 * c.b * c.hkv * c.lq * c.lk
-    out["bytes_dense"] = 2.0 * 64 * 64 * n_live_blocks + 2 * (bias_b + mask_b) + dbias_b
-    out["bytes_ranges"] = 8.0 * c.b * c.hkv * c.lk + 2 * bias_b + dbias_b
-    out["tflops_dense"] = round(flops / (out["dense_ms"] * 1e-3) / 1e12, 2)
-    out["tflops_ranges"] = round(flops / (out["ranges_ms"] * 1e-3) / 1e12, 2)
-    out["gbs_ranges"] = round(out["bytes_ranges"] / (out["ranges_ms"] * 1e-3) / 1e9, 1)
-    out["blocks_partial"], out["blocks_full"] = n_p, n_f
-    del q, k, v, do, mask, bias, dbias, ws
-    torch.cuda.empty_cache()
-    return out
-
-
-def time_classify_other(c, dma, np, torch, classify_forward, fused, t_bwd, reps=5):
-    """Classification + forward by the path the step does not use (run with `not fused`)."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-    classify_forward(fused)
+def time_topk(c, dma, torch, stream):
+    """GPU top-k mask construction (dma_topk_mask) on a fresh N(0,1) bf16 bias of the workload's shape."""
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    raw = torch.randn((c.b * c.hkv * c.lq, c.lk), generator=gen, device="cuda").to(torch.bfloat16)
+    mk, bo = torch.empty_like(raw), torch.empty_like(raw)
+    dma.dma_topk_mask(raw, c.topk, mk, bo, stream)
     torch.cuda.synchronize()
-    for r in range(reps):
-        classify_forward(fused, ev[r])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        dma.dma_topk_mask(raw, c.topk, mk, bo, stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    po = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev]).mean(axis=0)
-    return {"path": "separate dma_block_classify + dma_attn_fwd" if fused else "fused dma_attn_fwd_classify",
-            "classify_ms": round(float(po[0]), 4), "fwd_ms": round(float(po[1]), 4),
-            "classify_fwd_ms": round(float(po.sum()), 4), "step_ms_with_it": round(float(po.sum()) + t_bwd, 4)}
+    t_topk = e0.elapsed_time(e1) / reps
+    bytes_topk = 3.0 * raw.numel() * 2  # bias read once, mask and bias written
+    del raw, mk, bo
+    return {"ms": round(t_topk, 4), "gbs": round(bytes_topk / (t_topk * 1e-3) / 1e9, 1),
+            "frac_hbm": round(bytes_topk / (t_topk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "rows": c.b * c.hkv * c.lq, "lk": c.lk, "k": c.topk}
 
 
-def time_bits(c, dma, np, q, k, v, do, mask, bias, o, lse, dq, dk, dv, dbias, ws, stream, dense_ms):
-    import torch
-
-    st = torch.empty(dma.block_state_shape(c.b, c.hkv, c.lq, c.lk), dtype=torch.uint8, device="cuda")
+def time_bits(st, dma, np, torch, dense_step_ms):
+    """The step with the bit-packed PARTIAL-block mask (classify writes 512 B per PARTIAL block;
+    forward and backward read those bits instead of the bf16 mask), per phase."""
+    c, s = st.c, st.stream
+    state = torch.empty_like(st.state)
     mb = torch.empty((dma.dma_mask_bits_size(c.b, c.hkv, c.lq, c.lk),), dtype=torch.uint8, device="cuda")
     reps = 3
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps + 1)]
     for r in range(reps + 1):  # the first repetition warms up
         e = ev[r]
-        e[0].record(stream)
-        dma.dma_block_classify_bits(mask, c.b, c.hkv, c.lq, c.lk, c.causal, st, mb, stream)
-        e[1].record(stream)
-        dma.dma_attn_fwd_bits(q, k, v, mb, bias, st, c.scale_f32, c.causal, o, lse, stream)
-        e[2].record(stream)
-        dma.dma_attn_bwd_bits(q, k, v, mb, bias, st, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws, stream)
-        e[3].record(stream)
+        e[0].record(s)
+        dma.dma_block_classify_bits(st.mask, c.b, c.hkv, c.lq, c.lk, c.causal, state, mb, s)
+        e[1].record(s)
+        dma.dma_attn_fwd_bits(st.q, st.k, st.v, mb, st.bias, state, c.scale_f32, c.causal, st.o, st.lse, s)
+        e[2].record(s)
+        dma.dma_attn_bwd_bits(st.q, st.k, st.v, mb, st.bias, state, st.o, st.do, st.lse, c.scale_f32, c.causal, st.dq,
+                              st.dk, st.dv, st.dbias, st.ws, s)
+        e[3].record(s)
     torch.cuda.synchronize()
     t = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in ev[1:]])
     t = t.mean(axis=0)
-    n_p = int((st == 1).sum())
+    n_p = int((state == 1).sum())
     out = {"classify_ms": round(float(t[0]), 4), "fwd_ms": round(float(t[1]), 4), "bwd_ms": round(float(t[2]), 4),
-           "step_ms": round(float(t.sum()), 4), "dense_step_ms": round(float(sum(dense_ms)), 4),
+           "step_ms": round(float(t.sum()), 4), "dense_step_ms": round(float(dense_step_ms), 4),
            "blocks_partial": n_p,
-           # mask bytes read by forward + backward: bf16 tiles of the dense path, bits here
            "mask_bytes_dense": 2 * 2.0 * 64 * 64 * n_p, "mask_bytes_bits": 2 * 512.0 * n_p,
            "bits_bytes_written": 512.0 * n_p}
-    del st, mb
+    del state, mb
     return out
+
+
+def measured_copy_gbs(torch, mib=4096):
+    """Read + write bandwidth of a device copy of `mib` MiB (the practical HBM rate of a plain copy)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2.0 * mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)
 
 
 def main():
@@ -286,49 +404,11 @@ def main():
 
     import block_sparse_dynamic_amd as dma
     import synth
-    from synth.device import upload_dense, upload_mask_bias
 
     c = synth.CASES[args.config]
     torch.cuda.set_device(0)
-    t_gen = time.perf_counter()
-    q, k, v, do = upload_dense(c)
-    mask, bias = upload_mask_bias(c)
-    torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t_gen
-    print(f"[bench] {c.name}: inputs generated and uploaded in {t_gen:.1f} s", file=sys.stderr, flush=True)
-
-    state = torch.empty(dma.block_state_shape(c.b, c.hkv, c.lq, c.lk), dtype=torch.uint8, device="cuda")
-    o = torch.empty_like(q)
-    lse = torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dbias = torch.empty((c.b, c.hkv, c.lq, c.lk), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8,
-                     device="cuda")
-    stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-
-    fused = not args.separate_classify
-
-    def classify_forward(separate, timed=None):
-        if timed is not None:
-            timed[0].record(stream)
-        if separate:
-            dma.dma_block_classify(mask, c.b, c.hkv, c.lq, c.lk, c.causal, state, stream)
-        if timed is not None:
-            timed[1].record(stream)
-        if separate:
-            dma.dma_attn_fwd(q, k, v, mask, bias, state, c.scale_f32, c.causal, o, lse, stream)
-        else:
-            dma.dma_attn_fwd_classify(q, k, v, mask, bias, c.scale_f32, c.causal, state, o, lse, stream)
-        if timed is not None:
-            timed[2].record(stream)
-
-    def step(timed=None):
-        classify_forward(not fused, timed)
-        dma.dma_attn_bwd(q, k, v, mask, bias, state, o, do, lse, c.scale_f32, c.causal, dq, dk, dv, dbias, ws,
-                         stream)
-        if timed is not None:
-            timed[3].record(stream)
+    st = Step(c, dma, torch, np, path="fused")
+    print(f"[bench] {c.name}: inputs generated and uploaded in {st.t_gen:.1f} s", file=sys.stderr, flush=True)
 
     if args.calibrate_copy_mib > 0:  # one plain copy of known size, for counter calibration
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -337,102 +417,38 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    # ---- the contract's timed region: K steps, synchronised on both sides ----------------------
     for _ in range(args.warmup):
-        step()
+        st.run()
     torch.cuda.synchronize()
-    per = np.zeros((args.steps, 3))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [st.events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(evs[s])
+        st.run(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for s in range(args.steps):
-        e = evs[s]
-        per[s] = [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-    t_cls, t_fwd, t_bwd = per.mean(axis=0)  # ms
     ms_step = wall / args.steps * 1e3
+    per = np.array([Step.phase_ms(e) for e in evs]).mean(axis=0)
+    ph = dict(zip(Step.PHASES, per))
+    w = work_of(c, st.state, np, fused=True, has_mask=st.mask is not None)
+    tflops = (w["f_fwd"] + w["f_bwd"]) / (ms_step * 1e-3) / 1e12
+    mand = w["b_cls"] + w["b_fwd"] + w["b_bwd"]
+    t_bwd = ph["bwd_prepare"] + ph["bwd_main"] + ph["bwd_dq"]
 
-    # the other classification path (separate pass or fused), outside the step, same inputs
-    # (left out of counter and trace runs, --no-next, which must hold the step's kernels only)
-    classify_other = None
-    if not args.no_next and args.calibrate_copy_mib == 0:
-        classify_other = time_classify_other(c, dma, np, torch, classify_forward, fused, t_bwd)
-
-
-    # Next-row measurement, outside the step: the top-k mask construction (dma_topk_mask) on
-    # a fresh N(0,1) bf16 bias of the workload's shape, k = the workload's top-k.
-    next_rows = {}
-    if c.mask == "topk" and not args.no_next and args.calibrate_copy_mib == 0:
-        gen = torch.Generator(device="cuda").manual_seed(1234)
-        raw = torch.randn((c.b * c.hkv * c.lq, c.lk), generator=gen, device="cuda").to(torch.bfloat16)
-        mk, bo = torch.empty_like(raw), torch.empty_like(raw)
-        dma.dma_topk_mask(raw, c.topk, mk, bo, stream)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 3
-        e0.record(stream)
-        for _ in range(reps):
-            dma.dma_topk_mask(raw, c.topk, mk, bo, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t_topk = e0.elapsed_time(e1) / reps
-        bytes_topk = 3.0 * raw.numel() * 2  # bias read once, mask and bias written
-        next_rows["topk_mask"] = {"ms": round(t_topk, 4), "gbs": round(bytes_topk / (t_topk * 1e-3) / 1e9, 1),
-                                  "frac_hbm": round(bytes_topk / (t_topk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                  "rows": c.b * c.hkv * c.lq, "lk": c.lk, "k": c.topk}
-        del raw, mk, bo
-
-    # Next-row measurement, outside the step: the same step with the bit-packed PARTIAL-block
-    # mask (classification writes 512 B per PARTIAL block; forward and backward read those bits
-    # instead of the bf16 mask), per phase over a few repetitions.
-    if c.mask != "none" and not args.no_next and args.calibrate_copy_mib == 0:
-        next_rows["mask_bits"] = time_bits(c, dma, np, q, k, v, do, mask, bias, o, lse, dq, dk, dv, dbias, ws,
-                                           stream, (t_cls, t_fwd, t_bwd))
-
-    # Next-row measurement, outside the step: column-range mask input on the Doc-packed workload
-    # (the pages' column-wise form), one classify + forward + backward with the dense mask and
-    # with the ranges, each timed over a few repetitions.
-    if not args.no_next and args.calibrate_copy_mib == 0:
-        next_rows["column_ranges"] = time_ranges(args, dma, synth, np)
-
-    n_skip, n_p, n_f = block_counts(state)
-    n_ns = n_p + n_f
-    G, d = c.hq // c.hkv, c.d
-    f_fwd = 4.0 * d * 64 * 64 * G * n_ns
-    f_bwd = 10.0 * d * 64 * 64 * G * n_ns
-    # blocks wholly excluded by causality are never read by classification
-    nqb, nkb = (c.lq + 63) // 64, (c.lk + 63) // 64
-    qb = np.arange(nqb)[:, None]
-    kb = np.arange(nkb)[None, :]
-    live = (kb * 64 <= np.minimum(qb * 64 + 63, c.lq - 1) + (c.lk - c.lq)) if c.causal else np.ones((nqb, nkb), bool)
-    n_live = int(live.sum()) * c.b * c.hkv
-    has_mask = mask is not None
-    # a separate classification reads the mask of every causally live block once more; fused,
-    # the forward's own mask reads classify
-    b_cls = 2.0 * 64 * 64 * n_live if (has_mask and not fused) else 0.0
-    b_fwd = 2.0 * 64 * 64 * (2 * n_p + n_f)
-    b_bwd = b_fwd + 2.0 * c.b * c.hkv * c.lq * c.lk
-    tflops = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    gbs = (b_cls + b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9
-
-    # dominant launch: the one with the largest share of the step
-    phases = {"bwd": (t_bwd, f_bwd, "dma_attn_bwd (bwd_pre + kt + pair_base + bwd_main + dq)"),
-              "fwd": (t_fwd, f_fwd, "dma_attn_fwd_classify (fwd_kernel, classification fused)" if fused else
-                      "dma_attn_fwd (fwd_kernel)")}
-    dom = max(phases, key=lambda k: phases[k][0])
-    t_dom, f_dom, dom_name = phases[dom]
-    achieved = f_dom / (t_dom * 1e-3) / 1e12
+    # dominant kernel: the backward main kernel, timed by the events around it in the K steps
+    achieved = w["f_bwd_main"] / (ph["bwd_main"] * 1e-3) / 1e12
     traffic = None  # measured HBM bytes per launch, only while the kernels are the ones measured
     if args.traffic_json and os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             tj = json.load(f)
         if tj.get("source_hash") == kernel_source_hash():
-            traffic = tj["bytes_per_launch"].get(dom)
+            traffic = tj["bytes_per_launch"].get("bwd_main")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
-                "ms_per_launch": round(t_dom, 4)}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "bwd_main_kernel (dma_attn_bwd_part DMA_BWD_MAIN): S, dP, dV, dK products",
+                "algorithmic_flop_per_launch": w["f_bwd_main"], "ms_per_launch": round(float(ph["bwd_main"]), 4)}
 
     line = {
         "metric": "fwd+bwd effective TFLOP/s (unmasked tiles) + HBM GB/s, L=16K GQA top-k",
@@ -446,26 +462,53 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "precision": "bf16 inputs and MFMA operands (P V with P as two bf16 parts), fp32 accumulation and softmax",
         "data": "synthetic (seeded; N(0,1) q/k/v/dO/bias, top-k mask from the bias)",
-        "config": {"workload": f"{c.name}: b={c.b} L={c.lq} Hq={c.hq} Hkv={c.hkv} d={c.d} "
-                               f"{'top-k ' + str(c.topk) if c.mask == 'topk' else c.mask} mask, "
-                               f"{'causal' if c.causal else 'non-causal'}",
-                   "b": c.b, "seq_len": c.lq, "hq": c.hq, "hkv": c.hkv, "d": c.d,
-                   "blocks_nonskip": n_ns, "blocks_partial": n_p, "blocks_full": n_f, "blocks_skip": n_skip},
-        "hbm_gbs_mandatory": round(gbs, 1),
-        "classify_fused": fused,
-        "phases_ms": {"classify": round(t_cls, 4), "fwd": round(t_fwd, 4), "bwd": round(t_bwd, 4)},
-        "phases_tflops": {"fwd": round(f_fwd / (t_fwd * 1e-3) / 1e12, 2),
-                          "bwd": round(f_bwd / (t_bwd * 1e-3) / 1e12, 2)},
-        "phases_gbs_mandatory": {"classify": round(b_cls / (t_cls * 1e-3) / 1e9, 1) if b_cls > 0 else None,
-                                 "fwd": round(b_fwd / (t_fwd * 1e-3) / 1e9, 1),
-                                 "bwd": round(b_bwd / (t_bwd * 1e-3) / 1e9, 1)},
+        "config": {"workload": describe(c), "b": c.b, "seq_len": c.lq, "hq": c.hq, "hkv": c.hkv, "d": c.d,
+                   "blocks_nonskip": w["blocks_nonskip"], "blocks_partial": w["blocks_partial"],
+                   "blocks_full": w["blocks_full"]},
+        "hbm_gbs_mandatory": round(mand / (ms_step * 1e-3) / 1e9, 1),
+        "classify_fused": True,
+        "phases_ms": {k: round(float(v), 4) for k, v in ph.items()},
+        "phases_tflops": {"fwd": round(w["f_fwd"] / ((ph["classify"] + ph["fwd"]) * 1e-3) / 1e12, 2),
+                          "bwd": round(w["f_bwd"] / (t_bwd * 1e-3) / 1e12, 2)},
         "roofline": roofline,
-        "classify_other": classify_other,
-        "next_rows": next_rows,
     }
+
+    if not args.no_next and args.calibrate_copy_mib == 0:
+        line["next_rows"] = {}
+        line["next_rows"]["mask_bits"] = time_bits(st, dma, np, torch, ms_step)
+        if c.mask == "topk":
+            line["next_rows"]["topk_mask"] = time_topk(c, dma, torch, st.stream)
+    if args.calibrate_copy_mib == 0:
+        line["measured_peaks"] = {"hbm_copy_gbs": measured_copy_gbs(torch), "hbm_spec_gbs": PEAK_HBM_GBS,
+                                  "mfma_bf16_spec_tflops": PEAK_BF16_TFLOPS}
+    head_method = None
+    if not args.no_workloads and args.calibrate_copy_mib == 0:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        if c.name in args.workloads.split(","):
+            head_method = method_measure(st, np, torch, flush)
+        st.free()
+        method = {}
+        for name in args.workloads.split(","):
+            if name == c.name:
+                method[name] = head_method
+                continue
+            wc = synth.CASES[name]
+            paths = ("separate", "ranges") if wc.mask == "doc" else ("fused",)
+            for path in paths:
+                print(f"[bench] {name} ({path})", file=sys.stderr, flush=True)
+                ws = Step(wc, dma, torch, np, path=path)
+                method[name if path == paths[0] else f"{name}_{path}"] = method_measure(
+                    ws, np, torch, flush, bound="hbm" if wc.mask == "doc" else "mfma")
+                ws.free()
+                del ws
+        line["method"] = method
+        del flush
+    else:
+        st.free()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(c, args.cpu_blocks, f_fwd + f_bwd)
+        line["cpu_baseline"] = cpu_baseline(c, args.cpu_blocks, w["f_fwd"] + w["f_bwd"])
     print(json.dumps(line), flush=True)
 
 

@@ -69,6 +69,10 @@ _lib.dma_attn_fwd_bits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i6
 _lib.dma_attn_bwd_bits.restype = _i32
 _lib.dma_attn_bwd_bits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                    _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dma_attn_bwd_part.restype = _i32
+_lib.dma_attn_bwd_part.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                   _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+BWD_PREPARE, BWD_MAIN, BWD_DQ = 0, 1, 2
 _lib.dma_attn_bwd_noalloc.restype = _i32
 _lib.dma_attn_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _f32, _i32, _vp, _vp, _vp, _vp, _vp]
@@ -214,6 +218,24 @@ def dma_attn_bwd(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, i
                            _ptr(dbias, "dbias", torch.bfloat16), _ptr(workspace, "workspace"),
                            workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dma_attn_bwd", st)
+
+
+def dma_attn_bwd_part(part: int, q, k, v, mask, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq,
+                      dk, dv, dbias, workspace, stream=None) -> None:
+    """One phase of dma_attn_bwd (BWD_PREPARE, BWD_MAIN, BWD_DQ, run in this order)."""
+    b, lq, lk, hq, hkv, d = _shapes("dma_attn_bwd_part", q, k, v, planes=(("mask", mask), ("bias", bias), ("dbias", dbias)),
+                                    qlike=(("o", o), ("dout", dout), ("dq", dq)), kvlike=(("dk", dk), ("dv", dv)),
+                                    lse=lse, state=block_state)
+    st = _lib.dma_attn_bwd_part(int(part), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                _ptr(v, "v", torch.bfloat16), _ptr(mask, "mask", torch.bfloat16),
+                                _ptr(bias, "bias", torch.bfloat16), _ptr(block_state, "block_state", torch.uint8),
+                                _ptr(o, "o", torch.bfloat16), _ptr(dout, "dout", torch.bfloat16),
+                                _ptr(lse, "lse", torch.float32), b, lq, lk, hq, hkv, d, float(scale),
+                                int(bool(is_causal)), _ptr(dq, "dq", torch.bfloat16), _ptr(dk, "dk", torch.bfloat16),
+                                _ptr(dv, "dv", torch.bfloat16), _ptr(dbias, "dbias", torch.bfloat16),
+                                _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check("dma_attn_bwd_part", st)
 
 
 def dma_attn_bwd_noalloc(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq, dk, dv,
@@ -383,6 +405,7 @@ __all__ = [
     "dma_block_size", "dma_status_string", "dma_block_classify", "dma_attn_fwd", "dma_attn_bwd_workspace_size",
     "dma_attn_bwd", "dma_attention", "block_state_shape", "DMAError", "LIB_PATH", "HEADER_PATH",
     "dma_block_classify_ranges", "dma_attn_fwd_ranges", "dma_attn_bwd_ranges", "dma_topk_mask", "dma_mask_bits_size",
-    "dma_block_classify_bits", "dma_attn_fwd_bits", "dma_attn_bwd_bits", "dma_attn_bwd_noalloc",
+    "dma_block_classify_bits", "dma_attn_fwd_bits", "dma_attn_bwd_bits", "dma_attn_bwd_noalloc", "dma_attn_bwd_part",
+    "BWD_PREPARE", "BWD_MAIN", "BWD_DQ",
     "NOALLOC_SCRATCH_BYTES",
 ]

@@ -238,7 +238,8 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   const int32_t* rend, const uint8_t* mbits, const uint16_t* bias, const uint8_t* block_state,
                   const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv,
                   int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
-                  void* workspace, size_t workspace_bytes, void* stream, bool validate_only = false) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool validate_only = false,
+                  int parts = dma::kBwdAll) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !dout || !lse || !dq || !dk || !dv || !workspace) return DMA_ERR_INVALID_ARGUMENT;
@@ -287,7 +288,7 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.d = d;
   a.scale = scale;
   a.causal = is_causal;
-  return hip_status(dma::launch_bwd(a, (hipStream_t)stream));
+  return hip_status(dma::launch_bwd(a, (hipStream_t)stream, parts));
 }
 }  // namespace
 
@@ -299,6 +300,20 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
   return attn_bwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d,
                        scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+}
+
+int dma_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,
+                      const uint16_t* bias, const uint8_t* block_state, const uint16_t* o, const uint16_t* dout,
+                      const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                      float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int parts = 0;
+  if (part == DMA_BWD_PREPARE) parts = dma::kBwdPrepare;
+  else if (part == DMA_BWD_MAIN) parts = dma::kBwdMain;
+  else if (part == DMA_BWD_DQ) parts = dma::kBwdDq;
+  else return DMA_ERR_INVALID_ARGUMENT;
+  return attn_bwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d,
+                       scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream, false, parts);
 }
 
 int dma_attn_bwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* mask_bits,

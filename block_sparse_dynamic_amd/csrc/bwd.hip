@@ -236,6 +236,38 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// dBias zeros of one 64-row query block z = plane * nqb + qb (256 threads): every 128-key pair
+// that no compute workgroup visits for it, i.e. a pair SKIP in both halves or one that
+// causality leaves without a valid position, gets 64 rows x 128 keys of zeros (clipped to lq and
+// lk), 16-byte stores, 256 bytes per row.  These workgroups follow the compute workgroups in the
+// grid, so the streaming writes fill the causal tail of the compute.  `stc` is 2048 bytes of LDS
+// that caches the block states of the row.
+__device__ void zero_fill_dbias(const BwdParams& p, int z, uint8_t* stc) {
+  const int plane = z / p.nqb, qb = z % p.nqb, tid = threadIdx.x;
+  const int64_t i0 = (int64_t)qb * kBlock;
+  const uint8_t* st_row = p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
+  uint16_t* base = p.dbias + (int64_t)plane * p.lq * p.lk + i0 * p.lk;
+  const int npl = (int)live_pairs(qb, p.lq, p.lk, p.causal);
+  const int rows = (int)min((int64_t)kBlock, p.lq - i0);
+  constexpr int kChunk = 2048;  // key blocks whose states are cached at a time
+  for (int kb_lo = 0; kb_lo < p.nkb; kb_lo += kChunk) {
+    __syncthreads();  // every reader of the previous chunk is done
+    for (int j = tid; j < kChunk; j += 256) stc[j] = kb_lo + j < p.nkb ? st_row[kb_lo + j] : kSkip;
+    __syncthreads();
+    const int KB_end = min(p.nkb2, (kb_lo + kChunk) / 2);
+    for (int KB = kb_lo / 2; KB < KB_end; ++KB) {
+      const bool dead = KB >= npl || (stc[2 * KB - kb_lo] == kSkip && stc[2 * KB + 1 - kb_lo] == kSkip);
+      if (!dead) continue;
+      for (int t2 = tid; t2 < kBlock * (kKeys / 8); t2 += 256) {
+        const int r = t2 / (kKeys / 8), c = t2 % (kKeys / 8);
+        const int64_t j = (int64_t)KB * kKeys + c * 8;
+        if (r < rows && j < p.lk)
+          *reinterpret_cast<u32x4*>(base + (int64_t)r * p.lk + j) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+}
+
 template <int D, int MK, int HPI>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   using Smem = BwdSmem<D, HPI>;
@@ -245,6 +277,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   constexpr int CPR = D / 8;            // 16-byte chunks per Q row
   __shared__ Smem sm;
 
+  if ((int)blockIdx.x >= p.total_wg) {  // a zero-fill workgroup: no compute, no barrier shared with others
+    zero_fill_dbias(p, (int)blockIdx.x - p.total_wg, &sm.st[0][0]);
+    return;
+  }
   const int w = blockIdx.x;
   const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
   const int plane = t / p.nkb2, KB = t % p.nkb2;  // low key blocks (most query blocks under causality) first
@@ -336,22 +372,14 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     lds_barrier();
     cache_lo = lo;
   };
-  // next query block with a non-SKIP half at or before `from`; rows of blocks that are SKIP
-  // in both halves get their zeros here
+  // next query block with a non-SKIP half at or before `from` (the dBias zeros of the blocks
+  // it passes over are written by the zero-fill workgroups)
   auto next_qb = [&](int from, uint8_t& s0, uint8_t& s1) -> int {
     for (int qb = from; qb >= 0; --qb) {
       if (qb < cache_lo) fill_cache(qb);
       s0 = (uint8_t)__builtin_amdgcn_readfirstlane(sm.st[0][qb - cache_lo]);
       s1 = (uint8_t)__builtin_amdgcn_readfirstlane(sm.st[1][qb - cache_lo]);
       if (s0 != kSkip || s1 != kSkip) return qb;
-      if (p.dbias != nullptr) {
-        for (int task = tid; task < kBlock * (kKeys / 8); task += 256) {
-          const int r = task / (kKeys / 8), c = task % (kKeys / 8);
-          const int64_t i = (int64_t)qb * kBlock + r, j = (int64_t)kb0 * kBlock + c * 8;
-          if (i < p.lq && j < p.lk)
-            *reinterpret_cast<u32x4*>(p.dbias + plane_off + i * p.lk + j) = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
     }
     return -1;
   };
@@ -1027,12 +1055,12 @@ static hipError_t launch_dq_t(const DqParams& q, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   const int64_t rows = a.b * a.lq * a.hq;
   const int nqb = (int)((a.lq + kBlock - 1) / kBlock), nkb = (int)((a.lk + kBlock - 1) / kBlock);
   const int nkb2 = (nkb + 1) / 2;
   const int64_t ktrow = (int64_t)nkb2 * 128;
-  {
+  if (parts & kBwdPrepare) {
     const int64_t threads = rows * (a.d / 8);
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.o, a.dout,
                        a.lse_in, a.nd, a.nl2, rows, a.lq, a.hq, (int)a.d);
@@ -1075,7 +1103,10 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.causal = a.causal;
   const int MK = a.rstart != nullptr ? kMaskRanges : a.mbits != nullptr ? kMaskBits : kMaskDense;
-  auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(p.total_wg), dim3(256), 0, stream, p); };
+  if (parts & kBwdMain) {
+  // the compute workgroups, then (with a dBias output) one zero-fill workgroup per query block
+  const int64_t grid = p.total_wg + (a.dbias != nullptr ? a.b * a.hkv * (int64_t)nqb : 0);
+  auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, p); };
   // an item covers two heads when the group size is even
   auto launch_d = [&](auto dconst) {
     constexpr int D = decltype(dconst)::value;
@@ -1093,6 +1124,8 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   else launch_d(std::integral_constant<int, 128>{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  }
+  if (!(parts & kBwdDq)) return hipSuccess;
 
   DqParams q;
   q.state = a.state;

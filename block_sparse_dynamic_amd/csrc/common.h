@@ -200,5 +200,8 @@ __host__ __device__ inline int64_t live_pairs(int64_t qb, int64_t lq, int64_t lk
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_topk(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out,
                        uint16_t* bias_out, hipStream_t stream);
-hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
+// The backward's three phases (a bit set of them): the row terms, K^T and dS tile offsets; the
+// main kernel (dK, dV, dBias and the dS chunks); dQ from the dS chunks.
+constexpr int kBwdPrepare = 1, kBwdMain = 2, kBwdDq = 4, kBwdAll = 7;
+hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts = kBwdAll);
 }  // namespace dma

@@ -189,6 +189,25 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One phase of dma_attn_bwd, for callers that time or schedule the phases
+ * separately (the benchmark times the main kernel on its own).  Calling
+ * DMA_BWD_PREPARE, DMA_BWD_MAIN and DMA_BWD_DQ in this order on one stream with
+ * the same arguments and workspace is dma_attn_bwd, bit for bit:
+ *   DMA_BWD_PREPARE  the row terms -rowsum(dout * o) and -lse log2(e), K
+ *                    transposed and the dS tile offsets, into the workspace
+ *   DMA_BWD_MAIN     dk, dv and dbias, and the nonzero dS chunks into the workspace
+ *   DMA_BWD_DQ       dq from the dS chunks
+ * Arguments and errors are those of dma_attn_bwd (every call validates all of
+ * them); an unknown part is DMA_ERR_INVALID_ARGUMENT.
+ */
+enum { DMA_BWD_PREPARE = 0, DMA_BWD_MAIN = 1, DMA_BWD_DQ = 2 };
+int dma_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,
+                      const uint16_t* bias, const uint8_t* block_state, const uint16_t* o, const uint16_t* dout,
+                      const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                      float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass that allocates nothing and takes no workspace, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  Arguments, outputs and errors are

@@ -352,3 +352,13 @@ def test_noalloc_validates_before_touching_the_device(lib):
     assert call(b=2, lq=16384, lk=16384, hq=16, hkv=4) == WS_SMALL
     need = lib.dma_attn_bwd_workspace_size(1, 2048, 2048, 16, 4, 128, 1)
     assert need > 64 << 20 and call(lq=2048, lk=2048, hq=16, hkv=4) == WS_SMALL
+
+
+def test_bwd_part_rejects_unknown_part(lib):
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    f = lib.dma_attn_bwd_part
+    f.argtypes = [i32] + [vp] * 9 + [i64] * 6 + [f32, i32] + [vp] * 5 + [sz, vp]
+    args = [P] * 9 + [1, 128, 128, 4, 2, 128, 0.1, 1] + [P] * 5 + [1 << 40, None]
+    assert f(3, *args) == INVALID
+    assert f(-1, *args) == INVALID
+    assert f(1, *args[:9], 1, 128, 128, 4, 2, 96, 0.1, 1, *args[17:]) == UNSUPPORTED  # validation runs first

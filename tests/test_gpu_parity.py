@@ -287,3 +287,26 @@ def test_v_beyond_fp16_range_at_masked_keys():
     dc, _ = H.check_small_case(c, prepare=prep)
     st = dc.state.cpu().numpy()
     assert (st == oracle.PARTIAL).any()
+
+
+def test_backward_phases_equal_one_call():
+    """dma_attn_bwd_part: the three phases in order on one stream are dma_attn_bwd, bit for bit."""
+    import block_sparse_dynamic_amd as dma
+    import gpu_harness as H
+
+    c = Case("bwd_parts", 37, 2, 200, 200, 8, 2, 128, True, "blocks")
+    dc = H.DeviceCase(c)
+    dc.classify()
+    dc.forward()
+    dc.backward()
+    ref = [H.bits(t) for t in (dc.dq, dc.dk, dc.dv, dc.dbias)]
+    dq, dk, dv = torch.empty_like(dc.q), torch.empty_like(dc.k), torch.empty_like(dc.v)
+    dbias = torch.full_like(dc.dbias, float("nan"))
+    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8,
+                     device="cuda")
+    for part in (dma.BWD_PREPARE, dma.BWD_MAIN, dma.BWD_DQ):
+        dma.dma_attn_bwd_part(part, dc.q, dc.k, dc.v, dc.mask, dc.bias, dc.state, dc.o, dc.do, dc.lse, c.scale_f32,
+                              c.causal, dq, dk, dv, dbias, ws)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dbias"), ref, [H.bits(t) for t in (dq, dk, dv, dbias)]):
+        assert np.array_equal(a, b), f"{name} differs"
