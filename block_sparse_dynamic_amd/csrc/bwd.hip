@@ -182,11 +182,42 @@ constexpr int kKeys = 128;  // keys per workgroup: two classification blocks
 constexpr int kRows = 32;   // query rows per item (half a classification block)
 constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LDS at a time
 
+constexpr int kWaves = 8;                 // waves of a backward workgroup: 16 keys each
+constexpr int kThreads = kWaves * 64;
+constexpr int kWKeys = kKeys / kWaves;    // keys per wave
+
+// LDS layouts of the backward tiles.  A Q or dO tile [32 rows][D] and a raw bias or mask tile
+// [32 rows][128 keys] keep the 16-byte chunk c of row r at chunk c ^ bx<chunks per row>(r),
+// rows unpadded.  The 16x16x32 operand reads of this kernel take, per 16 lanes, one chunk of
+// 16 aligned rows (128-bit reads), and per 32 lanes, two adjacent chunks of 8 aligned rows
+// (transposing 64-bit reads); LDS serves 64 banks of 4 bytes.  With 16 chunks a row (256
+// bytes) the XOR 2 (r%8) + (r/8)%2 puts both patterns on 64 distinct banks; with 8 chunks (128
+// bytes, two rows span the banks) 2 ((r/2)%4) + (r/8)%2 does.  Any XOR suits the DMA loads,
+// which write whole rows in lane order.
+template <int CPR>
+__device__ __forceinline__ int bx(int r) {
+  if constexpr (CPR == 16) {
+    return ((r & 7) << 1) | ((r >> 3) & 1);
+  } else {
+    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  }
+}
+template <int W>  // W bf16 a row
+__device__ __forceinline__ int bt_off(int row, int col) {
+  return row * W + ((((col >> 3) ^ bx<W / 8>(row)) << 3) | (col & 7));
+}
+// The dS^T tile [128 keys][32 queries] keeps the 8-byte unit u of row r at unit u ^ 2 ((r/4)%4):
+// the dS writes (16 aligned rows x units {u, u+1} per 32 lanes) and the export's transposing
+// reads (4 aligned rows x all 8 units per 32 lanes) both touch 64 distinct banks.
+__device__ __forceinline__ int st_off(int row, int col) {
+  return (row << 5) | ((((col >> 2) ^ (((row >> 2) & 3) << 1)) << 2) | (col & 3));
+}
+
 template <int D, int HPI>
 struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay single 16-byte LDS accesses
-  static constexpr int kTile = kRows * D;       // Q or dO tile [row][d], tile_off<D> layout
-  static constexpr int kBTile = kRows * kKeys;  // raw bias or mask tile [row][key], swz128 layout
-  static constexpr int kSTile = kKeys * kRows;  // dS^T [key][query], swz32 layout
+  static constexpr int kTile = kRows * D;       // Q or dO tile [row][d], bt_off<D> layout
+  static constexpr int kBTile = kRows * kKeys;  // raw bias or mask tile [row][key], bt_off<128> layout
+  static constexpr int kSTile = kKeys * kRows;  // dS^T [key][query], st_off layout
   // Two buffers each: the current item's and the next item's, which loads meanwhile; an item
   // covers HPI consecutive heads of the group.
   uint16_t q[2][HPI][kTile];
@@ -196,10 +227,10 @@ struct alignas(16) BwdSmem {  // 16-byte aligned so tile reads and writes stay s
   uint16_t s[2][HPI][kSTile];
   float nl2[2][HPI][64];  // -lse * log2(e) of the item's rows (rows 32..63 take the out-of-range lanes of the load)
   float nd[2][HPI][64];   // -D = -rowsum(dO * O)
-  // Initial values of the S accumulator in the S layout, one slot per lane: bias / scale on
+  // Initial values of the S accumulators in the S layout, one slot per lane: bias / scale on
   // valid pairs, -inf (signed so that scale * it is -inf) elsewhere.  Written when a query
   // block starts, read by the same lane for every head of the group.
-  f32x4 beff[4][4][64];  // [wave][row group][lane]
+  f32x4 beff[kWaves][2][64];   // [wave][16-row tile][lane]
   int64_t pb[kStateChunk];     // pair_base of the same query blocks (first dS tile pair of each)
   uint8_t st[2][kStateChunk];  // block states of the two key blocks for a range of query blocks
 };
@@ -236,12 +267,12 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// dBias zeros of one 64-row query block z = plane * nqb + qb (256 threads): every 128-key pair
-// that no compute workgroup visits for it, i.e. a pair SKIP in both halves or one that
-// causality leaves without a valid position, gets 64 rows x 128 keys of zeros (clipped to lq and
-// lk), 16-byte stores, 256 bytes per row.  These workgroups follow the compute workgroups in the
-// grid, so the streaming writes fill the causal tail of the compute.  `stc` is 2048 bytes of LDS
-// that caches the block states of the row.
+// dBias zeros of one 64-row query block z = plane * nqb + qb: every 128-key pair that no
+// compute workgroup visits for it, i.e. a pair SKIP in both halves or one that causality leaves
+// without a valid position, gets 64 rows x 128 keys of zeros (clipped to lq and lk), 16-byte
+// stores, 256 bytes per row.  These workgroups follow the compute workgroups in the grid, so the
+// streaming writes fill the causal tail of the compute.  `stc` is 2048 bytes of LDS that caches
+// the block states of the row.
 __device__ void zero_fill_dbias(const BwdParams& p, int z, uint8_t* stc) {
   const int plane = z / p.nqb, qb = z % p.nqb, tid = threadIdx.x;
   const int64_t i0 = (int64_t)qb * kBlock;
@@ -252,13 +283,13 @@ __device__ void zero_fill_dbias(const BwdParams& p, int z, uint8_t* stc) {
   constexpr int kChunk = 2048;  // key blocks whose states are cached at a time
   for (int kb_lo = 0; kb_lo < p.nkb; kb_lo += kChunk) {
     __syncthreads();  // every reader of the previous chunk is done
-    for (int j = tid; j < kChunk; j += 256) stc[j] = kb_lo + j < p.nkb ? st_row[kb_lo + j] : kSkip;
+    for (int j = tid; j < kChunk; j += kThreads) stc[j] = kb_lo + j < p.nkb ? st_row[kb_lo + j] : kSkip;
     __syncthreads();
     const int KB_end = min(p.nkb2, (kb_lo + kChunk) / 2);
     for (int KB = kb_lo / 2; KB < KB_end; ++KB) {
       const bool dead = KB >= npl || (stc[2 * KB - kb_lo] == kSkip && stc[2 * KB + 1 - kb_lo] == kSkip);
       if (!dead) continue;
-      for (int t2 = tid; t2 < kBlock * (kKeys / 8); t2 += 256) {
+      for (int t2 = tid; t2 < kBlock * (kKeys / 8); t2 += kThreads) {
         const int r = t2 / (kKeys / 8), c = t2 % (kKeys / 8);
         const int64_t j = (int64_t)KB * kKeys + c * 8;
         if (r < rows && j < p.lk)
@@ -268,13 +299,24 @@ __device__ void zero_fill_dbias(const BwdParams& p, int z, uint8_t* stc) {
   }
 }
 
+// One workgroup per (batch, kv head, 128 keys); eight waves own 16 keys each.  The products are
+// v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16 and k = (l/16)*8..+7; B: column l%16, the
+// same k; C: column l%16, rows (l/16)*4..+3).  S = Q K^T and dP = dO V^T, as two 16-row tiles
+// with the wave's 16 keys as columns, leave each lane one key and 8 query rows: rows 4g..4g+3 of
+// both tiles (g = lane/16).  Taken with that row order as the contraction index, those 8 values
+// are the A operand of dV = P^T dO and dK = dS^T Q as they stand, and the B operands (dO, Q: 8
+// rows of one d column per lane) come from the row-major tiles by two transposing reads.  With
+// 16 keys a wave's K, V, dK and dV take 96 registers, so two waves share a SIMD: one's vector
+// and memory work fills the other's idle issue cycles.
 template <int D, int MK, int HPI>
-__global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   using Smem = BwdSmem<D, HPI>;
   constexpr int SR = kRows;
   constexpr int RPL = 512 / D;          // tile rows filled by one wave load (1 KB): 4 or 8
-  constexpr int QL = kRows / RPL / 4;   // wave loads per Q (or dO) tile and wave: 2 or 1
+  constexpr int NLT = kRows / RPL;      // wave loads per Q (or dO) tile: 8 or 4
   constexpr int CPR = D / 8;            // 16-byte chunks per Q row
+  constexpr int KS = D / 32;            // k-steps of the S and dP products
+  constexpr int DT = D / 16;            // 16-wide d tiles of dK and dV
   __shared__ Smem sm;
 
   if ((int)blockIdx.x >= p.total_wg) {  // a zero-fill workgroup: no compute, no barrier shared with others
@@ -290,9 +332,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   // wave and the block states below are uniform across a wave; readfirstlane tells the compiler
   // so, which keeps the loop control and the buffer resources in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int half = wave >> 1;           // which 64-key classification block this wave is in
-  const int key_loc = wave * 32 + l32;  // key of this lane inside the 128
+  const int l16 = lane & 15, g4 = lane >> 4;  // a lane's key (column) and row group
+  const int half = wave >> 2;                 // which 64-key classification block this wave is in
+  const int key_loc = wave * kWKeys + l16;    // key of this lane inside the 128
   const int64_t key_abs = (int64_t)kb0 * kBlock + key_loc;
   const int64_t shift = p.lk - p.lq;
   const int64_t plane_off = (int64_t)plane * p.lq * p.lk;
@@ -308,7 +350,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   {
     constexpr int kZero = (int)(sizeof(Smem) / 16);
     u32x4* z = reinterpret_cast<u32x4*>(&sm.q[0][0][0]);
-    for (int i = tid; i < kZero; i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < kZero; i += kThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
   }
 
   // Is each of the two key blocks non-SKIP for some query block?  The K and V rows of a key
@@ -317,7 +359,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   bool live[2];
   {
     int any0 = 0, any1 = 0;
-    for (int qb = tid; qb < p.nqb; qb += 256) {
+    for (int qb = tid; qb < p.nqb; qb += kThreads) {
       any0 |= st_col[(int64_t)qb * p.nkb] != kSkip;
       if (has_kb1) any1 |= st_col[(int64_t)qb * p.nkb + 1] != kSkip;
     }
@@ -333,20 +375,20 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     kre = p.rend[(int64_t)plane * p.lk + j];
   }
 
-  // this lane's key rows of K and V, the B operands of S = Q K^T and dP = dO V^T
-  // (d = s*16 + hi*8 ..), held in registers for the whole kernel
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // this lane's key of K and V, the B operands of S = Q K^T and dP = dO V^T (k-step ks: d =
+  // ks*32 + g4*8 ..), held in registers for the whole kernel
+  bf16x8 kreg[KS], vreg[KS];
   {
-    const int64_t off = ((bidx * p.lk + key_abs) * p.hkv + g) * D + hi * 8;
+    const int64_t off = ((bidx * p.lk + key_abs) * p.hkv + g) * D + g4 * 8;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
       if (key_abs < p.lk && live[half]) {
-        kw = *reinterpret_cast<const u32x4*>(p.k + off + s * 16);
-        vw = *reinterpret_cast<const u32x4*>(p.v + off + s * 16);
+        kw = *reinterpret_cast<const u32x4*>(p.k + off + ks * 32);
+        vw = *reinterpret_cast<const u32x4*>(p.v + off + ks * 32);
       }
-      kreg[s] = __builtin_bit_cast(bf16x8, kw);
-      vreg[s] = __builtin_bit_cast(bf16x8, vw);
+      kreg[ks] = __builtin_bit_cast(bf16x8, kw);
+      vreg[ks] = __builtin_bit_cast(bf16x8, vw);
     }
   }
 
@@ -358,8 +400,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   auto fill_cache = [&](int qb_hi) {
     lds_barrier();  // every reader of the previous chunk is done
     const int lo = max(0, qb_hi - kStateChunk + 1);
-    for (int t = tid; t < 2 * kStateChunk; t += 256) {
-      const int hf = t / kStateChunk, j = t % kStateChunk, qb = lo + j;
+    for (int t2 = tid; t2 < 2 * kStateChunk; t2 += kThreads) {
+      const int hf = t2 / kStateChunk, j = t2 % kStateChunk, qb = lo + j;
       uint8_t v = kSkip;
       // A pair that causality leaves no valid position for this query block (KB at or past its
       // live pairs) owns no dS slot: it is SKIP whatever the bitmap says, so a bitmap classified
@@ -384,28 +426,27 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     return -1;
   };
 
-  // Per-lane byte offsets of the item loads.  Wave load n of this wave fills tile rows
-  // (wave * loads + n) * rows-per-load onwards; lane l lands on physical chunk l % chunks-per-row
-  // of row l / chunks-per-row there and fetches the logical chunk the swizzle keeps at that
-  // slot.  The item's base and the rows it may read (past lq the range check returns nothing)
-  // go into the buffer resource.
-  uint32_t qv[QL];
-#pragma unroll
-  for (int n = 0; n < QL; ++n) {
-    const int r = (wave * QL + n) * RPL + lane / CPR;
-    const int c = (lane % CPR) ^ tile_xor<D>(r);
-    qv[n] = (uint32_t)r * (uint32_t)(p.hq * D * 2) + (uint32_t)c * 16u;
+  // Per-lane byte offsets of the item loads.  Wave load n fills tile rows n * rows-per-load
+  // onwards; lane l lands on physical chunk l % chunks-per-row of row l / chunks-per-row there
+  // and fetches the logical chunk the swizzle keeps at that slot.  The item's base and the rows
+  // it may read (past lq the range check returns nothing) go into the buffer resource.  Wave w
+  // does wave load w of each Q and dO tile (D = 64: the first four waves).
+  const bool loads_q = wave < NLT;
+  uint32_t qv;
+  {
+    const int r = (loads_q ? wave : 0) * RPL + lane / CPR;
+    const int c = (lane % CPR) ^ bx<CPR>(r);
+    qv = (uint32_t)r * (uint32_t)(p.hq * D * 2) + (uint32_t)c * 16u;
   }
-  // bias and mask rows: 128 keys = 16 chunks, 4 rows per wave load, two loads per wave; a
-  // chunk past lk is never fetched, and bh records which key block the chunk is in
-  uint32_t bv[2];
-  bool bh[2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int r = (wave * 2 + n) * 4 + lane / 16;
-    const int c = (lane % 16) ^ tile_xor<128>(r);
-    bv[n] = ((int64_t)kb0 * kBlock + c * 8 < p.lk) ? (uint32_t)r * (uint32_t)(p.lk * 2) + (uint32_t)c * 16u : kOutOfRange;
-    bh[n] = c >= 8;
+  // bias and mask rows: 128 keys = 16 chunks, 4 rows per wave load, one load per wave; a chunk
+  // past lk is never fetched, and bh records which key block the chunk is in
+  uint32_t bv;
+  bool bh;
+  {
+    const int r = wave * 4 + lane / 16;
+    const int c = (lane % 16) ^ bx<16>(r);
+    bv = ((int64_t)kb0 * kBlock + c * 8 < p.lk) ? (uint32_t)r * (uint32_t)(p.lk * 2) + (uint32_t)c * 16u : kOutOfRange;
+    bh = c >= 8;
   }
   const uint16_t* q_plane = p.q + (bidx * p.lq * p.hq + g * p.G) * D;     // + (i * hq + hh) * D
   const uint16_t* g_plane = p.dout + (bidx * p.lq * p.hq + g * p.G) * D;
@@ -428,37 +469,30 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     const int rows_left = min(kRows, (int)p.lq - i0);  // >= 1
     const int64_t item = ((int64_t)i0 * p.hq + hh) * D;
     const uint32_t qbytes = (uint32_t)(rows_left - 1) * qrow_bytes + (uint32_t)D * 2u;
+    if (loads_q) {
 #pragma unroll
-    for (int h2 = 0; h2 < HPI; ++h2) {
-      const u32x4 rq = rsrc_words(q_plane + item + h2 * D, qbytes), rg = rsrc_words(g_plane + item + h2 * D, qbytes);
-#pragma unroll
-      for (int n = 0; n < QL; ++n) {
-        const uint32_t dst = (uint32_t)((B * HPI + h2) * kTileBytes + (wave * QL + n) * 1024);
-        dma_x4(rq, lds_q + dst, qv[n]);
-        dma_x4(rg, lds_g + dst, qv[n]);
+      for (int h2 = 0; h2 < HPI; ++h2) {
+        const u32x4 rq = rsrc_words(q_plane + item + h2 * D, qbytes), rg = rsrc_words(g_plane + item + h2 * D, qbytes);
+        const uint32_t dst = (uint32_t)((B * HPI + h2) * kTileBytes + wave * 1024);
+        dma_x4(rq, lds_q + dst, qv);
+        dma_x4(rg, lds_g + dst, qv);
       }
     }
     if (hh == 0) {
       const uint32_t bbytes = (uint32_t)(rows_left - 1) * (uint32_t)p.lk * 2u + krange;
       if (p.bias != nullptr) {
         const u32x4 rb = rsrc_words(bias_plane + (int64_t)i0 * p.lk, bbytes);
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          dma_x4(rb, lds_b + (uint32_t)B * kBTileBytes + (uint32_t)((wave * 2 + n) * 1024),
-                 ((bh[n] ? s1 : s0) != kSkip) ? bv[n] : kOutOfRange);
+        dma_x4(rb, lds_b + (uint32_t)B * kBTileBytes + (uint32_t)(wave * 1024), ((bh ? s1 : s0) != kSkip) ? bv : kOutOfRange);
       }
       if (has_mask) {
         const u32x4 rm = rsrc_words(mask_plane + (int64_t)i0 * p.lk, bbytes);
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          dma_x4(rm, lds_m + (uint32_t)B * kBTileBytes + (uint32_t)((wave * 2 + n) * 1024),
-                 ((bh[n] ? s1 : s0) == kPartial) ? bv[n] : kOutOfRange);
+        dma_x4(rm, lds_m + (uint32_t)B * kBTileBytes + (uint32_t)(wave * 1024), ((bh ? s1 : s0) == kPartial) ? bv : kOutOfRange);
       }
       if constexpr (MK == kMaskBits) {
         // rows rh*32 .. +31 of a PARTIAL key block are 256 contiguous bytes of its bits: wave
-        // 2 + hf fetches those of block hf, one dword per lane, to bytes hf*256 .. of the tile
-        const int hf = wave - 2;
-        if (hf >= 0 && (hf ? s1 : s0) == kPartial) {
+        // 4 + hf fetches those of block hf, one dword per lane, to bytes hf*256 .. of the tile
+        const int hf = wave - 4;
+        if (hf >= 0 && hf < 2 && (hf ? s1 : s0) == kPartial) {
           const uint8_t* src =
               p.mbits + (((int64_t)plane * p.nqb + qb) * p.nkb + kb0 + hf) * kBitsPerBlock + rh * (kRows * 8);
           dma_x1(rsrc_words(src, kRows * 8), lds_m + (uint32_t)B * kBTileBytes + (uint32_t)hf * 256u,
@@ -476,46 +510,41 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     }
   };
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x4 dk[DT], dv[DT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x4{};
+    dv[dt] = f32x4{};
   }
-  f32x16 dbacc = f32x16{};
+  f32x4 dbacc[2] = {f32x4{}, f32x4{}};
 
-  // tr-read addressing: inside a 16-lane group, lane s points at row +s/4, column +4(s%4)
+  // Per-lane LDS element offsets.  S / dP A operands: row t*16 + l16, d = ks*32 + g4*8 (chunk
+  // 4 ks + g4 of the row).  dV / dK B operands: transposing reads, lane s of a 16-lane group at
+  // row 4 g4 + s/4 (+16), columns dt*16 + 4 (s%4): lane l16 receives rows 4 g4 .. +3 of column
+  // dt*16 + l16.  Raw bias / mask tiles (init values): transposing reads at row t*16 + 4 g4 +
+  // l16/4, key column wave*16 + 4 (l16%4): this lane's key, rows t*16 + 4 g4 .. +3.  dS^T tile
+  // writes: the lane's key row, query columns 4 g4 and 16 + 4 g4 (8 bytes each).
+  int aoff[2][KS], troff[DT][2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aoff[tt][ks] = bt_off<D>(tt * 16 + l16, ks * 32 + g4 * 8);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    troff[dt][0] = bt_off<D>(4 * g4 + (l16 >> 2), dt * 16 + 4 * (l16 & 3));
+    troff[dt][1] = bt_off<D>(16 + 4 * g4 + (l16 >> 2), dt * 16 + 4 * (l16 & 3));
+  }
+  int boff[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) boff[tt] = bt_off<kKeys>(tt * 16 + 4 * g4 + (l16 >> 2), wave * kWKeys + 4 * (l16 & 3));
+  const int swoff0 = st_off(key_loc, 4 * g4), swoff1 = st_off(key_loc, 16 + 4 * g4);
+  // dS export: wave w exports k-step w of the dQ kernel's B operand (keys w*16 + (l/32)*8 .. +7
+  // of query row l%32), read from the dS^T tile by two transposing reads
   const int trow = (lane & 15) >> 2;
   const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  // Per-lane LDS element offsets.  The swizzles XOR a per-row term into the 16-byte chunk
-  // index, so the offsets of the other column steps of one lane follow from the first by an
-  // XOR with a constant (bits 4 and up of the element offset), and a whole number of 16-row
-  // (Q, dO, K) or 32-row (dS^T) steps adds a constant: one base per lane, the rest in the
-  // instruction stream.  Buffer 1 of a tile sits one tile above buffer 0, beyond every bit
-  // the XORs touch.
-  const int aoff0 = tile_off<D>(l32, hi * 8);              // S/dP operands, column step s: ^ (s << 4)
-  const int goff0 = tile_off<D>(hi * 4 + trow, tcol);        // dV/dK tr reads, column step dt: ^ (dt << 5)
-  constexpr int kG1Xor = D == 128 ? 16 : 32;                 // 8 rows further down: + 8 D, then ^ this
-  const int swoff0 = swz32(l32, hi * 4) + wave * 32 * SR;    // dS^T writes, row group gi: ^ (gi << 3)
-  // the same offsets with every XOR applied, in elements of buffer 0: an item adds its buffer's
-  // base, so each read costs one add
-  int aoffs[D / 16], goffs[D / 32][2], swoffs[4];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) aoffs[s] = aoff0 ^ (s << 4);
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    goffs[dt][0] = goff0 ^ (dt << 5);
-    goffs[dt][1] = ((goff0 ^ (dt << 5)) + 8 * D) ^ kG1Xor;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) swoffs[j] = swoff0 ^ (j << 3);
-  int sq[2][2];                      // dS export, dS^T rows (ks%2)*16 + hi*8 + trow (+4), + (ks/2)*32
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    sq[par][0] = swz32(par * 16 + hi * 8 + trow, tcol);
-    sq[par][1] = swz32(par * 16 + hi * 8 + trow + 4, tcol);
-  }
-  const int boff0 = swz128(hi * 4 + trow, wave * 32 + tcol);  // raw bias and mask tiles, row group 0
+  const int hi32 = lane >> 5;
+  const int sq0 = st_off((wave & 1) * 16 + hi32 * 8 + trow, tcol) + (wave >> 1) * 32 * SR;
+  const int sq1 = st_off((wave & 1) * 16 + hi32 * 8 + trow + 4, tcol) + (wave >> 1) * 32 * SR;
 
   // Item pipeline: the loads of item n+1 go straight into the other buffer while item n
   // computes.  One barrier per item, after the dS^T tile is written: every wave has waited for
@@ -536,15 +565,61 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
   int64_t pbv = qb >= 0 ? sm.pb[qb - cache_lo] : 0;
   dma_barrier();
 
+  // ---- dS of an item to the workspace: its nonzero chunks only, in dQ-kernel order ----------
+  // 16-byte chunk c of a slot holds keys (c/64)*16 + ((c/32)%2)*8 .. +7 of query row c%32.
+  // Wave w owns the 64 chunks of k-step w (lane l: chunk w*64 + l) and packs its nonzero ones,
+  // in lane order, at the start of the slot's w-th 1 KiB; its 64-bit ballot (which lanes stored
+  // one) is the slot's mask w.  dS is zero wherever P is (masked, SKIP or non-causal keys), so
+  // with sparse masks most chunks are zero.  A chunk of zeros (either sign) is read back as +0,
+  // which leaves every dQ sum unchanged.  One buffer range per item over its heads' slots (head
+  // h2 of the item is 2 slots further: the two 32-row halves interleave).  A negative slot (no
+  // item yet) gets empty ranges, which drop every store.
+  auto export_ds = [&](int Bx, int64_t slot) {
+    const bool ok = slot >= 0;
+    const int64_t sl = ok ? slot : 0;
+    const __amdgpu_buffer_rsrc_t rds =
+        make_rsrc(p.ds + sl * (kRows * kKeys), ok ? (uint32_t)((2 * HPI - 1) * kRows * kKeys * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rmp = make_rsrc(p.dsmap + sl * 8, ok ? (uint32_t)((2 * HPI - 1) * 8 * 8) : 0u);
+#pragma unroll
+    for (int h2 = 0; h2 < HPI; ++h2) {
+      const bf16x8 ch = join_bf16x8(lds_read_tr16(&sm.s[Bx][h2][sq0]), lds_read_tr16(&sm.s[Bx][h2][sq1]));
+      const u32x4 wv = __builtin_bit_cast(u32x4, ch);
+      const bool nz = ((wv[0] | wv[1] | wv[2] | wv[3]) & 0x7FFF7FFFu) != 0u;
+      const uint64_t m0 = __ballot(nz);
+      const uint32_t r0 = __builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u));
+      // no branches: a chunk that is not stored, and the mask stores of lanes past 0, take
+      // offsets past the buffer range, which drops them
+      const uint32_t seg = (uint32_t)(h2 * 2 * kRows * kKeys * 2 + wave * (64 * 16));
+      __builtin_amdgcn_raw_buffer_store_b128(wv, rds, nz ? seg + r0 * 16u : kOutOfRange, 0, 0);
+      u32x2 mv;
+      mv[0] = (uint32_t)m0;
+      mv[1] = (uint32_t)(m0 >> 32);
+      __builtin_amdgcn_raw_buffer_store_b64(mv, rmp, lane == 0 ? (uint32_t)(h2 * 16 + wave) * 8u : kOutOfRange, 0, 0);
+    }
+  };
+  // ---- dBias of an item's rows, summed over the group (`bytes` = 0 when the item stores none) --
+  // Rows at or past the item's last row fall outside the range; a lane whose key is past lk
+  // takes an offset beyond it, so its stores are dropped as well.
+  auto store_dbias = [&](const f32x4* db, int i0x, uint32_t bytes) {
+    const uint32_t rb = (uint32_t)p.lk * 2u;
+    // integer address arithmetic: dbias may be null (then bytes is 0 and nothing is stored)
+    const uintptr_t base = (uintptr_t)p.dbias + (uintptr_t)((plane_off + (int64_t)i0x * p.lk + (int64_t)kb0 * kBlock) * 2);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(reinterpret_cast<void*>(base), bytes);
+    const uint32_t lane_off = (key_abs < p.lk) ? (uint32_t)(4 * g4) * rb + (uint32_t)key_loc * 2u : kOutOfRange;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(db[tt][e]), r, lane_off + (uint32_t)(tt * 16 + e) * rb, 0, 0);
+  };
+  // the previous item, whose stores run inside the current one
+  int64_t prev_slot = -1;
+  uint32_t prev_db_bytes = 0;
+  int prev_i0 = 0;
+  f32x4 dbprev[2] = {f32x4{}, f32x4{}};
+
   int buf = 0;
   while (qb >= 0) {
-    // The loop-carried accumulators and K/V operands sit in accumulation registers at both ends
-    // of the item: pinned at the end only, the allocator parks some of them in vector registers
-    // during the item (64 moves per item) to give the S and dP tiles their place.
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(kreg[s]), "+a"(vreg[s]));
     const int B = buf;
     const int i0 = qb * kBlock + rh * kRows;
     const int rows_left = min(kRows, (int)p.lq - i0);
@@ -567,253 +642,125 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     if (nqb >= 0) issue(B ^ 1, nqb, nrh, nhh, ns0, ns1);
 
     if (hh == 0) {
-      // S-layout initial values from the raw tiles: this lane's key (wave*32 + l32) and rows
-      // gi*8 + hi*4 .. +3 of the item.  A pair is valid when it is in range and its block is
-      // FULL, or PARTIAL with a non-zero mask (none given: every pair) in causal order.
-      // Tiles that were not loaded read as zeros, and a zero bias is no bias.
+      // S-layout initial values from the raw tiles: this lane's key and rows t*16 + 4 g4 + e of
+      // the item.  A pair is valid when it is in range and its block is FULL, or PARTIAL with a
+      // non-zero mask (none given: every pair) in causal order.  Tiles that were not loaded read
+      // as zeros, and a zero bias is no bias.
       const bool key_ok = my_st != kSkip && key_abs < p.lk;
       const bool partial = my_st == kPartial;
       // causal: row r of the item is valid for this key when r >= key - (lk - lq) - i0
       const int64_t cfirst = p.causal ? key_abs - shift - i0 : (int64_t)INT32_MIN;
       const int first_r = (int)max((int64_t)0, min(cfirst, (int64_t)kRows));
-      // rows [lo, up) are in range (and causal on a PARTIAL block) for this lane's key, as a
-      // mask shifted so that bit gi*8 + e stands for row gi*8 + hi*4 + e
+      // rows [lo, up) are in range (and causal on a PARTIAL block) for this lane's key
       const int lo = partial ? first_r : 0, up = key_ok ? rows_left : 0;
       const uint32_t below_up = up >= 32 ? 0xFFFFFFFFu : (1u << up) - 1u;
       const uint32_t below_lo = lo >= 32 ? 0xFFFFFFFFu : (1u << lo) - 1u;
-      const uint32_t rv = (below_up & ~below_lo) >> (hi * 4);
-      // bit input: row r's bits of this lane's key are bit l32 of dword r*2 + (wave & 1) of its block
-      const uint32_t* mrow = reinterpret_cast<const uint32_t*>(&sm.m[B][0]) + half * 64 + (wave & 1);
+      const uint32_t rv = below_up & ~below_lo;  // bit r: item row r
+      // bit input: row r's bits of this lane's key are bit (key % 32) of dword r*2 + key/32 of its block
+      const int kbit = (wave & 3) * kWKeys + l16;  // this lane's key inside its 64-key block
+      const uint32_t* mrow = reinterpret_cast<const uint32_t*>(&sm.m[B][0]) + half * 64 + (kbit >> 5);
       // the mask is read on PARTIAL blocks only (uniform across the wave)
       auto init = [&](auto use_mask) {
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          // 8 rows down the row term of the swizzle flips chunk bit 1 (element bit 4)
-          const int bo = (boff0 + gi * 8 * 128) ^ ((gi & 1) << 4);
-          const i16x4 xb = lds_read_tr16(&sm.b[B][bo]);
+        for (int tt = 0; tt < 2; ++tt) {
+          const i16x4 xb = lds_read_tr16(&sm.b[B][boff[tt]]);
           i16x4 xm = {0, 0, 0, 0};
-          if constexpr (decltype(use_mask)::value && MK == kMaskDense) xm = lds_read_tr16(&sm.m[B][bo]);
+          if constexpr (decltype(use_mask)::value && MK == kMaskDense) xm = lds_read_tr16(&sm.m[B][boff[tt]]);
           f32x4 iv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int idx = gi * 8 + e;
-            // all ones where the row is valid, else zero (a sign-extended one-bit field)
-            const uint32_t rm = (uint32_t)((int32_t)(rv << (31 - idx)) >> 31);
-            bool v;
-            if constexpr (!decltype(use_mask)::value) {
-              v = rm != 0u;
-            } else if constexpr (MK == kMaskDense) {
-              v = ((uint32_t)(uint16_t)xm[e] & 0x7FFFu & rm) != 0u;
-            } else if constexpr (MK == kMaskRanges) {
-              const int r = gi * 8 + hi * 4 + e;
-              v = rm != 0u && krs <= i0 + r && i0 + r < kre;
-            } else {
-              const int r = gi * 8 + hi * 4 + e;
-              v = rm != 0u && ((mrow[r * 2] >> l32) & 1u) != 0;
+            const int r = tt * 16 + 4 * g4 + e;
+            bool v = ((rv >> r) & 1u) != 0u;
+            if constexpr (decltype(use_mask)::value) {
+              if constexpr (MK == kMaskDense) {
+                v = v && ((uint32_t)(uint16_t)xm[e] & 0x7FFFu) != 0u;
+              } else if constexpr (MK == kMaskRanges) {
+                v = v && krs <= i0 + r && i0 + r < kre;
+              } else {
+                v = v && ((mrow[r * 2] >> (kbit & 31)) & 1u) != 0;
+              }
             }
             iv[e] = v ? clamp_bias(__uint_as_float((uint32_t)(uint16_t)xb[e] << 16)) * inv_scale : neg_inf_s;
           }
-          sm.beff[wave][gi][lane] = iv;
+          sm.beff[wave][tt][lane] = iv;
         }
       };
       if (partial && (MK != kMaskDense || has_mask)) init(std::true_type{});
       else init(std::false_type{});
-      dbacc = f32x16{};
+      dbacc[0] = f32x4{};
+      dbacc[1] = f32x4{};
     }
 
     // A SKIP half runs the same straight-line code: its initial S values are -inf, so P and
-    // dS are exactly zero and it adds nothing (a branch here would make the compiler shuttle
-    // the dK/dV accumulators between register files on every item).
-    // ---- S + bias/scale = Q K^T + init and dP - D = dO V^T - D: 32 queries x 32 keys -----------
+    // dS are exactly zero and it adds nothing.
 #pragma unroll
     for (int h2 = 0; h2 < HPI; ++h2) {
-      if (h2 > 0) {  // the loop-carried registers stay in the accumulation file between heads
+      // ---- S + bias/scale = Q K^T + init and dP - D = dO V^T - D: 32 queries x 16 keys -------
+      f32x4 sacc[2], pacc[2], nl[2];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(kreg[s]), "+a"(vreg[s]));
+      for (int tt = 0; tt < 2; ++tt) {
+        sacc[tt] = sm.beff[wave][tt][lane];
+        pacc[tt] = *reinterpret_cast<const f32x4*>(&sm.nd[B][h2][tt * 16 + 4 * g4]);
+        nl[tt] = *reinterpret_cast<const f32x4*>(&sm.nl2[B][h2][tt * 16 + 4 * g4]);
       }
-      f32x16 sacc, pacc;
-  #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const f32x4 iv = sm.beff[wave][gi][lane];
-        const f32x4 nd = *reinterpret_cast<const f32x4*>(&sm.nd[B][h2][gi * 8 + hi * 4]);
-  #pragma unroll
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[B][h2][aoff[tt][ks]]);
+          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[B][h2][aoff[tt][ks]]);
+          sacc[tt] = mfma16(aq, kreg[ks], sacc[tt]);
+          pacc[tt] = mfma16(ag, vreg[ks], pacc[tt]);
+        }
+      if (h2 == 0) {  // the previous item's stores, while this head's products run
+        export_ds(B ^ 1, prev_slot);
+        store_dbias(dbprev, prev_i0, prev_db_bytes);
+      }
+      // ---- P = exp2(scale2 * S' - lse log2 e), dS = P (dP - D) ---------------------------------
+      u32x4 pw, sw;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float pv[4], ds[4];
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sacc[gi * 4 + e] = iv[e];
-          pacc[gi * 4 + e] = nd[e];
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[tt][e], scale2, nl[tt][e]));
+          ds[e] = pv[e] * pacc[tt][e];
+          dbacc[tt][e] += ds[e];
         }
+        pw[2 * tt] = pack_bf16x2(pv[0], pv[1]);
+        pw[2 * tt + 1] = pack_bf16x2(pv[2], pv[3]);
+        sw[2 * tt] = pack_bf16x2(ds[0], ds[1]);
+        sw[2 * tt + 1] = pack_bf16x2(ds[2], ds[3]);
       }
-      // Every operand read is issued before the first product (a scheduling barrier keeps
-      // them there), so the products wait on LDS once instead of once per k-step.
-      bf16x8 opq[D / 16], opg[D / 16];
-  #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        opq[s] = *reinterpret_cast<const bf16x8*>(&sm.q[B][h2][aoffs[s]]);
-        opg[s] = *reinterpret_cast<const bf16x8*>(&sm.g[B][h2][aoffs[s]]);
+      const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw);
+      // ---- dV += P^T dO and dK += dS^T Q over the item's 32 rows ------------------------------
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 bg = join_bf16x8(lds_read_tr16(&sm.g[B][h2][troff[dt][0]]), lds_read_tr16(&sm.g[B][h2][troff[dt][1]]));
+        dv[dt] = mfma16(ap, bg, dv[dt]);
       }
-      f32x4 nl[4];
-  #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) nl[gi] = *reinterpret_cast<const f32x4*>(&sm.nl2[B][h2][gi * 8 + hi * 4]);
-      __builtin_amdgcn_sched_barrier(0);
-      // The wave issues in order and is the only one on its SIMD, so the vector work of the item
-      // only overlaps the matrix products if it sits between them: S first; then the dP products
-      // with P = exp2(...) of the finished S between them; the dV products (they need P only)
-      // with dS = P (dP - D); the dK products with the dS^T tile writes.  Group barriers fix
-      // that interleave (one product, then up to seven vector instructions).
-      // ---- S + bias/scale = Q K^T + init: 32 queries x 32 keys ----------------------------------
-  #pragma unroll
-      for (int s = 0; s < D / 16; ++s) sacc = mfma32(opq[s], kreg[s], sacc);
-      // the transposing reads of the dV/dK operands do not depend on P or dS: they issue between
-      // the S products (one product, then four reads), whose dependent chain leaves the wave idle
-      i16x4 trg[2][D / 32][2], trq[2][D / 32][2];
-  #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-  #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          trg[ks][dt][0] = lds_read_tr16(&sm.g[B][h2][goffs[dt][0] + ks * 16 * D]);
-          trg[ks][dt][1] = lds_read_tr16(&sm.g[B][h2][goffs[dt][1] + ks * 16 * D]);
-          trq[ks][dt][0] = lds_read_tr16(&sm.q[B][h2][goffs[dt][0] + ks * 16 * D]);
-          trq[ks][dt][1] = lds_read_tr16(&sm.q[B][h2][goffs[dt][1] + ks * 16 * D]);
-        }
-  #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 bq = join_bf16x8(lds_read_tr16(&sm.q[B][h2][troff[dt][0]]), lds_read_tr16(&sm.q[B][h2][troff[dt][1]]));
+        dk[dt] = mfma16(as, bq, dk[dt]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- dP - D = dO V^T - D, and between its products P = exp2(scale2 * S' - lse log2 e) ----
-  #pragma unroll
-      for (int s = 0; s < D / 16; ++s) pacc = mfma32(opg[s], vreg[s], pacc);
-      f32x16 pv;
-  #pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-  #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pv[gi * 4 + e] = __builtin_amdgcn_exp2f(fmaf(sacc[gi * 4 + e], scale2, nl[gi][e]));
-      bf16x8 ap[2];
-  #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 pw;
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(pv[ks * 8 + 2 * e], pv[ks * 8 + 2 * e + 1]);
-        ap[ks] = __builtin_bit_cast(bf16x8, pw);
-      }
-  #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // then seven vector instructions
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- dV += P^T dO, and between its products dS = P (dP - D) ------------------------------
-  #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-  #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          dv[dt] = mfma32(ap[ks], join_bf16x8(trg[ks][dt][0], trg[ks][dt][1]), dv[dt]);
-      u32x4 sw[2];
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float ds = pv[i] * pacc[i];
-        pacc[i] = ds;
-        dbacc[i] += ds;
-      }
-  #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) sw[ks][e] = pack_bf16x2(pacc[ks * 8 + 2 * e], pacc[ks * 8 + 2 * e + 1]);
-  #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- dK += dS^T Q, and between its products the dS^T tile writes ----------------------------
-  #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 as = __builtin_bit_cast(bf16x8, sw[ks]);
-  #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          dk[dt] = mfma32(as, join_bf16x8(trq[ks][dt][0], trq[ks][dt][1]), dk[dt]);
-        // the same bf16 pairs (rows gi*4 + 2e', + 1 of the S layout) form the dS^T rows below
-        u32x2 lo2, hi2;
-        lo2[0] = sw[ks][0];
-        lo2[1] = sw[ks][1];
-        hi2[0] = sw[ks][2];
-        hi2[1] = sw[ks][3];
-        *reinterpret_cast<u32x2*>(&sm.s[B][h2][swoffs[2 * ks]]) = lo2;
-        *reinterpret_cast<u32x2*>(&sm.s[B][h2][swoffs[2 * ks + 1]]) = hi2;
-      }
+      // the dS^T tile rows of this lane's key: query columns 4 g4 .. +3 and 16 + 4 g4 .. +3
+      u32x2 lo2, hi2;
+      lo2[0] = sw[0];
+      lo2[1] = sw[1];
+      hi2[0] = sw[2];
+      hi2[1] = sw[3];
+      *reinterpret_cast<u32x2*>(&sm.s[B][h2][swoff0]) = lo2;
+      *reinterpret_cast<u32x2*>(&sm.s[B][h2][swoff1]) = hi2;
     }
     dma_barrier();  // dS^T complete; the next item's buffers are loaded; this item's are free
 
-    // ---- dS of the item to the workspace: its nonzero chunks only, in dQ-kernel order --------
-    // 16-byte chunk c holds keys (c/64)*16 + ((c/32)%2)*8 .. +7 of query row c%32.  This lane
-    // owns chunks tid and tid + 256: transposing reads of the dS^T tile give it those 8 keys of
-    // its query (k-steps wave and wave + 4, rows hi*8 of the step).  dS is zero wherever P is
-    // (masked, SKIP or non-causal keys), so with sparse masks most chunks are zero: each wave
-    // packs its nonzero chunks (half 0 in lane order, then half 1) at the start of its own
-    // quarter of the slot, and records which lanes stored one in two 64-bit masks.  A chunk of
-    // zeros (either sign) is read back as +0, which leaves every dQ sum unchanged.
-    // One buffer range per item over its heads' slots (head h2 of the item is 2 slots further:
-    // the two 32-row halves interleave), for the chunks and for the masks; the head and the
-    // wave go into the per-lane offsets.
-    const int64_t slot_a = (((int64_t)plane * p.npairs + pbc + KB) * p.G + hh) * 2 + rh;
-    const __amdgpu_buffer_rsrc_t rds =
-        make_rsrc(p.ds + slot_a * (kRows * kKeys), (uint32_t)((2 * HPI - 1) * kRows * kKeys * 2));
-    const __amdgpu_buffer_rsrc_t rmp = make_rsrc(p.dsmap + slot_a * 8, (uint32_t)((2 * HPI - 1) * 8 * 8));
-#pragma unroll
-    for (int h2 = 0; h2 < HPI; ++h2) {
-      bf16x8 ch[2];
-      bool nz[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int ks = wave + 4 * hf;
-        const int sofs = (ks >> 1) * 32 * SR;
-        const i16x4 a0 = lds_read_tr16(&sm.s[B][h2][sq[ks & 1][0] + sofs]);
-        const i16x4 a1 = lds_read_tr16(&sm.s[B][h2][sq[ks & 1][1] + sofs]);
-        ch[hf] = join_bf16x8(a0, a1);
-        const u32x4 w = __builtin_bit_cast(u32x4, ch[hf]);
-        nz[hf] = ((w[0] | w[1] | w[2] | w[3]) & 0x7FFF7FFFu) != 0u;
-      }
-      const uint64_t m0 = __ballot(nz[0]), m1 = __ballot(nz[1]);
-      const int r0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u));
-      const int r1 = __popcll(m0) +
-                     (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u));
-      // no branches in the loop: a chunk that is not stored, and the mask stores of lanes past
-      // 1, take offsets past the buffer range, which drops them
-      const uint32_t seg = (uint32_t)(h2 * 2 * kRows * kKeys * 2 + wave * (2 * 64 * 16));
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[0]), rds, nz[0] ? seg + (uint32_t)r0 * 16u : kOutOfRange, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ch[1]), rds, nz[1] ? seg + (uint32_t)r1 * 16u : kOutOfRange, 0, 0);
-      const uint64_t mw = lane ? m1 : m0;
-      u32x2 mv;
-      mv[0] = (uint32_t)mw;
-      mv[1] = (uint32_t)(mw >> 32);
-      __builtin_amdgcn_raw_buffer_store_b64(mv, rmp, lane < 2 ? (uint32_t)(h2 * 16 + wave + 4 * lane) * 8u : kOutOfRange, 0, 0);
-    }
-
-    // ---- dBias of the item's rows, summed over the group: store after the last head -------------
-    if (hh + HPI == p.G && p.dbias != nullptr) {
-      // rows at or past rows_left fall outside the resource; a lane whose key is past lk
-      // takes an offset beyond it, so its stores are dropped as well
-      const uint32_t rbytes = (uint32_t)p.lk * 2u;
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(p.dbias + plane_off + (int64_t)i0 * p.lk + (int64_t)kb0 * kBlock, (uint32_t)rows_left * rbytes);
-      uint32_t rb = rbytes;
-      asm volatile("" : "+s"(rb));  // keep the row offsets below inside the loop (not hoisted)
-      const uint32_t lane_off = (key_abs < p.lk) ? (uint32_t)(hi * 4) * rb + (uint32_t)key_loc * 2u : kOutOfRange;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t rc = (i >> 2) * 8 + (i & 3);
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dbacc[i]), r, lane_off + rc * rb, 0, 0);
-      }
-    }
-    // the dK/dV accumulators live in the accumulation registers: no VALU ever reads them in
-    // the loop, which keeps the vector registers for the S/dP work and its operands
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(kreg[s]), "+a"(vreg[s]));
+    // the item's dS and (after the group's last head) dBias leave during the next item
+    prev_slot = (((int64_t)plane * p.npairs + pbc + KB) * p.G + hh) * 2 + rh;
+    prev_db_bytes = (hh + HPI == p.G && p.dbias != nullptr) ? (uint32_t)rows_left * ((uint32_t)p.lk * 2u) : 0u;
+    prev_i0 = i0;
+    dbprev[0] = dbacc[0];
+    dbprev[1] = dbacc[1];
     buf ^= 1;
     qb = nqb;
     rh = nrh;
@@ -822,16 +769,21 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     cs1 = ns1;
   }
 
-  // ---- dK, dV: lane holds d = dt*32 + l32 for keys (i/4)*8 + hi*4 + i%4 of this wave -------------
+  if (prev_slot >= 0) {
+    export_ds(buf ^ 1, prev_slot);
+    store_dbias(dbprev, prev_i0, prev_db_bytes);
+  }
+
+  // ---- dK, dV: lane holds d = dt*16 + l16 for keys wave*16 + 4 g4 + e ------------------------
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t key = (int64_t)kb0 * kBlock + wave * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+  for (int e = 0; e < 4; ++e) {
+    const int64_t key = (int64_t)kb0 * kBlock + wave * kWKeys + 4 * g4 + e;
     if (key < p.lk) {
-      const int64_t off = ((bidx * p.lk + key) * p.hkv + g) * D + l32;
+      const int64_t off = ((bidx * p.lk + key) * p.hkv + g) * D + l16;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        p.dk[off + dt * 32] = f32_to_bf16(dk[dt][i] * p.scale);
-        p.dv[off + dt * 32] = f32_to_bf16(dv[dt][i]);
+      for (int dt = 0; dt < DT; ++dt) {
+        p.dk[off + dt * 16] = f32_to_bf16(dk[dt][e] * p.scale);
+        p.dv[off + dt * 16] = f32_to_bf16(dv[dt][e]);
       }
     }
   }
@@ -958,9 +910,8 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const uint64_t m = mk[ks];
-      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) +
-                            (ks >= 4 ? (uint32_t)__popcll(mk[ks - 4]) : 0u);
-      const uint32_t off = ((m >> lane) & 1u) ? ((uint32_t)(ks & 3) * (2 * 64 * 8) + rank * 8u) * 2u : kOutOfRange;
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t off = ((m >> lane) & 1u) ? ((uint32_t)ks * 64u + rank) * 16u : kOutOfRange;
       dst[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
     }
   };
@@ -1106,7 +1057,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   if (parts & kBwdMain) {
   // the compute workgroups, then (with a dBias output) one zero-fill workgroup per query block
   const int64_t grid = p.total_wg + (a.dbias != nullptr ? a.b * a.hkv * (int64_t)nqb : 0);
-  auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, p); };
+  auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p); };
   // an item covers two heads when the group size is even
   auto launch_d = [&](auto dconst) {
     constexpr int D = decltype(dconst)::value;
