@@ -182,6 +182,11 @@ constexpr int kKeys = 128;  // keys per workgroup: two classification blocks
 constexpr int kRows = 32;   // query rows per item (half a classification block)
 constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LDS at a time
 
+constexpr int kLeadA = 2;  // S/dP operand steps read ahead of their products
+constexpr int kLeadB = 3;  // dV/dK operand steps read ahead of their products
+// An empty statement that LDS reads and writes cannot be moved across (MFMAs and other
+// arithmetic still can): it fixes how far operand reads run ahead of their use.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 constexpr int kWaves = 8;                 // waves of a backward workgroup: 16 keys each
 constexpr int kThreads = kWaves * 64;
 constexpr int kWKeys = kKeys / kWaves;    // keys per wave
@@ -703,15 +708,26 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
         pacc[tt] = *reinterpret_cast<const f32x4*>(&sm.nd[B][h2][tt * 16 + 4 * g4]);
         nl[tt] = *reinterpret_cast<const f32x4*>(&sm.nl2[B][h2][tt * 16 + 4 * g4]);
       }
+      // operand reads run kLeadA steps (one step: a Q and a dO read) ahead of their products;
+      // the empty asm statements pin where each read issues, so the scheduler cannot pull
+      // them back next to their use
+      {
+        constexpr int NA = 2 * KS;  // steps: (k-step, row tile)
+        bf16x8 aq[NA], ag[NA];
+        auto read_a = [&](int i) {
+          aq[i] = *reinterpret_cast<const bf16x8*>(&sm.q[B][h2][aoff[i & 1][i >> 1]]);
+          ag[i] = *reinterpret_cast<const bf16x8*>(&sm.g[B][h2][aoff[i & 1][i >> 1]]);
+        };
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+        for (int i = 0; i < kLeadA; ++i) read_a(i);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[B][h2][aoff[tt][ks]]);
-          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(&sm.g[B][h2][aoff[tt][ks]]);
-          sacc[tt] = mfma16(aq, kreg[ks], sacc[tt]);
-          pacc[tt] = mfma16(ag, vreg[ks], pacc[tt]);
+        for (int i = 0; i < NA; ++i) {
+          if (i + kLeadA < NA) read_a(i + kLeadA);
+          lds_order();
+          sacc[i & 1] = mfma16(aq[i], kreg[i >> 1], sacc[i & 1]);
+          pacc[i & 1] = mfma16(ag[i], vreg[i >> 1], pacc[i & 1]);
         }
+      }
       if (h2 == 0) {  // the previous item's stores, while this head's products run
         export_ds(B ^ 1, prev_slot);
         store_dbias(dbprev, prev_i0, prev_db_bytes);
@@ -734,15 +750,24 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
       }
       const bf16x8 ap = __builtin_bit_cast(bf16x8, pw), as = __builtin_bit_cast(bf16x8, sw);
       // ---- dV += P^T dO and dK += dS^T Q over the item's 32 rows ------------------------------
+      // steps 0 .. DT-1: dV column tiles (dO operand), DT .. 2 DT-1: dK column tiles (Q operand);
+      // the transposing reads run kLeadB steps ahead
+      {
+        bf16x8 bo[2 * DT];
+        auto read_b = [&](int j) {
+          const uint16_t* t = j < DT ? &sm.g[B][h2][0] : &sm.q[B][h2][0];
+          const int dt = j % DT;
+          bo[j] = join_bf16x8(lds_read_tr16(t + troff[dt][0]), lds_read_tr16(t + troff[dt][1]));
+        };
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 bg = join_bf16x8(lds_read_tr16(&sm.g[B][h2][troff[dt][0]]), lds_read_tr16(&sm.g[B][h2][troff[dt][1]]));
-        dv[dt] = mfma16(ap, bg, dv[dt]);
-      }
+        for (int j = 0; j < kLeadB; ++j) read_b(j);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 bq = join_bf16x8(lds_read_tr16(&sm.q[B][h2][troff[dt][0]]), lds_read_tr16(&sm.q[B][h2][troff[dt][1]]));
-        dk[dt] = mfma16(as, bq, dk[dt]);
+        for (int j = 0; j < 2 * DT; ++j) {
+          if (j + kLeadB < 2 * DT) read_b(j + kLeadB);
+          lds_order();
+          if (j < DT) dv[j] = mfma16(ap, bo[j], dv[j]);
+          else dk[j - DT] = mfma16(as, bo[j], dk[j - DT]);
+        }
       }
       // the dS^T tile rows of this lane's key: query columns 4 g4 .. +3 and 16 + 4 g4 .. +3
       u32x2 lo2, hi2;
