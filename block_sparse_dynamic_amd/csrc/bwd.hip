@@ -533,19 +533,14 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   // dt*16 + l16.  Raw bias / mask tiles (init values): transposing reads at row t*16 + 4 g4 +
   // l16/4, key column wave*16 + 4 (l16%4): this lane's key, rows t*16 + 4 g4 .. +3.  dS^T tile
   // writes: the lane's key row, query columns 4 g4 and 16 + 4 g4 (8 bytes each).
-  int aoff[2][KS], troff[DT][2];
+  // The swizzles depend on the row modulo 16, so the second 16-row tile is the first's offsets
+  // plus 16 rows: a compile-time constant that the LDS instructions take as an immediate.
+  int aoff0[KS], troff0[DT];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int ks = 0; ks < KS; ++ks) aoff0[ks] = bt_off<D>(l16, ks * 32 + g4 * 8);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) aoff[tt][ks] = bt_off<D>(tt * 16 + l16, ks * 32 + g4 * 8);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    troff[dt][0] = bt_off<D>(4 * g4 + (l16 >> 2), dt * 16 + 4 * (l16 & 3));
-    troff[dt][1] = bt_off<D>(16 + 4 * g4 + (l16 >> 2), dt * 16 + 4 * (l16 & 3));
-  }
-  int boff[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) boff[tt] = bt_off<kKeys>(tt * 16 + 4 * g4 + (l16 >> 2), wave * kWKeys + 4 * (l16 & 3));
+  for (int dt = 0; dt < DT; ++dt) troff0[dt] = bt_off<D>(4 * g4 + (l16 >> 2), dt * 16 + 4 * (l16 & 3));
+  const int boff0 = bt_off<kKeys>(4 * g4 + (l16 >> 2), wave * kWKeys + 4 * (l16 & 3));
   const int swoff0 = st_off(key_loc, 4 * g4), swoff1 = st_off(key_loc, 16 + 4 * g4);
   // dS export: wave w exports k-step w of the dQ kernel's B operand (keys w*16 + (l/32)*8 .. +7
   // of query row l%32), read from the dS^T tile by two transposing reads
@@ -650,6 +645,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
     }
     if (nqb >= 0) issue(B ^ 1, nqb, nrh, nhh, ns0, ns1);
 
+    f32x4 ivr[2];  // the item's initial S values (head 0 takes them from registers)
     if (hh == 0) {
       // S-layout initial values from the raw tiles: this lane's key and rows t*16 + 4 g4 + e of
       // the item.  A pair is valid when it is in range and its block is FULL, or PARTIAL with a
@@ -672,9 +668,9 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
       auto init = [&](auto use_mask) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const i16x4 xb = lds_read_tr16(&sm.b[B][boff[tt]]);
+          const i16x4 xb = lds_read_tr16(&sm.b[B][boff0 + tt * 16 * kKeys]);
           i16x4 xm = {0, 0, 0, 0};
-          if constexpr (decltype(use_mask)::value && MK == kMaskDense) xm = lds_read_tr16(&sm.m[B][boff[tt]]);
+          if constexpr (decltype(use_mask)::value && MK == kMaskDense) xm = lds_read_tr16(&sm.m[B][boff0 + tt * 16 * kKeys]);
           f32x4 iv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -691,13 +687,17 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
             }
             iv[e] = v ? clamp_bias(__uint_as_float((uint32_t)(uint16_t)xb[e] << 16)) * inv_scale : neg_inf_s;
           }
-          sm.beff[wave][tt][lane] = iv;
+          sm.beff[wave][tt][lane] = iv;  // for the later items of the row half
+          ivr[tt] = iv;
         }
       };
       if (partial && (MK != kMaskDense || has_mask)) init(std::true_type{});
       else init(std::false_type{});
       dbacc[0] = f32x4{};
       dbacc[1] = f32x4{};
+    } else {
+      ivr[0] = sm.beff[wave][0][lane];
+      ivr[1] = sm.beff[wave][1][lane];
     }
 
     // A SKIP half runs the same straight-line code: its initial S values are -inf, so P and
@@ -708,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
       f32x4 sacc[2], pacc[2], nl[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        sacc[tt] = sm.beff[wave][tt][lane];
+        sacc[tt] = h2 == 0 ? ivr[tt] : sm.beff[wave][tt][lane];
         pacc[tt] = *reinterpret_cast<const f32x4*>(&sm.nd[B][h2][tt * 16 + 4 * g4]);
         nl[tt] = *reinterpret_cast<const f32x4*>(&sm.nl2[B][h2][tt * 16 + 4 * g4]);
       }
@@ -719,8 +719,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
         constexpr int NA = 2 * KS;  // steps: (k-step, row tile)
         bf16x8 aq[NA], ag[NA];
         auto read_a = [&](int i) {
-          aq[i] = *reinterpret_cast<const bf16x8*>(&sm.q[B][h2][aoff[i & 1][i >> 1]]);
-          ag[i] = *reinterpret_cast<const bf16x8*>(&sm.g[B][h2][aoff[i & 1][i >> 1]]);
+          aq[i] = *reinterpret_cast<const bf16x8*>(&sm.q[B][h2][aoff0[i >> 1] + (i & 1) * 16 * D]);
+          ag[i] = *reinterpret_cast<const bf16x8*>(&sm.g[B][h2][aoff0[i >> 1] + (i & 1) * 16 * D]);
         };
 #pragma unroll
         for (int i = 0; i < kLeadA; ++i) read_a(i);
@@ -761,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
         auto read_b = [&](int j) {
           const uint16_t* t = j < DT ? &sm.g[B][h2][0] : &sm.q[B][h2][0];
           const int dt = j % DT;
-          bo[j] = join_bf16x8(lds_read_tr16(t + troff[dt][0]), lds_read_tr16(t + troff[dt][1]));
+          bo[j] = join_bf16x8(lds_read_tr16(t + troff0[dt]), lds_read_tr16(t + troff0[dt] + 16 * D));
         };
 #pragma unroll
         for (int j = 0; j < kLeadB; ++j) read_b(j);
