@@ -71,6 +71,12 @@ def parse():
                     help="turn two rocprofv3 counter passes (FETCH_SIZE and WRITE_SIZE csv files under "
                          "COUNTER_DIR, each over a run with --calibrate-copy-mib N; give the same N here) into "
                          "bytes per launch, then exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_DIR", "OUT_MD"), default=None,
+                    help="turn rocprofv3 SQ counter passes (csv files under COUNTER_DIR) into a per-kernel "
+                         "markdown summary, then exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"), default=None,
+                    help="turn a rocprofv3 --kernel-trace --stats run (kernel_stats.csv under TRACE_DIR) into "
+                         "a markdown table, then exit")
     return ap.parse_args()
 
 
@@ -389,10 +395,80 @@ def measured_copy_gbs(torch, mib=4096):
     return round(2.0 * mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)
 
 
+def summarize_counters(counter_dir: str, out_md: str):
+    """Per-kernel SQ counters (mean over dispatches, summed over the GPU) and derived ratios."""
+    import csv
+    import glob
+    import re
+    from collections import defaultdict
+
+    per = defaultdict(lambda: defaultdict(list))
+    for f in sorted(glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            per[re.sub(r"\(.*", "", r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = []
+    for k in sorted(per):
+        if not any(sub in k for sub in ("fwd_kernel", "bwd_main_kernel", "dq_kernel")):
+            continue  # the three kernels that hold the products
+        c = {n: sum(v) / len(v) for n, v in per[k].items()}
+        lines.append(f"### `{k}`\n")
+        waves = c.get("SQ_WAVES")
+        ratios = []
+        if "SQ_WAVE_CYCLES" in c:
+            for n, label in (("SQ_ACTIVE_INST_ANY", "issuing (any instruction)"),
+                             ("SQ_WAIT_INST_ANY", "ready, waiting for issue"), ("SQ_WAIT_ANY", "waiting (s_waitcnt, barrier)"),
+                             ("SQ_ACTIVE_INST_VALU", "issuing VALU / MFMA"), ("SQ_ACTIVE_INST_LDS", "issuing LDS"),
+                             ("SQ_ACTIVE_INST_SCA", "issuing scalar"), ("SQ_WAIT_INST_LDS", "waiting on LDS issue")):
+                if n in c:
+                    ratios.append((f"{label}: {n} / SQ_WAVE_CYCLES", c[n] / c["SQ_WAVE_CYCLES"]))
+        if "SQ_BUSY_CU_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            ratios.append(("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES)",
+                           c["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * c["SQ_BUSY_CU_CYCLES"])))
+        if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+            ratios.append(("LDS bank-conflict cycles / LDS active cycles", c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]))
+        if ratios:
+            lines.append("| ratio | value |\n|---|---|")
+            lines += [f"| {a} | {b:.3f} |" for a, b in ratios]
+            lines.append("")
+        lines.append("| counter | per dispatch | per wave |\n|---|---|---|")
+        for n in sorted(c):
+            pw = f"{c[n] / waves:.1f}" if waves and n.startswith("SQ_INSTS") else ""
+            lines.append(f"| {n} | {c[n]:.4g} | {pw} |")
+        lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(trace_dir: str, out_md: str):
+    """Kernel durations from a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    assert len(files) == 1, f"expected one kernel_stats.csv under {trace_dir}, found {files}"
+    rows = list(csv.DictReader(open(files[0])))
+    lines = ["| kernel | calls | total (us) | average (us) | min (us) | max (us) | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("|", "/")
+        lines.append(f"| `{name[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.calibrate_copy_mib)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (each (batch, kv head) plane "
@@ -486,12 +562,13 @@ def main():
     head_method = None
     if not args.no_workloads and args.calibrate_copy_mib == 0:
         flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-        if c.name in args.workloads.split(","):
+        # a document-mask workload is measured on its separate and range paths, not the fused one
+        if c.name in args.workloads.split(",") and c.mask != "doc":
             head_method = method_measure(st, np, torch, flush)
         st.free()
         method = {}
         for name in args.workloads.split(","):
-            if name == c.name:
+            if name == c.name and c.mask != "doc":
                 method[name] = head_method
                 continue
             wc = synth.CASES[name]
