@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
     return;
   }
   const int w = blockIdx.x;
-  const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
+  const int t = xcd_task(w, p.total_wg, p.total_wg / p.nkb2);  // units: planes
   const int plane = t / p.nkb2, KB = t % p.nkb2;  // low key blocks (most query blocks under causality) first
   const int kb0 = 2 * KB;
   const bool has_kb1 = kb0 + 1 < p.nkb;
@@ -854,7 +854,7 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   __shared__ uint8_t srow[2 * kPairChunk];  // block states of the query block's row, pairs [cache_lo, + kPairChunk)
 
   const int w = blockIdx.x;
-  const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
+  const int t = xcd_task(w, p.total_wg, p.total_wg / p.nqb);  // units: (plane, head chunk)
   const int unit = t / p.nqb;
   const int qb = p.nqb - 1 - (t % p.nqb);
   const int plane = unit / p.chunks, chunk = unit % p.chunks;

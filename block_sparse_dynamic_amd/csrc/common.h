@@ -50,6 +50,24 @@ __device__ __forceinline__ bool attends_hi(uint32_t w) { return (w & 0x7FFF0000u
 // normaliser would be left.  A clamped entry still weighs exp(-2^12) = 0 against every
 // unclamped score of its row, and equal entries stay equal, so only a row whose valid keys all
 // carry distinct biases beyond the clamp is changed (its weights no longer favour the larger).
+// Task of workgroup w of `total`, which the hardware dispatches to XCD w % 8 (the k-th of them
+// on an XCD being w / 8).  The tasks form `units` independent ranges of equal length (a (batch,
+// KV head) plane, or a plane's head chunk), each ordered longest first under causality.  With
+// the units a multiple of 8, XCD x gets the contiguous tasks of whole units: every XCD the same
+// work, and one XCD's L2 serves a unit's shared rows.  With 1, 2 or 4 units, each unit gets 8 /
+// units XCDs of its own, its range is cut into twice as many contiguous segments, and the j-th
+// of its XCDs takes segments j and (last - j), the earlier one first: under a causal mask a
+// segment of long tasks and one of short ones (equal sums for a linear decline), still
+// contiguous rows or keys of one unit for the L2.  A plain contiguous split would give one XCD
+// the longest tasks of a range and another its shortest.  Other counts keep the dispatch order.
+__device__ __forceinline__ int xcd_task(int w, int total, int units) {
+  if (total % 8 == 0 && units % 8 == 0) return (w % 8) * (total / 8) + w / 8;
+  if ((units != 1 && units != 2 && units != 4) || total % 16 != 0) return w;
+  const int per = total / units, xpu = 8 / units, nseg = 2 * xpu, seg = per / nseg;
+  const int x = w % 8, k = w / 8, unit = x / xpu, j = x % xpu;
+  return unit * per + (k < seg ? j * seg + k : (nseg - 1 - j) * seg + (k - seg));
+}
+
 constexpr float kBiasClamp = 4096.f;
 __device__ __forceinline__ float clamp_bias(float b) { return __builtin_amdgcn_fmed3f(b, -kBiasClamp, kBiasClamp); }
 

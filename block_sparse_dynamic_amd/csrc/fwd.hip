@@ -94,11 +94,10 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   constexpr int KR = FwdSmem<D>::kRow, BR = FwdSmem<D>::kBRow;
   __shared__ FwdSmem<D> sm;
 
-  // XCD-aware order: workgroup w runs on XCD w % 8; give each XCD a contiguous
-  // range of (unit, query block) so the units of one (b, g) share an L2, and run
-  // query blocks from the last (longest under causality) to the first.
+  // XCD-aware order (xcd_task): units of (plane, head chunk), query blocks from the last
+  // (longest under causality) to the first.
   const int w = blockIdx.x;
-  const int t = (p.total_wg % 8 == 0) ? (w % 8) * (p.total_wg / 8) + w / 8 : w;
+  const int t = xcd_task(w, p.total_wg, p.total_wg / p.nqb);
   const int unit = t / p.nqb;
   const int qb = p.nqb - 1 - (t % p.nqb);
   const int plane = unit / p.chunks, chunk = unit % p.chunks;

@@ -22,7 +22,6 @@ The fp64 oracle evaluated at |bias| ~ 3e38 cannot see that result: the bias abso
 q.k term of the score (fp64 spacing there is 2^75), which turns softmax(q.k) over such keys
 into uniform weights.  For those inputs the oracle is therefore evaluated on the clamped
 bias, where fp64 keeps every term.
-  dQ dK dV dB  ||x_gpu - x_ref||_2 / ||x_ref||_2 <= 2e-2
 """
 from __future__ import annotations
 
