@@ -648,16 +648,17 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
     f32x4 ivr[2];  // the item's initial S values (head 0 takes them from registers)
     if (hh == 0) {
       // S-layout initial values from the raw tiles: this lane's key and rows t*16 + 4 g4 + e of
-      // the item.  A pair is valid when it is in range and its block is FULL, or PARTIAL with a
-      // non-zero mask (none given: every pair) in causal order.  Tiles that were not loaded read
-      // as zeros, and a zero bias is no bias.
+      // the item.  A pair is valid when it is in range, in causal order, and its block is FULL, or
+      // PARTIAL with a non-zero mask (none given: every pair).  Causality is applied on FULL
+      // blocks too, as the forward does: a bitmap classified without it may mark a diagonal
+      // block FULL.  Tiles that were not loaded read as zeros, and a zero bias is no bias.
       const bool key_ok = my_st != kSkip && key_abs < p.lk;
       const bool partial = my_st == kPartial;
       // causal: row r of the item is valid for this key when r >= key - (lk - lq) - i0
       const int64_t cfirst = p.causal ? key_abs - shift - i0 : (int64_t)INT32_MIN;
       const int first_r = (int)max((int64_t)0, min(cfirst, (int64_t)kRows));
-      // rows [lo, up) are in range (and causal on a PARTIAL block) for this lane's key
-      const int lo = partial ? first_r : 0, up = key_ok ? rows_left : 0;
+      // rows [lo, up) are in range and causal for this lane's key
+      const int lo = first_r, up = key_ok ? rows_left : 0;
       const uint32_t below_up = up >= 32 ? 0xFFFFFFFFu : (1u << up) - 1u;
       const uint32_t below_lo = lo >= 32 ? 0xFFFFFFFFu : (1u << lo) - 1u;
       const uint32_t rv = below_up & ~below_lo;  // bit r: item row r

@@ -121,9 +121,12 @@ int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq,
  * finite: the kernel carries scores as q.k + bias / |scale|),
  * DMA_ERR_UNSUPPORTED (d, group, lq or lk above 2^24: 32-bit offsets inside a
  * tile row range; |scale| outside [2^-100, 2^100]).
- * The block_state must come from dma_block_classify with the same mask, sizes
- * and is_causal: a bitmap that marks blocks FULL which the call's causality
- * cuts gives wrong results (never an access outside the buffers).
+ * The block_state must come from dma_block_classify with the same mask and
+ * sizes; one classified without causality may serve a causal call (forward and
+ * backward apply causality inside every block, and the backward treats pairs
+ * that causality leaves without a valid position as SKIP: only extra work).  A
+ * bitmap of another mask gives wrong results (never an access outside the
+ * buffers).
  */
 int dma_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask, const uint16_t* bias,
                  const uint8_t* block_state, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,

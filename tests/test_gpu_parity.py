@@ -310,3 +310,31 @@ def test_backward_phases_equal_one_call():
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv", "dbias"), ref, [H.bits(t) for t in (dq, dk, dv, dbias)]):
         assert np.array_equal(a, b), f"{name} differs"
+
+
+@pytest.mark.gpu
+def test_noncausal_bitmap_serves_causal_attention():
+    """A bitmap classified without causality handed to the causal forward and backward: it marks blocks past
+    the diagonal non-SKIP and, where the mask is all ones, diagonal blocks FULL.  Both directions apply
+    causality inside every block and the backward skips the pairs that causality leaves without a valid
+    position, so every output equals the causal bitmap's bit for bit."""
+    import block_sparse_dynamic_amd as dma
+    import gpu_harness as H
+
+    for c in (Case("nc_bitmap_blocks", 41, 2, 320, 320, 8, 2, 64, True, "blocks"),
+              Case("nc_bitmap_ones", 42, 1, 256, 256, 4, 1, 128, True, "ones")):
+        ref = H.DeviceCase(c)
+        ref.classify()
+        ref.forward()
+        ref.backward()
+        alt = H.DeviceCase(c)
+        dma.dma_block_classify(alt.mask, c.b, c.hkv, c.lq, c.lk, False, alt.state)
+        torch.cuda.synchronize()
+        assert not torch.equal(alt.state, ref.state), "the non-causal bitmap should differ"
+        alt.forward()
+        alt.backward()
+        torch.cuda.synchronize()
+        for name in ("o", "lse", "dq", "dk", "dv", "dbias"):
+            a, b = getattr(ref, name), getattr(alt, name)
+            same = np.array_equal(H.bits(a), H.bits(b)) if a.dtype == torch.bfloat16 else torch.equal(a, b)
+            assert same, f"{c.name}: {name} differs with the non-causal bitmap"
