@@ -538,7 +538,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "precision": "bf16 inputs and MFMA operands (P V with P as two bf16 parts), fp32 accumulation and softmax",
+        "precision": "bf16 inputs and MFMA operands, except P V in fp16 (V scaled per 8-key group, exact for bf16 V); "
+                     "fp32 accumulation and softmax",
         "data": "synthetic (seeded; N(0,1) q/k/v/dO/bias, top-k mask from the bias)",
         "config": {"workload": describe(c), "b": c.b, "seq_len": c.lq, "hq": c.hq, "hkv": c.hkv, "d": c.d,
                    "blocks_nonskip": w["blocks_nonskip"], "blocks_partial": w["blocks_partial"],

@@ -33,13 +33,16 @@
 //      maximum (and with it the running output) moves only when a row maximum
 //      exceeds it by more than 2^8 in weight, so weights stay in [0, 256] and
 //      the rescale runs rarely (the wave skips it when no row needs it).
-//   4. O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, with V in bf16 exactly as
-//      given and the weights P split into two bf16 parts, P = P_hi + P_lo
-//      (P_hi = P truncated to bf16, P_lo = the remainder rounded to bf16): two
-//      products per k-step give P to about 16 significant bits over the whole
-//      bf16 range of V.  P^T goes from the accumulator registers straight into
-//      the B operand (the key order inside a k-step only has to agree between
-//      A and B); V^T comes out of the row-major V tile by ds_read_b64_tr_b16.
+//   4. O^T += V^T P^T on v_mfma_f32_32x32x16_f16, one product per k-step.  V
+//      is staged as fp16 scaled by a power of two per 8-key group (its largest
+//      magnitude in [2^14, 2^15), so the bf16 values are exact in fp16), and
+//      the weights as P * 2^(group exponent - e_ref) rounded to fp16 (relative
+//      2^-11), e_ref being the largest group exponent met so far: the output
+//      accumulators stay in units of 2^e_ref and are rescaled exactly when it
+//      rises; O takes the factor 2^e_ref at the end.  P^T goes from the
+//      accumulator registers straight into the B operand (the key order inside
+//      a k-step only has to agree between A and B); V^T comes out of the
+//      row-major V tile by ds_read_b64_tr_b16.
 #include <math.h>
 
 #include <type_traits>
@@ -86,6 +89,7 @@ struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay s
   int32_t rs[2][kBlock];       // column ranges of the blocks staged in alternate iterations (range input)
   int32_t re[2][kBlock];
   int32_t cls[2][2][8];        // per-wave any / all of a staged block's validity (fused classification)
+  int32_t ve[3][8];            // exponent of each 8-key group of the V buffers: V = V_tile * 2^ve
 };
 
 template <int D, int HC, int MK>
@@ -178,11 +182,17 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   // Per-thread byte offsets of the tile loads inside a block (the same for every block); the
   // block's corner and the bytes it may read go into buffer resources, whose range checks
   // return zeros for keys past lk and rows past lq.
+  // K and V: wave w loads and stages rows w*RPW .. +RPW-1 of a block (whole 8-key groups, each
+  // of which gets one V exponent), 16-byte chunk kc[n] of row kr[n].
+  constexpr int RPW = kBlock / (NT / 64);
   uint32_t kvo[KN], bo[BN];
+  int kr[KN], kc[KN];
 #pragma unroll
   for (int n = 0; n < KN; ++n) {
-    const int task = tid + n * NT;
-    kvo[n] = (uint32_t)((task / (D / 8)) * p.hkv * D + (task % (D / 8)) * 8) * 2u;
+    const int li = lane + n * 64;
+    kr[n] = wave * RPW + li / (D / 8);
+    kc[n] = li % (D / 8);
+    kvo[n] = (uint32_t)(kr[n] * p.hkv * D + kc[n] * 8) * 2u;
   }
 #pragma unroll
   for (int n = 0; n < BN; ++n) {
@@ -239,11 +249,8 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   // range input, are in sm.rs[buf]); in the classifying mode also each wave's any / all.
   auto stage_kb = [&](int buf, int kb, uint8_t st) {
 #pragma unroll
-    for (int n = 0; n < KN; ++n) {
-      const int task = tid + n * NT;
-      const int r = task / (D / 8), c = task % (D / 8);
-      *reinterpret_cast<u32x4*>(&sm.k[buf][tile_off<D>(r, c * 8)]) = pk[n];  // rows past lk are zeros
-    }
+    for (int n = 0; n < KN; ++n)
+      *reinterpret_cast<u32x4*>(&sm.k[buf][tile_off<D>(kr[n], kc[n] * 8)]) = pk[n];  // rows past lk are zeros
     const bool full = (st == kFull);
     bool any_v = false, all_v = true;  // fused classification: this thread's positions of the block
 #pragma unroll
@@ -311,13 +318,37 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       }
     }
   };
+  // V goes to LDS as fp16 scaled by a power of two per wave's rows (so per 8-key group): the
+  // largest magnitude of the rows lands in [2^14, 2^15), where every bf16 value within 2^29 of it
+  // is exact in fp16 (smaller ones move by at most 2^-39 of it).  The exponent e with
+  // V = tile * 2^e goes to sm.ve for the P V products.
   auto stage_v = [&](int buf, bool keep) {
+    uint32_t mx = 0u;  // largest |V| bits (bf16 magnitudes order as integers)
+#pragma unroll
+    for (int n = 0; n < KN; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = max(mx, max(pv[n][e] & 0x7FFFu, (pv[n][e] >> 16) & 0x7FFFu));
+    // wave maximum by DPP (no LDS round trips): prefix maxima within each row of 16 lanes, then
+    // across rows; lane 63 ends with the wave's maximum (lanes shifted in from outside a row
+    // contribute 0, the identity)
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x111, 0xf, 0xf, false));  // row_shr:1
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x112, 0xf, 0xf, false));  // row_shr:2
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x114, 0xf, 0xf, false));  // row_shr:4
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x118, 0xf, 0xf, false));  // row_shr:8
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+    const int ef = keep ? (int)(mx >> 7) : 0;  // biased exponent of the largest value (0: zero or denormal)
+    const int sh = 141 - ef;                   // the largest value times 2^sh is in [2^14, 2^15)
 #pragma unroll
     for (int n = 0; n < KN; ++n) {
-      const int task = tid + n * NT;
-      const int r = task / (D / 8), c = task % (D / 8);
-      *reinterpret_cast<u32x4*>(&sm.v[buf][tile_off<D>(r, c * 8)]) = keep ? pv[n] : u32x4{0u, 0u, 0u, 0u};
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_f16x2(__builtin_amdgcn_ldexpf(bf16_lo(pv[n][e]), sh), __builtin_amdgcn_ldexpf(bf16_hi(pv[n][e]), sh));
+      *reinterpret_cast<u32x4*>(&sm.v[buf][tile_off<D>(kr[n], kc[n] * 8)]) = keep ? w : u32x4{0u, 0u, 0u, 0u};
     }
+    if (lane < RPW / 8) sm.ve[buf][wave * (RPW / 8) + lane] = -sh;
   };
 
   // Per-lane LDS element offsets of the K operand reads and the transposing V reads; the
@@ -335,25 +366,26 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     voff1[dt] = tile_off<D>(hi * 4 + trow + 8, dt * 32 + tcol);
   }
 
-  // O^T += V^T P_hi^T + V^T P_lo^T for the block whose V sits in buffer vb.  P in [0, 256] as two
-  // bf16 parts: P_hi keeps the upper half of each fp32 weight (truncation), P_lo = P - P_hi
-  // rounded to bf16, so P_hi + P_lo is within 2^-15 of P.  A single bf16 P (relative rounding
-  // 2^-8) would move O by more than the 1e-2 the output tolerance leaves after bf16 storage.
-  u32x4 ph[2][2], pl[2][2];  // the weights P_hi, P_lo [32-key half][16-key step]
+  // O^T += V^T P^T for the block whose V sits in buffer vb, both in fp16: V scaled per 8-key
+  // group (sm.ve), and P scaled to match, P * 2^(ve - e_ref), so that the output accumulators
+  // stay in units of 2^e_ref (e_ref: the largest group exponent met so far; the accumulators are
+  // rescaled, exactly, when it rises).  P * 2^(ve - e_ref) <= P <= 256 fits fp16, whose rounding
+  // (2^-11 relative) keeps O well inside the 1e-2 its bf16 storage leaves.
+  u32x4 pf[2][2];  // the weights, fp16 [32-key half][16-key step]
+  int e_ref = -1000;
   auto pv_products = [&](int vb) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, ph[kt][hh]), bl = __builtin_bit_cast(bf16x8, pl[kt][hh]);
+        const f16x8 bp = __builtin_bit_cast(f16x8, pf[kt][hh]);
         const int rbase = (kt * 32 + hh * 16) * KR;  // rows of this k-step, a compile-time offset
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const i16x4 a0 = lds_read_tr16(&sm.v[vb][voff0[dt] + rbase]);
           const i16x4 a1 = lds_read_tr16(&sm.v[vb][voff1[dt] + rbase]);
-          const bf16x8 av = join_bf16x8(a0, a1);
-          oacc[dt] = mfma32(av, bh, oacc[dt]);
-          oacc[dt] = mfma32(av, bl, oacc[dt]);
+          const f16x8 av = __builtin_bit_cast(f16x8, join_bf16x8(a0, a1));
+          oacc[dt] = mfma32_f16(av, bp, oacc[dt]);
         }
       }
   };
@@ -374,7 +406,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) ph[kt][hh] = pl[kt][hh] = u32x4{0u, 0u, 0u, 0u};
+    for (int hh = 0; hh < 2; ++hh) pf[kt][hh] = u32x4{0u, 0u, 0u, 0u};
   // the deferring waves' first P V reads buffer 2 with zero weights: clear it
   for (int t2 = tid; t2 < kBlock * KR / 8; t2 += NT) reinterpret_cast<u32x4*>(&sm.v[2][0])[t2] = u32x4{0u, 0u, 0u, 0u};
   if (kbc < p.nkb) {
@@ -475,17 +507,37 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
           rs += pw;
         }
       l_part += rs;
+      // the block's V exponents (uniform): the reference moves up to the largest, the output
+      // accumulators follow exactly; then the weights in units of 2^e_ref.  A lane's 8 weights
+      // of k-step (kt, hh) are keys kt*32 + hh*16 + 4 hi + {0..3} (group kt*4 + hh*2) and
+      // kt*32 + hh*16 + 8 + 4 hi + {0..3} (group kt*4 + hh*2 + 1): the accumulator layout, which
+      // the transposing V reads follow.
+      int ve[8];
+#pragma unroll
+      for (int g8 = 0; g8 < 8; ++g8) ve[g8] = __builtin_amdgcn_readfirstlane(sm.ve[vcur][g8]);
+      int eb = ve[0];
+#pragma unroll
+      for (int g8 = 1; g8 < 8; ++g8) eb = max(eb, ve[g8]);
+      if (eb > e_ref) {
+        const float f = __builtin_amdgcn_ldexpf(1.f, max(e_ref - eb, -200));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= f;
+        e_ref = eb;
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh) {
+          const float sa = __builtin_amdgcn_ldexpf(1.f, max(ve[kt * 4 + hh * 2] - e_ref, -200));
+          const float sb = __builtin_amdgcn_ldexpf(1.f, max(ve[kt * 4 + hh * 2 + 1] - e_ref, -200));
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t a = __float_as_uint(sacc[kt][hh * 8 + 2 * e]), b = __float_as_uint(sacc[kt][hh * 8 + 2 * e + 1]);
-            ph[kt][hh][e] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // upper halves of a (low) and b (high)
-            pl[kt][hh][e] = pack_bf16x2(__uint_as_float(a) - __uint_as_float(a & 0xFFFF0000u),
-                                        __uint_as_float(b) - __uint_as_float(b & 0xFFFF0000u));
+            const float sc = e < 2 ? sa : sb;
+            pf[kt][hh][e] = pack_f16x2(sacc[kt][hh * 8 + 2 * e] * sc, sacc[kt][hh * 8 + 2 * e + 1] * sc);
           }
+        }
       if (!defer) pv_products(vcur);
     }
     prev_ok = compute;
@@ -533,8 +585,11 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         u32x2 w2;
-        w2[0] = pack_bf16x2(oacc[dt][gi * 4 + 0] * inv, oacc[dt][gi * 4 + 1] * inv);
-        w2[1] = pack_bf16x2(oacc[dt][gi * 4 + 2] * inv, oacc[dt][gi * 4 + 3] * inv);
+        // O = accumulator * 2^e_ref / l, the power of two applied exactly last
+        w2[0] = pack_bf16x2(__builtin_amdgcn_ldexpf(oacc[dt][gi * 4 + 0] * inv, e_ref),
+                            __builtin_amdgcn_ldexpf(oacc[dt][gi * 4 + 1] * inv, e_ref));
+        w2[1] = pack_bf16x2(__builtin_amdgcn_ldexpf(oacc[dt][gi * 4 + 2] * inv, e_ref),
+                            __builtin_amdgcn_ldexpf(oacc[dt][gi * 4 + 3] * inv, e_ref));
         *reinterpret_cast<u32x2*>(op + dt * 32 + gi * 8) = w2;
       }
     if (hi == 0) p.lse[(bidx * p.hq + head) * p.lq + row] = l_tot > 0.f ? m_ref + logf(l_tot) : INFINITY;
