@@ -184,6 +184,7 @@ constexpr int kStateChunk = 1024;  // query blocks whose states are cached in LD
 
 constexpr int kLeadA = 2;  // S/dP operand steps read ahead of their products
 constexpr int kLeadB = 3;  // dV/dK operand steps read ahead of their products
+constexpr int kLeadQ = 4;  // dQ kernel: K^T operand reads ahead of their products
 // An empty statement that LDS reads and writes cannot be moved across (MFMAs and other
 // arithmetic still can): it fixes how far operand reads run ahead of their use.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
@@ -993,14 +994,24 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
     asm volatile("" ::: "memory");  // the masks of pair n + 3 load before the chunks of pair n + 2
     load_chunks(p2.kb < npair ? p2.kb : p0.kb, M[(r + 2) % 3], B[(r + 2) % 3]);
     asm volatile("" ::: "memory");  // keep the loads here: the compiler would sink them below the products
+    // steps i = ks * (D/32) + dt; the K^T operand reads run kLeadQ steps ahead of their products
+    // (keys ks*16 + hi*8 are 16-byte chunk 2*ks + hi; swz128 XORs the chunk index, so the k-step
+    // flips bits 4..6 of the per-lane offset)
+    {
+      constexpr int NS = 8 * (D / 32);
+      bf16x8 av[NS];
+      auto read_k = [&](int i) {
+        av[i] = *reinterpret_cast<const bf16x8*>(&ktile[kbo + (aoff[i % (D / 32)] ^ ((i / (D / 32)) << 4))]);
+      };
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+      for (int i = 0; i < kLeadQ; ++i) read_k(i);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        // keys ks*16 + hi*8 are 16-byte chunk 2*ks + hi; swz128 XORs the chunk index, so the
-        // k-step flips bits 4..6 of the per-lane offset
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&ktile[kbo + (aoff[dt] ^ (ks << 4))]);
-        acc[dt] = mfma32(av, B[r][ks], acc[dt]);
+      for (int i = 0; i < NS; ++i) {
+        if (i + kLeadQ < NS) read_k(i + kLeadQ);
+        // the product's accumulator passes through the fence, so the product stays after the
+        // read just issued (otherwise the scheduler moves it up next to its own read)
+        asm volatile("" : "+v"(acc[i % (D / 32)])::"memory");
+        acc[i % (D / 32)] = mfma32(av[i], B[r][i / (D / 32)], acc[i % (D / 32)]);
       }
     }
     p0 = p1;
