@@ -92,6 +92,12 @@ struct alignas(16) FwdSmem {  // 16-byte aligned so tile reads and writes stay s
   int32_t ve[3][8];            // exponent of each 8-key group of the V buffers: V = V_tile * 2^ve
 };
 
+// Operand reads issued this many products ahead (K for S, two V reads per step for P V).  Each
+// product's accumulator passes through an empty asm statement after the read issued for a later
+// product, which keeps the product behind that read: the scheduler would otherwise place every
+// product right after its own read and wait out the LDS round trip.
+constexpr int kLeadQK = 2, kLeadPV = 2;
+
 template <int D, int HC, int MK>
 __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   constexpr int NT = HC * 128;
@@ -374,20 +380,23 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   u32x4 pf[2][2];  // the weights, fp16 [32-key half][16-key step]
   int e_ref = -1000;
   auto pv_products = [&](int vb) {
+    constexpr int NJ = 4 * (D / 32);  // steps: (16-key step, d tile)
+    f16x8 av[NJ];
+    auto read_v = [&](int j) {
+      const int ks = j / (D / 32), dt = j % (D / 32);
+      const int rbase = ks * 16 * KR;
+      av[j] = __builtin_bit_cast(f16x8, join_bf16x8(lds_read_tr16(&sm.v[vb][voff0[dt] + rbase]),
+                                                     lds_read_tr16(&sm.v[vb][voff1[dt] + rbase])));
+    };
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int j = 0; j < kLeadPV; ++j) read_v(j);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const f16x8 bp = __builtin_bit_cast(f16x8, pf[kt][hh]);
-        const int rbase = (kt * 32 + hh * 16) * KR;  // rows of this k-step, a compile-time offset
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const i16x4 a0 = lds_read_tr16(&sm.v[vb][voff0[dt] + rbase]);
-          const i16x4 a1 = lds_read_tr16(&sm.v[vb][voff1[dt] + rbase]);
-          const f16x8 av = __builtin_bit_cast(f16x8, join_bf16x8(a0, a1));
-          oacc[dt] = mfma32_f16(av, bp, oacc[dt]);
-        }
-      }
+    for (int j = 0; j < NJ; ++j) {
+      if (j + kLeadPV < NJ) read_v(j + kLeadPV);
+      const int ks = j / (D / 32), dt = j % (D / 32);
+      asm volatile("" : "+v"(oacc[dt])::"memory");
+      oacc[dt] = mfma32_f16(av[j], __builtin_bit_cast(f16x8, pf[ks >> 1][ks & 1]), oacc[dt]);
+    }
   };
 
   // ---- the key-block loop, with the two waves of each SIMD in opposite phases ----------------
@@ -466,12 +475,17 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) sacc[kt][gi * 4 + e] = y[e];
         }
+      {  // steps i = k-step * 2 + key half; the K reads run kLeadQK steps ahead
+        constexpr int NI = 2 * (D / 16);
+        bf16x8 ak[NI];
+        auto read_k = [&](int i) { ak[i] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][koff[i >> 1] + (i & 1) * 32 * KR]); };
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
+        for (int i = 0; i < kLeadQK; ++i) read_k(i);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][koff[s] + kt * 32 * KR]);
-          sacc[kt] = mfma32(a, qreg[s], sacc[kt]);
+        for (int i = 0; i < NI; ++i) {
+          if (i + kLeadQK < NI) read_k(i + kLeadQK);
+          asm volatile("" : "+v"(sacc[i & 1])::"memory");
+          sacc[i & 1] = mfma32(ak[i], qreg[i >> 1], sacc[i & 1]);
         }
       }
       // ---- online softmax ----------------------------------------------------------------------
