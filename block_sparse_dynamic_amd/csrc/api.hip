@@ -202,8 +202,10 @@ namespace {
 //   kt         bf16 [b, hkv, d, nkb2 * 128]        K transposed
 //   ds         bf16 [b, hkv, npairs, G, 2, 32*128] dS tile slots of every live (query block, key pair)
 //   dsmap      u64  [b, hkv, npairs, G, 2, 8]      which 16-byte chunks of each slot are stored
+//   dkv        fp32 2 x [b, lk, hkv, d]            dK, dV sums of the split key pairs (only when
+//                                                  the backward splits them, see bwd_splits)
 struct WsLayout {
-  size_t rows, pair_base, kt, ds, dsmap, total;
+  size_t rows, pair_base, kt, ds, dsmap, dkv, total;
   int64_t npairs;
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -218,7 +220,9 @@ WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, i
   w.kt = w.pair_base + up256((size_t)(nqb + 1) * sizeof(int64_t));
   w.ds = w.kt + up256((size_t)b * hkv * d * nkb2 * 128 * sizeof(uint16_t));
   w.dsmap = w.ds + up256((size_t)b * hq * np * 2 * 32 * 128 * sizeof(uint16_t));
-  w.total = w.dsmap + up256((size_t)b * hq * np * 2 * 8 * sizeof(uint64_t));
+  w.dkv = w.dsmap + up256((size_t)b * hq * np * 2 * 8 * sizeof(uint64_t));
+  const size_t dkv_bytes = dma::bwd_splits(b, hkv, lq, lk, causal) > 1 ? (size_t)2 * b * lk * hkv * d * sizeof(float) : 0;
+  w.total = w.dkv + up256(dkv_bytes);
   return w;
 }
 }  // namespace
@@ -280,6 +284,7 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.ds = reinterpret_cast<uint16_t*>(ws + wl.ds);
   a.dsmap = reinterpret_cast<uint64_t*>(ws + wl.dsmap);
   a.npairs = wl.npairs;
+  a.dkv_acc = dma::bwd_splits(b, hkv, lq, lk, is_causal) > 1 ? reinterpret_cast<float*>(ws + wl.dkv) : nullptr;
   a.b = b;
   a.lq = lq;
   a.lk = lk;

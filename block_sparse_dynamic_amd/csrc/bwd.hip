@@ -172,8 +172,9 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   uint16_t* dbias;
+  float* dkv_acc;  // fp32 dK, dV sums when the pairs are split (splits > 1)
   int64_t lq, lk, hq, hkv;
-  int G, nqb, nkb, nkb2, total_wg;
+  int G, nqb, nkb, nkb2, splits, total_wg;
   float scale;
   int causal;
 };
@@ -334,11 +335,27 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
     return;
   }
   const int w = blockIdx.x;
-  const int t = xcd_task(w, p.total_wg, p.total_wg / p.nkb2);  // units: planes
-  const int plane = t / p.nkb2, KB = t % p.nkb2;  // low key blocks (most query blocks under causality) first
+  const int per_plane = p.nkb2 * p.splits;
+  const int t = xcd_task(w, p.total_wg, p.total_wg / per_plane);  // units: planes
+  // low key blocks (most query blocks under causality) first; a split pair's halves next to each other
+  const int plane = t / per_plane, KB = (t % per_plane) / p.splits, seg = (t % per_plane) % p.splits;
   const int kb0 = 2 * KB;
   const bool has_kb1 = kb0 + 1 < p.nkb;
   const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
+  // Query blocks this workgroup walks, [q_lo, q_hi]: all of them, or one half of the pair's live
+  // blocks (the first live one is the smallest qb with KB < live_pairs(qb), which only grows with qb)
+  int q_lo = 0, q_hi = p.nqb - 1;
+  if (p.splits > 1) {
+    int lo = 0, hi = p.nqb;  // first live query block, found by bisection
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (KB < live_pairs(mid, p.lq, p.lk, p.causal)) hi = mid;
+      else lo = mid + 1;
+    }
+    const int upper = lo + (p.nqb - lo) / 2;  // segment 0: [upper, nqb), segment 1: [lo, upper)
+    q_lo = seg == 0 ? upper : lo;
+    q_hi = seg == 0 ? p.nqb - 1 : upper - 1;
+  }
   // wave and the block states below are uniform across a wave; readfirstlane tells the compiler
   // so, which keeps the loop control and the buffer resources in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -427,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   // next query block with a non-SKIP half at or before `from` (the dBias zeros of the blocks
   // it passes over are written by the zero-fill workgroups)
   auto next_qb = [&](int from, uint8_t& s0, uint8_t& s1) -> int {
-    for (int qb = from; qb >= 0; --qb) {
+    for (int qb = from; qb >= q_lo; --qb) {
       if (qb < cache_lo) fill_cache(qb);
       s0 = (uint8_t)__builtin_amdgcn_readfirstlane(sm.st[0][qb - cache_lo]);
       s1 = (uint8_t)__builtin_amdgcn_readfirstlane(sm.st[1][qb - cache_lo]);
@@ -562,7 +579,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   // which would also wait for the item loads issued there.
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();     // buffers zeroed
-  int qb = next_qb(p.nqb - 1, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
+  int qb = next_qb(q_hi, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
   int rh = 0, hh = 0;
   if (qb >= 0) issue(0, qb, 0, 0, cs0, cs1);
   // first dS tile pair of the current query block, kept as read from LDS (uniform): the next
@@ -806,18 +823,47 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   }
 
   // ---- dK, dV: lane holds d = dt*16 + l16 for keys wave*16 + 4 g4 + e ------------------------
+  // (a split pair's halves add into the fp32 sums, which bwd_finalize_kernel converts)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t key = (int64_t)kb0 * kBlock + wave * kWKeys + 4 * g4 + e;
     if (key < p.lk) {
       const int64_t off = ((bidx * p.lk + key) * p.hkv + g) * D + l16;
+      if (p.splits > 1) {
+        float* acc_k = p.dkv_acc;
+        float* acc_v = p.dkv_acc + (p.total_wg / per_plane) / p.hkv * p.lk * p.hkv * D;  // + b lk hkv d
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        p.dk[off + dt * 16] = f32_to_bf16(dk[dt][e] * p.scale);
-        p.dv[off + dt * 16] = f32_to_bf16(dv[dt][e]);
+        for (int dt = 0; dt < DT; ++dt) {
+          atomicAdd(acc_k + off + dt * 16, dk[dt][e] * p.scale);
+          atomicAdd(acc_v + off + dt * 16, dv[dt][e]);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          p.dk[off + dt * 16] = f32_to_bf16(dk[dt][e] * p.scale);
+          p.dv[off + dt * 16] = f32_to_bf16(dv[dt][e]);
+        }
       }
     }
   }
+}
+
+// The dK and dV of split key pairs: zero the fp32 sums before the main kernel, convert them to
+// bf16 after it (n = b lk hkv d values each; 4 per thread).
+__global__ __launch_bounds__(256) void dkv_zero_kernel(float* __restrict__ acc, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) reinterpret_cast<f32x4*>(acc)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+__global__ __launch_bounds__(256) void dkv_finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dk,
+                                                           uint16_t* __restrict__ dv, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const f32x4 x = reinterpret_cast<const f32x4*>(acc)[i];
+  uint16_t* out = i < n4 ? dk + 4 * i : dv + 4 * (i - n4);
+  u32x2 w;
+  w[0] = pack_bf16x2(x[0], x[1]);
+  w[1] = pack_bf16x2(x[2], x[3]);
+  *reinterpret_cast<u32x2*>(out) = w;
 }
 
 // ---------------------------------------------------------------------------
@@ -1060,6 +1106,10 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
                        a.hkv, ktrow, nkb2 * 2, (int)a.d);
     hipLaunchKernelGGL(pair_base_kernel, dim3(1), dim3(1024), 0, stream, a.pair_base, (int64_t)nqb, a.lq, a.lk,
                        a.causal);
+    if (a.dkv_acc != nullptr) {
+      const int64_t n4 = 2 * a.b * a.lk * a.hkv * a.d / 4;
+      hipLaunchKernelGGL(dkv_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a.dkv_acc, n4);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1083,6 +1133,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   p.dk = a.dk;
   p.dv = a.dv;
   p.dbias = a.dbias;
+  p.dkv_acc = a.dkv_acc;
   p.lq = a.lq;
   p.lk = a.lk;
   p.hq = a.hq;
@@ -1091,7 +1142,8 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   p.nqb = nqb;
   p.nkb = nkb;
   p.nkb2 = nkb2;
-  p.total_wg = (int)(a.b * a.hkv * p.nkb2);
+  p.splits = a.dkv_acc != nullptr ? bwd_splits(a.b, a.hkv, a.lq, a.lk, a.causal) : 1;
+  p.total_wg = (int)(a.b * a.hkv * p.nkb2 * p.splits);
   p.scale = a.scale;
   p.causal = a.causal;
   const int MK = a.rstart != nullptr ? kMaskRanges : a.mbits != nullptr ? kMaskBits : kMaskDense;
@@ -1114,6 +1166,11 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   };
   if (a.d == 64) launch_d(std::integral_constant<int, 64>{});
   else launch_d(std::integral_constant<int, 128>{});
+  if (a.dkv_acc != nullptr) {
+    const int64_t n4 = a.b * a.lk * a.hkv * a.d / 4;
+    hipLaunchKernelGGL(dkv_finalize_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, stream,
+                       a.dkv_acc, a.dk, a.dv, n4);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   }

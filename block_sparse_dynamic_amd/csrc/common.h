@@ -208,10 +208,21 @@ struct AttnArgs {
                       // holding only the tile's nonzero 16-byte chunks, packed per writing wave
   uint64_t* dsmap;    // per slot 8 masks: which chunks of each (wave, half) of the writer are stored
   int64_t npairs;     // live key-block pairs of one plane (pair_base[nqb])
+  float* dkv_acc;     // fp32 [2][b, lk, hkv, d]: dK, dV sums of split pairs (bwd_splits > 1), else null
   int64_t b, lq, lk, hq, hkv, d;
   float scale;
   int causal;
 };
+
+// Workgroups per 128-key pair in the backward.  Under causality a pair's walk over query blocks
+// runs from all of them (the first pair) down to one or two (the last), and one workgroup per
+// pair leaves the longest walk setting the kernel's time when the pairs are few (up to 256,
+// about one per CU): there each pair's walk is cut in two halves run by two workgroups, which
+// add their dK and dV into an fp32 accumulator.  Shared by the workspace sizing and the launch.
+__host__ __device__ inline int bwd_splits(int64_t b, int64_t hkv, int64_t lq, int64_t lk, int causal) {
+  const int64_t nqb = (lq + 63) / 64, nkb2 = ((lk + 63) / 64 + 1) / 2;
+  return (causal && b * hkv * nkb2 <= 256 && nqb >= 8) ? 2 : 1;
+}
 
 // Key-block pairs (128 keys) that can hold a valid position for query block qb: all of them
 // without causality, else those whose first key is at most the block's last row + lk - lq.

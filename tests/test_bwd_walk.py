@@ -6,7 +6,9 @@ blocks are not both SKIP; every visit stores the item's dS chunks into the slot
 ((plane * npairs + pair_base[qb] + KB) * G + head) * 2 + half of the workspace.  The dQ kernel
 reads, for each query block, the slots of its live pairs that are not SKIP in both halves.
 
-This emulation follows the kernel's control: query blocks from nqb - 1 down to 0, the block
+This emulation follows the kernel's control: query blocks from nqb - 1 down to 0 (or, where the
+backward splits each key pair over two workgroups, the two halves of the pair's live query
+blocks, each walked downwards by its own workgroup with its own cache), the block
 states cached a chunk of 1024 query blocks at a time, a pair that causality leaves no valid
 position for the query block (KB >= live_pairs(qb)) taken as SKIP whatever the bitmap says,
 heads in steps of two (one when the group size is odd), rows in two 32-row halves (one past
@@ -35,12 +37,29 @@ def live_pairs(qb, lq, lk, causal):
     return 0 if last < 0 else min(nkb2, last // 128 + 1)
 
 
+def bwd_splits(b, hkv, lq, lk, causal):
+    """Workgroups per 128-key pair: two (each walking half of the pair's live query blocks) when the
+    backward is causal, the pairs over all planes are at most 256 and there are at least 8 query blocks."""
+    nqb, nkb2 = (lq + 63) // 64, ((lk + 63) // 64 + 1) // 2
+    return 2 if causal and b * hkv * nkb2 <= 256 and nqb >= 8 else 1
+
+
 def ws_size(b, lq, lk, hq, hkv, d, causal):
     up = lambda x: (x + 255) // 256 * 256
     nqb, nkb2 = (lq + 63) // 64, ((lk + 63) // 64 + 1) // 2
     npairs = sum(live_pairs(qb, lq, lk, causal) for qb in range(nqb))
+    dkv = up(2 * b * lk * hkv * d * 4) if bwd_splits(b, hkv, lq, lk, causal) > 1 else 0
     return up(2 * b * hq * lq * 4) + up((nqb + 1) * 8) + up(b * hkv * d * nkb2 * 128 * 2) + \
-        up(b * hq * npairs * 64 * 128 * 2) + up(b * hq * npairs * 2 * 8 * 8)
+        up(b * hq * npairs * 64 * 128 * 2) + up(b * hq * npairs * 2 * 8 * 8) + dkv
+
+
+def segments(KB, nqb, lq, lk, causal, splits):
+    """Query-block ranges [lo, hi] of the workgroups of key pair KB."""
+    if splits == 1:
+        return [(0, nqb - 1)]
+    lo = next(qb for qb in range(nqb + 1) if qb == nqb or KB < live_pairs(qb, lq, lk, causal))
+    upper = lo + (nqb - lo) // 2
+    return [(upper, nqb - 1), (lo, upper - 1)]
 
 
 def main_kernel_slots(state, b, hkv, G, lq, lk, causal):
@@ -69,19 +88,21 @@ def main_kernel_slots(state, b, hkv, G, lq, lk, causal):
                             st[hf, j] = state[bb, g, qb, kb0 + hf]
                 return lo, st
 
-            qb = nqb - 1
-            while qb >= 0:
-                if qb < cache_lo:
-                    cache_lo, cache = fill(qb)
-                s0, s1 = cache[0, qb - cache_lo], cache[1, qb - cache_lo]
-                if s0 != SKIP or s1 != SKIP:
-                    halves = 1 if qb * 64 + 32 >= lq else 2
-                    for rh in range(halves):
-                        for hh in range(0, G, hpi):
-                            slot_a = ((plane * npairs + int(pair_base[qb]) + KB) * G + hh) * 2 + rh
-                            for h2 in range(hpi):
-                                slots.append((plane, slot_a + 2 * h2))
-                qb -= 1
+            for q_lo, q_hi in segments(KB, nqb, lq, lk, causal, bwd_splits(b, hkv, lq, lk, causal)):
+                cache_lo = nqb  # each workgroup starts with an empty cache
+                qb = q_hi
+                while qb >= q_lo:
+                    if qb < cache_lo:
+                        cache_lo, cache = fill(qb)
+                    s0, s1 = cache[0, qb - cache_lo], cache[1, qb - cache_lo]
+                    if s0 != SKIP or s1 != SKIP:
+                        halves = 1 if qb * 64 + 32 >= lq else 2
+                        for rh in range(halves):
+                            for hh in range(0, G, hpi):
+                                slot_a = ((plane * npairs + int(pair_base[qb]) + KB) * G + hh) * 2 + rh
+                                for h2 in range(hpi):
+                                    slots.append((plane, slot_a + 2 * h2))
+                    qb -= 1
     return slots, npairs
 
 
@@ -105,8 +126,9 @@ def dq_kernel_slots(state, b, hkv, G, lq, lk, causal, npairs):
     return reads
 
 
-CASES = [(1, 200, 200, 4, 2, 1), (2, 1000, 1000, 4, 1, 1), (1, 130, 264, 8, 2, 1), (1, 200, 136, 2, 1, 1),
-         (1, 264, 264, 16, 4, 0), (1, 300, 300, 3, 1, 1), (1, 70000, 70000, 1, 1, 1)]
+CASES = [(1, 200, 200, 4, 2, 1), (2, 1000, 1000, 4, 1, 1), (1, 600, 600, 4, 2, 1), (2, 520, 540, 1, 2, 1),
+         (1, 130, 264, 8, 2, 1), (1, 200, 136, 2, 1, 1), (1, 264, 264, 16, 4, 0), (1, 300, 300, 3, 1, 1),
+         (1, 70000, 70000, 1, 1, 1)]
 
 
 @pytest.mark.parametrize("b,lq,lk,G,hkv,causal", CASES)

@@ -38,6 +38,10 @@ SMALL = [
     # the forward carries scores as q.k + bias/|scale| and negates Q for a negative scale
     Case("negative_scale", 23, 1, 200, 200, 4, 2, 128, True, "blocks", scale=-0.09),
     Case("large_scale_d64", 24, 1, 192, 192, 4, 2, 64, True, "topk", 64, scale=0.5),
+    # causal with few key pairs and at least 8 query blocks: the backward splits every pair's walk
+    # over two workgroups that add their dK, dV in fp32 (ragged rows and keys)
+    Case("split_pairs", 25, 1, 600, 600, 8, 2, 128, True, "blocks"),
+    Case("split_pairs_d64_g1", 26, 2, 520, 544, 2, 2, 64, True, "topk", 96),
 ]
 
 
