@@ -165,7 +165,12 @@ int dma_attn_fwd_classify(const uint16_t* q, const uint16_t* k, const uint16_t* 
  * which dQ is formed without atomics (FlashMask README: deterministic backward),
  * with 128 bytes per slot that record which of its 16-byte chunks are nonzero
  * (only those are written and read back).  With is_causal the count of live
- * pairs is about half of all pairs. */
+ * pairs is about half of all pairs.  When the backward is causal with at most
+ * 256 key pairs over all (batch, kv head) planes and at least 8 query blocks,
+ * each pair's walk is split over two workgroups and the workspace also holds
+ * fp32 dK and dV sums (2 x b x lk x hkv x d floats); two partial sums added
+ * onto zero in either order give the same bits, so the results stay
+ * deterministic. */
 size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
                                    int is_causal);
 
