@@ -34,10 +34,13 @@
 //      exceeds it by more than 2^8 in weight, so weights stay in [0, 256] and
 //      the rescale runs rarely (the wave skips it when no row needs it).
 //   4. O^T += V^T P^T on v_mfma_f32_32x32x16_f16, one product per k-step.  V
-//      is staged as fp16 scaled by a power of two per 8-key group (its largest
-//      magnitude in [2^14, 2^15), so the bf16 values are exact in fp16), and
-//      the weights as P * 2^(group exponent - e_ref) rounded to fp16 (relative
-//      2^-11), e_ref being the largest group exponent met so far: the output
+//      is staged as fp16 scaled by a power of two per 8-key group (a multiple
+//      of 8 that puts its largest magnitude in [2^7, 2^15), so the bf16 values
+//      are exact in fp16), and the weights as P * 2^(group exponent - e_ref)
+//      rounded to fp16 (relative 2^-11; no scaling when the groups share
+//      e_ref; P carries a constant 2^7 that cancels in O and keeps weights
+//      scaled down for small groups out of fp16's subnormals), e_ref being
+//      the largest group exponent met so far: the output
 //      accumulators stay in units of 2^e_ref and are rescaled exactly when it
 //      rises; O takes the factor 2^e_ref at the end.  P^T goes from the
 //      accumulator registers straight into the B operand (the key order inside
@@ -73,6 +76,11 @@ struct FwdParams {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kStateChunkF = 1024;                    // key blocks whose states are cached in LDS at a time
 constexpr float kRescaleMargin = 8.f * 0.69314718f;  // natural-log units
+// The weights are computed as exp(x - m_ref) * 2^kPShift: under the rescale margin they stay below
+// 2^15, inside fp16, and weights scaled down to a smaller V group's units keep 7 more bits before
+// they reach fp16's subnormals.  The factor cancels in O = sum(P V) / sum(P); the log-sum-exp
+// takes it out.
+constexpr float kPShift = 7.f;
 constexpr uint16_t kBf16NegInf = 0xFF80u;
 
 template <int D>
@@ -324,10 +332,12 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       }
     }
   };
-  // V goes to LDS as fp16 scaled by a power of two per wave's rows (so per 8-key group): the
-  // largest magnitude of the rows lands in [2^14, 2^15), where every bf16 value within 2^29 of it
-  // is exact in fp16 (smaller ones move by at most 2^-39 of it).  The exponent e with
-  // V = tile * 2^e goes to sm.ve for the P V products.
+  // V goes to LDS as fp16 scaled by a power of two per wave's rows (so per 8-key group).  The
+  // exponent e with V = tile * 2^e is the smallest multiple of 8 that puts the rows' largest
+  // magnitude below 2^15: it lands in [2^7, 2^15), where every bf16 value within 2^22 of it is
+  // exact in fp16 (smaller ones move by at most 2^-32 of it).  Groups whose largest magnitudes
+  // lie within the same factor-256 band share e, so the weights of a block usually need no
+  // scaling.  e goes to sm.ve for the P V products.
   auto stage_v = [&](int buf, bool keep) {
     uint32_t mx = 0u;  // largest |V| bits (bf16 magnitudes order as integers)
 #pragma unroll
@@ -345,7 +355,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x143, 0xc, 0xf, false));  // row_bcast:31
     mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
     const int ef = keep ? (int)(mx >> 7) : 0;  // biased exponent of the largest value (0: zero or denormal)
-    const int sh = 141 - ef;                   // the largest value times 2^sh is in [2^14, 2^15)
+    const int sh = -((ef - 134) & ~7);         // -e: ef - 141 (largest value in [2^14, 2^15)) rounded up to a multiple of 8
 #pragma unroll
     for (int n = 0; n < KN; ++n) {
       u32x4 w;
@@ -375,8 +385,9 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
   // O^T += V^T P^T for the block whose V sits in buffer vb, both in fp16: V scaled per 8-key
   // group (sm.ve), and P scaled to match, P * 2^(ve - e_ref), so that the output accumulators
   // stay in units of 2^e_ref (e_ref: the largest group exponent met so far; the accumulators are
-  // rescaled, exactly, when it rises).  P * 2^(ve - e_ref) <= P <= 256 fits fp16, whose rounding
-  // (2^-11 relative) keeps O well inside the 1e-2 its bf16 storage leaves.
+  // rescaled, exactly, when it rises).  P * 2^(ve - e_ref) <= P < 2^15 (P carries 2^kPShift)
+  // fits fp16, whose rounding (2^-11 relative) keeps O well inside the 1e-2 its bf16 storage
+  // leaves.
   u32x4 pf[2][2];  // the weights, fp16 [32-key half][16-key step]
   int e_ref = -1000;
   auto pv_products = [&](int vb) {
@@ -496,8 +507,8 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
       mx = max_with_half_swap(mx) * as;
       // The reference maximum moves only when a row's maximum exceeds it by more than
-      // kRescaleMargin (8 in log2 units): below that the weights exp(x - m_ref) stay under 256,
-      // which fp32 sums and the two-part bf16 P hold without loss, and the rescale of the
+      // kRescaleMargin (8 in log2 units): below that the weights exp(x - m_ref) stay under 256
+      // (2^15 with the 2^kPShift factor), which fp32 sums and fp16 weights hold, and the rescale of the
       // output accumulators (64 multiplies per lane) runs a few times per row instead of on most
       // key blocks.  It follows every P V of the old reference, whichever order the wave runs.
       if (__any(mx > m_ref + kRescaleMargin)) {
@@ -510,7 +521,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       }
-      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref * kLog2e;
+      const float mb = ((m_ref == -INFINITY) ? 0.f : m_ref * kLog2e) - kPShift;
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -540,6 +551,18 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
           for (int i = 0; i < 16; ++i) oacc[dt][i] *= f;
         e_ref = eb;
       }
+      bool uniform = true;  // every group at e_ref: the weights go to fp16 unscaled
+#pragma unroll
+      for (int g8 = 0; g8 < 8; ++g8) uniform = uniform && ve[g8] == e_ref;
+      if (uniform) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              pf[kt][hh][e] = pack_f16x2(sacc[kt][hh * 8 + 2 * e], sacc[kt][hh * 8 + 2 * e + 1]);
+      } else {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -552,6 +575,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
             pf[kt][hh][e] = pack_f16x2(sacc[kt][hh * 8 + 2 * e] * sc, sacc[kt][hh * 8 + 2 * e + 1] * sc);
           }
         }
+      }
       if (!defer) pv_products(vcur);
     }
     prev_ok = compute;
@@ -606,7 +630,8 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
                             __builtin_amdgcn_ldexpf(oacc[dt][gi * 4 + 3] * inv, e_ref));
         *reinterpret_cast<u32x2*>(op + dt * 32 + gi * 8) = w2;
       }
-    if (hi == 0) p.lse[(bidx * p.hq + head) * p.lq + row] = l_tot > 0.f ? m_ref + logf(l_tot) : INFINITY;
+    // l_tot carries the weights' 2^kPShift
+    if (hi == 0) p.lse[(bidx * p.hq + head) * p.lq + row] = l_tot > 0.f ? m_ref + logf(l_tot) - kPShift * 0.69314718f : INFINITY;
   }
 }
 
