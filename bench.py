@@ -276,6 +276,65 @@ def method_measure(st, np, torch, flush, n_warm=2, n_iter=10, bound="mfma"):
     return out
 
 
+def band_count(c, ws_bytes: int) -> int:
+    """Bands of query blocks dma_attn_bwd runs in for this workspace (1: the one pass): the most
+    slot pairs per plane that fit beside the fixed regions, then consecutive blocks while their
+    live pairs fit."""
+    up = lambda x: (x + 255) // 256 * 256
+    nqb, nkb2 = (c.lq + 63) // 64, ((c.lk + 63) // 64 + 1) // 2
+
+    def live(qb):
+        if not c.causal:
+            return nkb2
+        last = qb * 64 + 63 + c.lk - c.lq
+        return 0 if last < 0 else min(nkb2, last // 128 + 1)
+
+    fixed = up(2 * c.b * c.hq * c.lq * 4) + up((nqb + 1) * 8) + up(c.b * c.hkv * c.d * nkb2 * 128 * 2)
+    total = sum(live(qb) for qb in range(nqb))
+    if ws_bytes >= fixed + up(c.b * c.hq * total * 16384) + up(c.b * c.hq * total * 128) + \
+            (up(2 * c.b * c.lk * c.hkv * c.d * 4) if c.causal and c.b * c.hkv * nkb2 <= 256 and nqb >= 8 else 0):
+        return 1
+    fixed += up(2 * c.b * c.lk * c.hkv * c.d * 4)
+    np_ = min(total, (ws_bytes - fixed) // (c.b * c.hq * 16512))
+    while np_ > 0 and fixed + up(c.b * c.hq * np_ * 16384) + up(c.b * c.hq * np_ * 128) > ws_bytes:
+        np_ -= 1
+    n, lo = 0, 0
+    while lo < nqb:
+        hi, k = lo, 0
+        while hi < nqb and (hi == lo or k + live(hi) <= np_):
+            k += live(hi)
+            hi += 1
+        n, lo = n + 1, hi
+    return n
+
+
+def time_banded(st, dma, torch, np, n_iter=5):
+    """dma_attn_bwd (all phases, one call) with the one-pass workspace, with one mask plane of it and
+    with the smallest: the backward then runs in bands of query blocks, trading time for memory."""
+    c = st.c
+    sizes = (("one_pass", st.ws.numel()), ("one_mask_plane", c.b * c.hkv * c.lq * c.lk * 2),
+             ("min", dma.dma_attn_bwd_workspace_size_min(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal)))
+    out = {"workload": describe(c)}
+    for label, nbytes in sizes:
+        ws = st.ws[:nbytes]
+
+        def bwd():
+            dma.dma_attn_bwd(st.q, st.k, st.v, st.mask, st.bias, st.state, st.o, st.do, st.lse, c.scale_f32, c.causal,
+                             st.dq, st.dk, st.dv, st.dbias, ws, st.stream)
+
+        bwd()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_iter)]
+        for a, b in ev:
+            a.record(st.stream)
+            bwd()
+            b.record(st.stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        out[label] = {"workspace_bytes": int(nbytes), "bands": band_count(c, nbytes), "bwd_ms": round(ms, 3)}
+        print(f"[bench] {c.name} backward, {label} workspace: {ms:.2f} ms", file=sys.stderr, flush=True)
+    return out
+
+
 def describe(c) -> str:
     m = f"top-k {c.topk}" if c.mask == "topk" else ("document" if c.mask == "doc" else c.mask)
     return (f"{c.name}: b={c.b} L={c.lq} Hq={c.hq} Hkv={c.hkv} d={c.d} {m} mask, "
@@ -579,6 +638,8 @@ def main():
                 ws = Step(wc, dma, torch, np, path=path)
                 method[name if path == paths[0] else f"{name}_{path}"] = method_measure(
                     ws, np, torch, flush, bound="hbm" if wc.mask == "doc" else "mfma")
+                if name == "long" and not args.no_next:
+                    line.setdefault("next_rows", {})["banded_backward"] = time_banded(ws, dma, torch, np)
                 ws.free()
                 del ws
         line["method"] = method

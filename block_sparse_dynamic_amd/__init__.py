@@ -48,6 +48,8 @@ _lib.dma_attn_fwd_classify.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64
                                        _vp, _vp, _vp]
 _lib.dma_attn_bwd_workspace_size.restype = _sz
 _lib.dma_attn_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32]
+_lib.dma_attn_bwd_workspace_size_min.restype = _sz
+_lib.dma_attn_bwd_workspace_size_min.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32]
 _lib.dma_attn_bwd.restype = _i32
 _lib.dma_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32,
                               _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -202,6 +204,10 @@ def dma_attn_fwd_classify(q, k, v, mask, bias, scale: float, is_causal: bool, bl
 
 def dma_attn_bwd_workspace_size(b: int, lq: int, lk: int, hq: int, hkv: int, d: int, is_causal: bool) -> int:
     return int(_lib.dma_attn_bwd_workspace_size(b, lq, lk, hq, hkv, d, int(bool(is_causal))))
+
+
+def dma_attn_bwd_workspace_size_min(b: int, lq: int, lk: int, hq: int, hkv: int, d: int, is_causal: bool) -> int:
+    return int(_lib.dma_attn_bwd_workspace_size_min(b, lq, lk, hq, hkv, d, int(bool(is_causal))))
 
 
 def dma_attn_bwd(q, k, v, mask, bias, block_state, o, dout, lse, scale: float, is_causal: bool, dq, dk, dv, dbias,
@@ -403,6 +409,7 @@ def dma_attention(query, key, value, attn_mask=None, attn_bias=None, is_causal=F
 
 __all__ = [
     "dma_block_size", "dma_status_string", "dma_block_classify", "dma_attn_fwd", "dma_attn_bwd_workspace_size",
+    "dma_attn_bwd_workspace_size_min",
     "dma_attn_bwd", "dma_attention", "block_state_shape", "DMAError", "LIB_PATH", "HEADER_PATH",
     "dma_block_classify_ranges", "dma_attn_fwd_ranges", "dma_attn_bwd_ranges", "dma_topk_mask", "dma_mask_bits_size",
     "dma_block_classify_bits", "dma_attn_fwd_bits", "dma_attn_bwd_bits", "dma_attn_bwd_noalloc", "dma_attn_bwd_part",

@@ -1,5 +1,6 @@
 // C ABI of libdma.so: argument validation and dispatch to the gfx950 kernels.
 // Declarations, layouts and error behaviour are documented in include/dma.h.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 
@@ -200,20 +201,26 @@ namespace {
 //   rows       fp32 2 x [b, hq, lq]                -rowsum(dO * O), then -lse * log2(e)
 //   pair_base  int64 [nqb + 1]                     first dS tile pair of each query block
 //   kt         bf16 [b, hkv, d, nkb2 * 128]        K transposed
-//   ds         bf16 [b, hkv, npairs, G, 2, 32*128] dS tile slots of every live (query block, key pair)
-//   dsmap      u64  [b, hkv, npairs, G, 2, 8]      which 16-byte chunks of each slot are stored
-//   dkv        fp32 2 x [b, lk, hkv, d]            dK, dV sums of the split key pairs (only when
-//                                                  the backward splits them, see bwd_splits)
+//   ds         bf16 [b, hkv, np, G, 2, 32*128]     dS tile slots of np (query block, key pair) pairs
+//                                                  per plane: every live one, or those of a band
+//   dsmap      u64  [b, hkv, np, G, 2, 8]          which 16-byte chunks of each slot are stored
+//   dkv        fp32 2 x [b, lk, hkv, d]            dK, dV sums of split key pairs or of a banded
+//                                                  backward (only then)
 struct WsLayout {
   size_t rows, pair_base, kt, ds, dsmap, dkv, total;
   int64_t npairs;
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
-WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int causal) {
+constexpr size_t kSlotPairBytes = 2 * 32 * 128 * sizeof(uint16_t) + 2 * 8 * sizeof(uint64_t);  // per head
+int64_t all_live_pairs(int64_t lq, int64_t lk, int causal) {
+  int64_t np = 0;
+  for (int64_t qb = 0, nqb = (lq + 63) / 64; qb < nqb; ++qb) np += dma::live_pairs(qb, lq, lk, causal);
+  return np;
+}
+// Slots for np pairs per plane; the fp32 dK/dV sums when acc.
+WsLayout ws_layout_n(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int64_t np, bool acc) {
   WsLayout w = {};
   const int64_t nqb = (lq + 63) / 64, nkb2 = ((lk + 63) / 64 + 1) / 2;
-  int64_t np = 0;
-  for (int64_t qb = 0; qb < nqb; ++qb) np += dma::live_pairs(qb, lq, lk, causal);
   w.npairs = np;
   w.rows = 0;
   w.pair_base = w.rows + up256((size_t)2 * b * hq * lq * sizeof(float));
@@ -221,9 +228,18 @@ WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, i
   w.ds = w.kt + up256((size_t)b * hkv * d * nkb2 * 128 * sizeof(uint16_t));
   w.dsmap = w.ds + up256((size_t)b * hq * np * 2 * 32 * 128 * sizeof(uint16_t));
   w.dkv = w.dsmap + up256((size_t)b * hq * np * 2 * 8 * sizeof(uint64_t));
-  const size_t dkv_bytes = dma::bwd_splits(b, hkv, lq, lk, causal) > 1 ? (size_t)2 * b * lk * hkv * d * sizeof(float) : 0;
-  w.total = w.dkv + up256(dkv_bytes);
+  w.total = w.dkv + up256(acc ? (size_t)2 * b * lk * hkv * d * sizeof(float) : 0);
   return w;
+}
+// One pass over all query blocks (the fastest backward).
+WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int causal) {
+  return ws_layout_n(b, lq, lk, hq, hkv, d, all_live_pairs(lq, lk, causal),
+                     dma::bwd_splits(b, hkv, lq, lk, causal) > 1);
+}
+// Bands of single query blocks: the smallest workspace the backward runs in.
+WsLayout ws_layout_min(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int causal) {
+  const int64_t nqb = (lq + 63) / 64;
+  return ws_layout_n(b, lq, lk, hq, hkv, d, dma::live_pairs(nqb - 1, lq, lk, causal), true);
 }
 }  // namespace
 
@@ -235,6 +251,12 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq
   return ws_layout(b, lq, lk, hq, hkv, d, is_causal).total;
 }
 
+size_t dma_attn_bwd_workspace_size_min(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                                       int is_causal) {
+  if (!sizes_ok(b, lq, lk, hq, hkv) || d < 1 || hq % hkv != 0 || (is_causal != 0 && is_causal != 1)) return 0;
+  return ws_layout_min(b, lq, lk, hq, hkv, d, is_causal).total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -243,7 +265,7 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   const uint16_t* o, const uint16_t* dout, const float* lse, int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv,
                   int64_t d, float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
                   void* workspace, size_t workspace_bytes, void* stream, bool validate_only = false,
-                  int parts = dma::kBwdAll) {
+                  int parts = dma::kBwdAll, bool allow_bands = false) {
   int st = check_attn(q, k, v, mask, bias, block_state, b, lq, lk, hq, hkv, d, is_causal);
   if (st != DMA_OK) return st;
   if (!o || !dout || !lse || !dq || !dk || !dv || !workspace) return DMA_ERR_INVALID_ARGUMENT;
@@ -256,8 +278,21 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   if (!scale_in_range(scale)) return DMA_ERR_UNSUPPORTED;
   // per-row byte ranges of dbias and row indices must stay within 32-bit offsets
   if (lk > kMaxLen || lq > kMaxLen) return DMA_ERR_UNSUPPORTED;
-  const WsLayout wl = ws_layout(b, lq, lk, hq, hkv, d, is_causal);
-  if (workspace_bytes < wl.total) return DMA_ERR_WORKSPACE_TOO_SMALL;
+  WsLayout wl = ws_layout(b, lq, lk, hq, hkv, d, is_causal);
+  int64_t band_pairs = 0;
+  if (workspace_bytes < wl.total) {
+    // a smaller workspace: bands of query blocks, each with as many slot pairs as fit
+    if (!allow_bands) return DMA_ERR_WORKSPACE_TOO_SMALL;
+    const WsLayout fixed = ws_layout_n(b, lq, lk, hq, hkv, d, 0, true);
+    if (workspace_bytes < fixed.total) return DMA_ERR_WORKSPACE_TOO_SMALL;
+    // an upper bound (the slot regions' 256-byte rounding only adds), then down to what fits
+    int64_t np = (int64_t)((workspace_bytes - fixed.total) / ((size_t)b * hq * kSlotPairBytes));
+    np = std::min(np, wl.npairs);
+    while (np > 0 && ws_layout_n(b, lq, lk, hq, hkv, d, np, true).total > workspace_bytes) --np;
+    if (np < dma::live_pairs((lq + 63) / 64 - 1, lq, lk, is_causal)) return DMA_ERR_WORKSPACE_TOO_SMALL;
+    wl = ws_layout_n(b, lq, lk, hq, hkv, d, np, true);
+    band_pairs = np;
+  }
   if (validate_only) return DMA_OK;
   dma::AttnArgs a = {};
   a.q = q;
@@ -284,7 +319,9 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.ds = reinterpret_cast<uint16_t*>(ws + wl.ds);
   a.dsmap = reinterpret_cast<uint64_t*>(ws + wl.dsmap);
   a.npairs = wl.npairs;
-  a.dkv_acc = dma::bwd_splits(b, hkv, lq, lk, is_causal) > 1 ? reinterpret_cast<float*>(ws + wl.dkv) : nullptr;
+  a.band_pairs = band_pairs;
+  a.dkv_acc = (band_pairs > 0 || dma::bwd_splits(b, hkv, lq, lk, is_causal) > 1) ? reinterpret_cast<float*>(ws + wl.dkv)
+                                                                                  : nullptr;
   a.b = b;
   a.lq = lq;
   a.lk = lk;
@@ -304,7 +341,8 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
                  int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, float scale, int is_causal, uint16_t* dq,
                  uint16_t* dk, uint16_t* dv, uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
   return attn_bwd_impl(q, k, v, mask, nullptr, nullptr, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq, hkv, d,
-                       scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+                       scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream, false, dma::kBwdAll,
+                       /*allow_bands=*/true);
 }
 
 int dma_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,
@@ -328,7 +366,8 @@ int dma_attn_bwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!mask_bits || !aligned16(mask_bits)) return DMA_ERR_INVALID_ARGUMENT;
   return attn_bwd_impl(q, k, v, nullptr, nullptr, nullptr, mask_bits, bias, block_state, o, dout, lse, b, lq, lk, hq,
-                       hkv, d, scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+                       hkv, d, scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream, false,
+                       dma::kBwdAll, /*allow_bands=*/true);
 }
 
 int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* start_row,
@@ -338,7 +377,8 @@ int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* dbias, void* workspace, size_t workspace_bytes, void* stream) {
   if (!start_row || !end_row || !aligned4(start_row) || !aligned4(end_row)) return DMA_ERR_INVALID_ARGUMENT;
   return attn_bwd_impl(q, k, v, nullptr, start_row, end_row, nullptr, bias, block_state, o, dout, lse, b, lq, lk, hq,
-                       hkv, d, scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+                       hkv, d, scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream, false,
+                       dma::kBwdAll, /*allow_bands=*/true);
 }
 
 int dma_topk_mask(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out, uint16_t* bias_out,

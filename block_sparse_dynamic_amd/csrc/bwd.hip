@@ -172,9 +172,14 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   uint16_t* dbias;
-  float* dkv_acc;  // fp32 dK, dV sums when the pairs are split (splits > 1)
+  float* dkv_acc;  // fp32 dK, dV sums when the pairs are split (splits > 1) or the query blocks banded
   int64_t lq, lk, hq, hkv;
+  // This launch covers query blocks [band_lo, band_hi] (all of them unless the backward runs in
+  // bands); the dS slots hold that range's pairs only, the first of which is pair_base[band_lo] = pb_lo.
+  int64_t pb_lo;
+  int band_lo, band_hi;
   int G, nqb, nkb, nkb2, splits, total_wg;
+  int wg_pairs;  // key pairs per plane in the grid: those live for some query block of the range
   float scale;
   int causal;
 };
@@ -278,14 +283,16 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// dBias zeros of one 64-row query block z = plane * nqb + qb: every 128-key pair that no
+// dBias zeros of one 64-row query block z = plane * nq + (qb - band_lo) (nq query blocks in the
+// launch's range): every 128-key pair that no
 // compute workgroup visits for it, i.e. a pair SKIP in both halves or one that causality leaves
 // without a valid position, gets 64 rows x 128 keys of zeros (clipped to lq and lk), 16-byte
 // stores, 256 bytes per row.  These workgroups follow the compute workgroups in the grid, so the
 // streaming writes fill the causal tail of the compute.  `stc` is 2048 bytes of LDS that caches
 // the block states of the row.
 __device__ void zero_fill_dbias(const BwdParams& p, int z, uint8_t* stc) {
-  const int plane = z / p.nqb, qb = z % p.nqb, tid = threadIdx.x;
+  const int nq = p.band_hi - p.band_lo + 1;
+  const int plane = z / nq, qb = p.band_lo + z % nq, tid = threadIdx.x;
   const int64_t i0 = (int64_t)qb * kBlock;
   const uint8_t* st_row = p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
   uint16_t* base = p.dbias + (int64_t)plane * p.lq * p.lk + i0 * p.lk;
@@ -335,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
     return;
   }
   const int w = blockIdx.x;
-  const int per_plane = p.nkb2 * p.splits;
+  const int per_plane = p.wg_pairs * p.splits;
   const int t = xcd_task(w, p.total_wg, p.total_wg / per_plane);  // units: planes
   // low key blocks (most query blocks under causality) first; a split pair's halves next to each other
   const int plane = t / per_plane, KB = (t % per_plane) / p.splits, seg = (t % per_plane) % p.splits;
@@ -356,6 +363,8 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
     q_lo = seg == 0 ? upper : lo;
     q_hi = seg == 0 ? p.nqb - 1 : upper - 1;
   }
+  q_lo = max(q_lo, p.band_lo);
+  q_hi = min(q_hi, p.band_hi);
   // wave and the block states below are uniform across a wave; readfirstlane tells the compiler
   // so, which keeps the loop control and the buffer resources in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
       if (qb <= qb_hi && (hf == 0 || has_kb1) && KB < live_pairs(qb, p.lq, p.lk, p.causal))
         v = st_col[(int64_t)qb * p.nkb + hf];
       sm.st[hf][j] = v;
-      if (hf == 0 && qb <= qb_hi) sm.pb[j] = p.pair_base[qb];
+      if (hf == 0 && qb <= qb_hi) sm.pb[j] = p.pair_base[qb] - p.pb_lo;  // the range's own slot numbering
     }
     lds_barrier();
     cache_lo = lo;
@@ -580,6 +589,7 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();     // buffers zeroed
   int qb = next_qb(q_hi, cs0, cs1);  // -1 when every block of the two key blocks is SKIP
+  const bool walked = qb >= 0;       // dK and dV are not all zero
   int rh = 0, hh = 0;
   if (qb >= 0) issue(0, qb, 0, 0, cs0, cs1);
   // first dS tile pair of the current query block, kept as read from LDS (uniform): the next
@@ -823,13 +833,17 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   }
 
   // ---- dK, dV: lane holds d = dt*16 + l16 for keys wave*16 + 4 g4 + e ------------------------
-  // (a split pair's halves add into the fp32 sums, which bwd_finalize_kernel converts)
+  // (a split pair's halves, or its parts in the bands of query blocks, add into the fp32 sums,
+  // zeroed before and converted by dkv_finalize_kernel after; a workgroup that walked nothing
+  // adds nothing.  Within a launch one or two workgroups add to a sum, and launches run in
+  // stream order, so the sums come out the same on every run)
+  if (p.dkv_acc != nullptr && !walked) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t key = (int64_t)kb0 * kBlock + wave * kWKeys + 4 * g4 + e;
     if (key < p.lk) {
       const int64_t off = ((bidx * p.lk + key) * p.hkv + g) * D + l16;
-      if (p.splits > 1) {
+      if (p.dkv_acc != nullptr) {
         float* acc_k = p.dkv_acc;
         float* acc_v = p.dkv_acc + (p.total_wg / per_plane) / p.hkv * p.lk * p.hkv * D;  // + b lk hkv d
 #pragma unroll
@@ -886,6 +900,8 @@ struct DqParams {
   const uint64_t* dsmap;
   uint16_t* dq;
   int64_t lq, lk, hq, hkv, npairs, ktrow;
+  int64_t pb_lo;      // first pair of the launch's query blocks (its slots are numbered from it)
+  int band_lo, nbq;   // the launch's query blocks: [band_lo, band_lo + nbq)
   int G, chunks, nqb, nkb, total_wg;
   float scale;
   int causal;
@@ -902,9 +918,9 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   __shared__ uint8_t srow[2 * kPairChunk];  // block states of the query block's row, pairs [cache_lo, + kPairChunk)
 
   const int w = blockIdx.x;
-  const int t = xcd_task(w, p.total_wg, p.total_wg / p.nqb);  // units: (plane, head chunk)
-  const int unit = t / p.nqb;
-  const int qb = p.nqb - 1 - (t % p.nqb);
+  const int t = xcd_task(w, p.total_wg, p.total_wg / p.nbq);  // units: (plane, head chunk)
+  const int unit = t / p.nbq;
+  const int qb = p.band_lo + p.nbq - 1 - (t % p.nbq);
   const int plane = unit / p.chunks, chunk = unit % p.chunks;
   const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -914,7 +930,7 @@ __global__ __launch_bounds__(HC * 128) void dq_kernel(DqParams p) {
   const int64_t head = g * p.G + hh;
 
   const int64_t npair = live_pairs(qb, p.lq, p.lk, p.causal);
-  const int64_t pbase = p.pair_base[qb];
+  const int64_t pbase = p.pair_base[qb] - p.pb_lo;
   const uint8_t* st_row = p.state + ((int64_t)plane * p.nqb + qb) * p.nkb;
   const uint16_t* ktp = p.kt + (int64_t)plane * D * p.ktrow;
   // the slot of pair KB for this wave: slot0 + KB * G * 2
@@ -1142,39 +1158,51 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   p.nqb = nqb;
   p.nkb = nkb;
   p.nkb2 = nkb2;
-  p.splits = a.dkv_acc != nullptr ? bwd_splits(a.b, a.hkv, a.lq, a.lk, a.causal) : 1;
-  p.total_wg = (int)(a.b * a.hkv * p.nkb2 * p.splits);
+  const bool banded = a.band_pairs > 0;
+  p.splits = a.dkv_acc != nullptr && !banded ? bwd_splits(a.b, a.hkv, a.lq, a.lk, a.causal) : 1;
   p.scale = a.scale;
   p.causal = a.causal;
   const int MK = a.rstart != nullptr ? kMaskRanges : a.mbits != nullptr ? kMaskBits : kMaskDense;
-  if (parts & kBwdMain) {
-  // the compute workgroups, then (with a dBias output) one zero-fill workgroup per query block
-  const int64_t grid = p.total_wg + (a.dbias != nullptr ? a.b * a.hkv * (int64_t)nqb : 0);
-  auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p); };
-  // an item covers two heads when the group size is even
-  auto launch_d = [&](auto dconst) {
-    constexpr int D = decltype(dconst)::value;
-    if (p.G % 2 == 0) {
-      if (MK == kMaskRanges) launch_main(bwd_main_kernel<D, kMaskRanges, 2>);
-      else if (MK == kMaskBits) launch_main(bwd_main_kernel<D, kMaskBits, 2>);
-      else launch_main(bwd_main_kernel<D, kMaskDense, 2>);
-    } else {
-      if (MK == kMaskRanges) launch_main(bwd_main_kernel<D, kMaskRanges, 1>);
-      else if (MK == kMaskBits) launch_main(bwd_main_kernel<D, kMaskBits, 1>);
-      else launch_main(bwd_main_kernel<D, kMaskDense, 1>);
-    }
+  const int G = p.G;
+  const int HC = G >= 4 ? 4 : G;
+
+  // The main kernel over query blocks [lo, hi] whose dS slots start at pair pb_lo and hold
+  // npairs pairs per plane: the compute workgroups (the key pairs live for some block of the
+  // range), then (with a dBias output) one zero-fill workgroup per query block of the range.
+  auto run_main = [&](int lo, int hi, int64_t pb_lo, int64_t npairs) -> hipError_t {
+    p.band_lo = lo;
+    p.band_hi = hi;
+    p.pb_lo = pb_lo;
+    p.npairs = npairs;
+    p.wg_pairs = (int)live_pairs(hi, a.lq, a.lk, a.causal);
+    p.total_wg = (int)(a.b * a.hkv * p.wg_pairs * p.splits);
+    const int64_t grid = p.total_wg + (a.dbias != nullptr ? a.b * a.hkv * (int64_t)(hi - lo + 1) : 0);
+    if (grid == 0) return hipSuccess;
+    auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p); };
+    // an item covers two heads when the group size is even
+    auto launch_d = [&](auto dconst) {
+      constexpr int D = decltype(dconst)::value;
+      if (p.G % 2 == 0) {
+        if (MK == kMaskRanges) launch_main(bwd_main_kernel<D, kMaskRanges, 2>);
+        else if (MK == kMaskBits) launch_main(bwd_main_kernel<D, kMaskBits, 2>);
+        else launch_main(bwd_main_kernel<D, kMaskDense, 2>);
+      } else {
+        if (MK == kMaskRanges) launch_main(bwd_main_kernel<D, kMaskRanges, 1>);
+        else if (MK == kMaskBits) launch_main(bwd_main_kernel<D, kMaskBits, 1>);
+        else launch_main(bwd_main_kernel<D, kMaskDense, 1>);
+      }
+    };
+    if (a.d == 64) launch_d(std::integral_constant<int, 64>{});
+    else launch_d(std::integral_constant<int, 128>{});
+    return hipGetLastError();
   };
-  if (a.d == 64) launch_d(std::integral_constant<int, 64>{});
-  else launch_d(std::integral_constant<int, 128>{});
-  if (a.dkv_acc != nullptr) {
+  auto run_finalize = [&]() -> hipError_t {
+    if (a.dkv_acc == nullptr) return hipSuccess;
     const int64_t n4 = a.b * a.lk * a.hkv * a.d / 4;
     hipLaunchKernelGGL(dkv_finalize_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, stream,
                        a.dkv_acc, a.dk, a.dv, n4);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  }
-  if (!(parts & kBwdDq)) return hipSuccess;
+    return hipGetLastError();
+  };
 
   DqParams q;
   q.state = a.state;
@@ -1187,24 +1215,52 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   q.lk = a.lk;
   q.hq = a.hq;
   q.hkv = a.hkv;
-  q.npairs = a.npairs;
   q.ktrow = ktrow;
-  q.G = p.G;
-  const int HC = q.G >= 4 ? 4 : q.G;
-  q.chunks = q.G / HC;
+  q.G = G;
+  q.chunks = G / HC;
   q.nqb = nqb;
   q.nkb = nkb;
-  q.total_wg = (int)(a.b * a.hkv * q.chunks * nqb);
   q.scale = a.scale;
   q.causal = a.causal;
-  if (a.d == 64) {
-    if (HC == 1) return launch_dq_t<64, 1>(q, stream);
-    if (HC == 2) return launch_dq_t<64, 2>(q, stream);
-    return launch_dq_t<64, 4>(q, stream);
+  // The dQ kernel over query blocks [lo, hi] (slots as for run_main).
+  auto run_dq = [&](int lo, int hi, int64_t pb_lo, int64_t npairs) -> hipError_t {
+    q.band_lo = lo;
+    q.nbq = hi - lo + 1;
+    q.pb_lo = pb_lo;
+    q.npairs = npairs;
+    q.total_wg = (int)(a.b * a.hkv * q.chunks * q.nbq);
+    if (a.d == 64) {
+      if (HC == 1) return launch_dq_t<64, 1>(q, stream);
+      if (HC == 2) return launch_dq_t<64, 2>(q, stream);
+      return launch_dq_t<64, 4>(q, stream);
+    }
+    if (HC == 1) return launch_dq_t<128, 1>(q, stream);
+    if (HC == 2) return launch_dq_t<128, 2>(q, stream);
+    return launch_dq_t<128, 4>(q, stream);
+  };
+
+  hipError_t e = hipSuccess;
+  if (!banded) {
+    if (parts & kBwdMain) {
+      if ((e = run_main(0, nqb - 1, 0, a.npairs)) != hipSuccess) return e;
+      if ((e = run_finalize()) != hipSuccess) return e;
+    }
+    if (parts & kBwdDq) return run_dq(0, nqb - 1, 0, a.npairs);
+    return hipSuccess;
   }
-  if (HC == 1) return launch_dq_t<128, 1>(q, stream);
-  if (HC == 2) return launch_dq_t<128, 2>(q, stream);
-  return launch_dq_t<128, 4>(q, stream);
+  // Bands of consecutive query blocks whose live pairs fit the dS slots (a.band_pairs per plane),
+  // each taken by the main kernel and then the dQ kernel; dK and dV gather in the fp32 sums.
+  int64_t pb_lo = 0;
+  for (int lo = 0; lo < nqb;) {
+    const int hi = (int)bwd_band_end(lo, nqb, a.lq, a.lk, a.causal, a.band_pairs) - 1;
+    int64_t np = 0;
+    for (int qb = lo; qb <= hi; ++qb) np += live_pairs(qb, a.lq, a.lk, a.causal);
+    if ((e = run_main(lo, hi, pb_lo, np)) != hipSuccess) return e;
+    if ((e = run_dq(lo, hi, pb_lo, np)) != hipSuccess) return e;
+    pb_lo += np;
+    lo = hi + 1;
+  }
+  return run_finalize();
 }
 
 }  // namespace dma

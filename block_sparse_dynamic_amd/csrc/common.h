@@ -208,7 +208,10 @@ struct AttnArgs {
                       // holding only the tile's nonzero 16-byte chunks, packed per writing wave
   uint64_t* dsmap;    // per slot 8 masks: which chunks of each (wave, half) of the writer are stored
   int64_t npairs;     // live key-block pairs of one plane (pair_base[nqb])
-  float* dkv_acc;     // fp32 [2][b, lk, hkv, d]: dK, dV sums of split pairs (bwd_splits > 1), else null
+  float* dkv_acc;     // fp32 [2][b, lk, hkv, d]: dK, dV sums of split pairs (bwd_splits > 1) or of
+                      // a backward in bands, else null
+  int64_t band_pairs; // backward in bands of query blocks whose live pairs fit this many dS slot
+                      // pairs per plane (bwd_band_end); 0: one pass over all query blocks
   int64_t b, lq, lk, hq, hkv, d;
   float scale;
   int causal;
@@ -234,6 +237,19 @@ __host__ __device__ inline int64_t live_pairs(int64_t qb, int64_t lq, int64_t lk
   if (last < 0) return 0;
   const int64_t n = last / 128 + 1;
   return n < nkb2 ? n : nkb2;
+}
+
+// The backward in bands: the band that starts at query block lo ends (exclusive) where adding
+// the next block's live pairs would pass max_pairs; it holds at least one block.
+inline int64_t bwd_band_end(int64_t lo, int64_t nqb, int64_t lq, int64_t lk, int causal, int64_t max_pairs) {
+  int64_t hi = lo, n = 0;
+  while (hi < nqb) {
+    const int64_t lp = live_pairs(hi, lq, lk, causal);
+    if (hi > lo && n + lp > max_pairs) break;
+    n += lp;
+    ++hi;
+  }
+  return hi;
 }
 
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);

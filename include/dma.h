@@ -170,9 +170,24 @@ int dma_attn_fwd_classify(const uint16_t* q, const uint16_t* k, const uint16_t* 
  * each pair's walk is split over two workgroups and the workspace also holds
  * fp32 dK and dV sums (2 x b x lk x hkv x d floats); two partial sums added
  * onto zero in either order give the same bits, so the results stay
- * deterministic. */
+ * deterministic.  This is the workspace of the fastest backward, one pass over
+ * all query blocks; dma_attn_bwd also runs in less (down to
+ * dma_attn_bwd_workspace_size_min). */
 size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
                                    int is_causal);
+
+/* The smallest workspace dma_attn_bwd (and its _bits and _ranges variants)
+ * accepts for these sizes (0 for invalid sizes): the row terms, K transposed,
+ * fp32 dK and dV sums (2 x b x lk x hkv x d floats) and the dS slots of one
+ * 64-row query block.  Given less than dma_attn_bwd_workspace_size(), the
+ * backward runs in bands of consecutive query blocks, as many per band as the
+ * slots that fit hold (Flash-DMA README, features: memory linear in the
+ * sequence length); each band runs the main and dQ kernels, and dK and dV gather
+ * in the fp32 sums in band order, so the results stay deterministic (they
+ * differ from the one-pass results by the rounding of those sums).  Fewer,
+ * larger bands run faster: pass as much workspace as can be spared. */
+size_t dma_attn_bwd_workspace_size_min(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d,
+                                       int is_causal);
 
 /*
  * Backward pass (Flash-DMA README: gradients for query, key, value and bias,
@@ -187,9 +202,13 @@ size_t dma_attn_bwd_workspace_size(int64_t b, int64_t lq, int64_t lk, int64_t hq
  *   dbias       bf16 [b, hkv, lq, lk] = dS summed over the query heads of each
  *               group; exactly 0 on invalid entries and SKIP blocks.  May be
  *               NULL: then the bias gradient is not produced.
- *   workspace   device scratch of at least dma_attn_bwd_workspace_size() bytes,
- *               16-byte aligned, owned by the caller, contents on entry ignored
- * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL.  A key pair that
+ *   workspace   device scratch of at least dma_attn_bwd_workspace_size() bytes
+ *               for the one-pass backward, or of at least
+ *               dma_attn_bwd_workspace_size_min() bytes for a backward in bands
+ *               of query blocks; 16-byte aligned, owned by the caller, contents
+ *               on entry ignored
+ * Errors: as dma_attn_fwd, plus DMA_ERR_WORKSPACE_TOO_SMALL (workspace_bytes
+ *   below dma_attn_bwd_workspace_size_min()).  A key pair that
  *   the call's causality leaves no valid position for a query block is taken as
  *   SKIP whatever block_state says (such a pair owns no dS slot).
  * dq is deterministic: the same inputs give bit-identical outputs.
@@ -209,7 +228,9 @@ int dma_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const 
  *   DMA_BWD_MAIN     dk, dv and dbias, and the nonzero dS chunks into the workspace
  *   DMA_BWD_DQ       dq from the dS chunks
  * Arguments and errors are those of dma_attn_bwd (every call validates all of
- * them); an unknown part is DMA_ERR_INVALID_ARGUMENT.
+ * them), except that the phases run only as one pass: a workspace below
+ * dma_attn_bwd_workspace_size() is DMA_ERR_WORKSPACE_TOO_SMALL.  An unknown part
+ * is DMA_ERR_INVALID_ARGUMENT.
  */
 enum { DMA_BWD_PREPARE = 0, DMA_BWD_MAIN = 1, DMA_BWD_DQ = 2 };
 int dma_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mask,

@@ -166,14 +166,16 @@ class DeviceCase:
         self.dma.dma_attn_fwd(self.q, self.k, self.v, self.mask, self.bias, self.state, c.scale_f32, c.causal,
                               self.o, self.lse)
 
-    def backward(self, do=None, want_dbias=True):
+    def backward(self, do=None, want_dbias=True, ws_bytes=None):
+        """dma_attn_bwd with the one-pass workspace, or with ws_bytes of workspace."""
         c = self.c
         do = self.do if do is None else do
         self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
         self.dbias = (torch.full((c.b, c.hkv, c.lq, c.lk), float("nan"), dtype=torch.bfloat16, device="cuda")
                       if want_dbias else None)
-        ws = torch.empty(self.dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8,
-                         device="cuda")
+        if ws_bytes is None:
+            ws_bytes = self.dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         self.dma.dma_attn_bwd(self.q, self.k, self.v, self.mask, self.bias, self.state, self.o, do, self.lse,
                               c.scale_f32, c.causal, self.dq, self.dk, self.dv, self.dbias, ws)
 
@@ -229,7 +231,7 @@ def doc_ranges(c: synth.Case):
     return np.ascontiguousarray(s), np.ascontiguousarray(e)
 
 
-def check_full_case(c: synth.Case, n_blocks: int = 64, log=print, path: str = "dense"):
+def check_full_case(c: synth.Case, n_blocks: int = 64, log=print, path: str = "dense", ws_bytes: int | None = None):
     """Parity at the workload's full size, in the launch configuration the benchmark times.
 
     Whole block bitmap bit-exact; O, LSE, dQ, dBias on `n_blocks` seeded 64-row query
@@ -239,6 +241,7 @@ def check_full_case(c: synth.Case, n_blocks: int = 64, log=print, path: str = "d
     path: "dense" (dma_block_classify, dma_attn_fwd, dma_attn_bwd), "fused" (the forward that
     classifies, dma_attn_fwd_classify), "ranges" (column ranges of a document mask, the
     dma_*_ranges entry points) or "bits" (the bit-packed PARTIAL blocks, dma_*_bits).
+    ws_bytes: the backward's workspace (default: the one-pass size; less runs it in bands).
     """
     import concurrent.futures
     import os
@@ -257,7 +260,9 @@ def check_full_case(c: synth.Case, n_blocks: int = 64, log=print, path: str = "d
         nb = (n + 63) // 64
         ref_state[bb, g, r0 // 64: r0 // 64 + nb] = blk[:nb]
 
-    log(f"[{c.name}/{path}] generating and uploading inputs", flush=True)
+    if ws_bytes is None:
+        ws_bytes = dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal)
+    log(f"[{c.name}/{path}] generating and uploading inputs (backward workspace {ws_bytes} bytes)", flush=True)
     q, k, v, do = upload_dense(c)
     mask, bias = upload_mask_bias(c, chunk_rows=1024, on_chunk=on_chunk)
     state = torch.empty((c.b, c.hkv, nqb, nkb), dtype=torch.uint8, device="cuda")
@@ -265,7 +270,7 @@ def check_full_case(c: synth.Case, n_blocks: int = 64, log=print, path: str = "d
     lse = torch.empty((c.b, c.hq, c.lq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dbias = torch.full((c.b, c.hkv, c.lq, c.lk), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(dma.dma_attn_bwd_workspace_size(c.b, c.lq, c.lk, c.hq, c.hkv, c.d, c.causal), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     if path == "ranges":
         s, e = doc_ranges(c)
         ts, te = torch.from_numpy(s).cuda(), torch.from_numpy(e).cuda()

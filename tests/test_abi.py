@@ -56,7 +56,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("dma_block_classify", "dma_attn_fwd", "dma_attn_bwd", "dma_attn_bwd_workspace_size",
-                 "dma_block_size", "dma_status_string", "dma_topk_mask", "dma_block_classify_ranges",
+                 "dma_attn_bwd_workspace_size_min", "dma_block_size", "dma_status_string", "dma_topk_mask", "dma_block_classify_ranges",
                  "dma_attn_fwd_ranges", "dma_attn_bwd_ranges", "dma_mask_bits_size", "dma_block_classify_bits",
                  "dma_attn_fwd_bits", "dma_attn_bwd_bits"):
         assert name in syms
@@ -354,6 +354,23 @@ def test_noalloc_validates_before_touching_the_device(lib):
     assert call(b=2, lq=16384, lk=16384, hq=16, hkv=4) == WS_SMALL
     need = lib.dma_attn_bwd_workspace_size(1, 2048, 2048, 16, 4, 128, 1)
     assert need > 64 << 20 and call(lq=2048, lk=2048, hq=16, hkv=4) == WS_SMALL
+
+
+def test_bwd_workspace_below_the_minimum_is_rejected(lib):
+    """A workspace below dma_attn_bwd_workspace_size_min is rejected before anything is enqueued;
+    the phase entry point, which runs only as one pass, rejects anything below the full size."""
+    sz, i64, i32 = ctypes.c_size_t, ctypes.c_int64, ctypes.c_int
+    lib.dma_attn_bwd_workspace_size_min.restype = sz
+    lib.dma_attn_bwd_workspace_size_min.argtypes = [i64] * 6 + [i32]
+    full = lib.dma_attn_bwd_workspace_size(1, 2048, 2048, 4, 2, 128, 1)
+    least = lib.dma_attn_bwd_workspace_size_min(1, 2048, 2048, 4, 2, 128, 1)
+    assert 0 < least < full
+    assert bwd(lib, lq=2048, lk=2048, wsb=least - 1) == WS_SMALL
+    f = lib.dma_attn_bwd_part
+    vp, f32 = ctypes.c_void_p, ctypes.c_float
+    f.argtypes = [i32] + [vp] * 9 + [i64] * 6 + [f32, i32] + [vp] * 5 + [sz, vp]
+    assert f(1, *([P] * 9), 1, 2048, 2048, 4, 2, 128, 0.1, 1, *([P] * 5), least, None) == WS_SMALL
+    assert f(1, *([P] * 9), 1, 2048, 2048, 4, 2, 128, 0.1, 1, *([P] * 5), full - 1, None) == WS_SMALL
 
 
 def test_bwd_part_rejects_unknown_part(lib):

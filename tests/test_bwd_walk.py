@@ -16,6 +16,12 @@ lq).  Checked on random bitmaps, including bitmaps classified without causality 
 causal backward: every slot written lies inside the plane's slot range, no slot is written
 twice, and the dQ kernel reads exactly the slots the main kernel wrote.  The live pair count is
 pinned to the library's own through dma_attn_bwd_workspace_size.
+
+With a workspace smaller than the one-pass size the backward runs in bands of consecutive query
+blocks: a band ends where the next block's live pairs would overflow the slots that fit, each band
+numbers its slots from its first pair, and the main kernel's grid covers the pairs live at the
+band's last block.  The same checks hold per band, every (query block, pair) item is walked in
+exactly one band, and the smallest workspace is pinned through dma_attn_bwd_workspace_size_min.
 """
 import ctypes
 import os
@@ -62,17 +68,40 @@ def segments(KB, nqb, lq, lk, causal, splits):
     return [(upper, nqb - 1), (lo, upper - 1)]
 
 
-def main_kernel_slots(state, b, hkv, G, lq, lk, causal):
-    """Slots the backward main kernel stores, in its walk order."""
+def bands(nqb, lq, lk, causal, max_pairs):
+    """[lo, hi] of the bands of query blocks: a band ends where the next block's live pairs would
+    pass max_pairs (each band holds at least one block); one band without a limit."""
+    if max_pairs is None:
+        return [(0, nqb - 1)]
+    out, lo = [], 0
+    while lo < nqb:
+        hi, n = lo, 0
+        while hi < nqb:
+            lp = live_pairs(hi, lq, lk, causal)
+            if hi > lo and n + lp > max_pairs:
+                break
+            n += lp
+            hi += 1
+        out.append((lo, hi - 1))
+        lo = hi
+    return out
+
+
+def main_kernel_slots(state, b, hkv, G, lq, lk, causal, band=None, items=None):
+    """Slots the backward main kernel stores, in its walk order, for the query blocks of `band`
+    ([lo, hi], all of them by default); `items` collects the (plane, qb, KB) items walked."""
     nqb, nkb = state.shape[2], state.shape[3]
-    nkb2 = (nkb + 1) // 2
+    lo_b, hi_b = band if band is not None else (0, nqb - 1)
     pair_base = np.concatenate([[0], np.cumsum([live_pairs(qb, lq, lk, causal) for qb in range(nqb)])])
-    npairs = int(pair_base[-1])
+    pb_lo = int(pair_base[lo_b])
+    npairs = int(pair_base[hi_b + 1]) - pb_lo
+    wg_pairs = live_pairs(hi_b, lq, lk, causal)  # the grid's pairs
+    splits = bwd_splits(b, hkv, lq, lk, causal) if band is None else 1
     hpi = 2 if G % 2 == 0 else 1
     slots = []
     for plane in range(b * hkv):
         bb, g = divmod(plane, hkv)
-        for KB in range(nkb2):
+        for KB in range(wg_pairs):
             kb0 = 2 * KB
             has_kb1 = kb0 + 1 < nkb
             cache_lo = nqb
@@ -88,7 +117,8 @@ def main_kernel_slots(state, b, hkv, G, lq, lk, causal):
                             st[hf, j] = state[bb, g, qb, kb0 + hf]
                 return lo, st
 
-            for q_lo, q_hi in segments(KB, nqb, lq, lk, causal, bwd_splits(b, hkv, lq, lk, causal)):
+            for q_lo, q_hi in segments(KB, nqb, lq, lk, causal, splits):
+                q_lo, q_hi = max(q_lo, lo_b), min(q_hi, hi_b)
                 cache_lo = nqb  # each workgroup starts with an empty cache
                 qb = q_hi
                 while qb >= q_lo:
@@ -96,28 +126,32 @@ def main_kernel_slots(state, b, hkv, G, lq, lk, causal):
                         cache_lo, cache = fill(qb)
                     s0, s1 = cache[0, qb - cache_lo], cache[1, qb - cache_lo]
                     if s0 != SKIP or s1 != SKIP:
+                        if items is not None:
+                            items.append((plane, qb, KB))
                         halves = 1 if qb * 64 + 32 >= lq else 2
                         for rh in range(halves):
                             for hh in range(0, G, hpi):
-                                slot_a = ((plane * npairs + int(pair_base[qb]) + KB) * G + hh) * 2 + rh
+                                slot_a = ((plane * npairs + int(pair_base[qb]) - pb_lo + KB) * G + hh) * 2 + rh
                                 for h2 in range(hpi):
                                     slots.append((plane, slot_a + 2 * h2))
                     qb -= 1
     return slots, npairs
 
 
-def dq_kernel_slots(state, b, hkv, G, lq, lk, causal, npairs):
+def dq_kernel_slots(state, b, hkv, G, lq, lk, causal, npairs, band=None):
     nqb, nkb = state.shape[2], state.shape[3]
+    lo_b, hi_b = band if band is not None else (0, nqb - 1)
     pair_base = np.concatenate([[0], np.cumsum([live_pairs(qb, lq, lk, causal) for qb in range(nqb)])])
+    pb_lo = int(pair_base[lo_b])
     reads = []
     for plane in range(b * hkv):
         bb, g = divmod(plane, hkv)
-        for qb in range(nqb):
+        for qb in range(lo_b, hi_b + 1):
             for hh in range(G):
                 for rh in range(2):
                     if rh == 1 and qb * 64 + 32 >= lq:
                         continue  # rows past lq: nothing written, nothing needed
-                    slot0 = ((plane * npairs + int(pair_base[qb])) * G + hh) * 2 + rh
+                    slot0 = ((plane * npairs + int(pair_base[qb]) - pb_lo) * G + hh) * 2 + rh
                     for kb2 in range(live_pairs(qb, lq, lk, causal)):
                         s0 = state[bb, g, qb, 2 * kb2]
                         s1 = state[bb, g, qb, 2 * kb2 + 1] if 2 * kb2 + 1 < nkb else SKIP
@@ -165,3 +199,61 @@ def test_live_pairs_match_the_library(b, lq, lk, G, hkv, causal):
     for d in (64, 128):
         assert L.dma_attn_bwd_workspace_size(b, lq, lk, G * hkv, hkv, d, causal) == ws_size(b, lq, lk, G * hkv, hkv, d,
                                                                                             causal)
+
+
+def ws_min_size(b, lq, lk, hq, hkv, d, causal):
+    """The dS slots of the largest single query block (the last), plus the fp32 dK/dV sums."""
+    up = lambda x: (x + 255) // 256 * 256
+    nqb, nkb2 = (lq + 63) // 64, ((lk + 63) // 64 + 1) // 2
+    np_ = live_pairs(nqb - 1, lq, lk, causal)
+    return up(2 * b * hq * lq * 4) + up((nqb + 1) * 8) + up(b * hkv * d * nkb2 * 128 * 2) + \
+        up(b * hq * np_ * 64 * 128 * 2) + up(b * hq * np_ * 2 * 8 * 8) + up(2 * b * lk * hkv * d * 4)
+
+
+@pytest.mark.parametrize("b,lq,lk,G,hkv,causal", CASES[:-1])
+@pytest.mark.parametrize("which", ["min", "third"])
+def test_banded_walk_covers_every_item_once(b, lq, lk, G, hkv, causal, which):
+    rng = np.random.default_rng(lq * 5 + lk + G + (which == "min"))
+    nqb, nkb = (lq + 63) // 64, (lk + 63) // 64
+    state = rng.integers(0, 3, size=(b, hkv, nqb, nkb)).astype(np.uint8)
+    total = sum(live_pairs(qb, lq, lk, causal) for qb in range(nqb))
+    smallest = live_pairs(nqb - 1, lq, lk, causal)
+    max_pairs = smallest if which == "min" else max(smallest, total // 3)
+    parts = bands(nqb, lq, lk, causal, max_pairs)
+    assert parts[0][0] == 0 and parts[-1][1] == nqb - 1
+    assert all(parts[i][1] + 1 == parts[i + 1][0] for i in range(len(parts) - 1)), "bands not consecutive"
+    all_items = []
+    for band in parts:
+        lo, hi = band
+        npairs = sum(live_pairs(qb, lq, lk, causal) for qb in range(lo, hi + 1))
+        assert npairs <= max_pairs or lo == hi, "a band of several blocks overflows the slots"
+        items = []
+        slots, np_ = main_kernel_slots(state, b, hkv, G, lq, lk, causal, band=band, items=items)
+        assert np_ == npairs
+        per_plane = npairs * G * 2
+        assert all(plane * per_plane <= s < (plane + 1) * per_plane for plane, s in slots), "slot outside the band"
+        written = [s for _, s in slots]
+        assert len(written) == len(set(written)), "a slot written twice"
+        reads = dq_kernel_slots(state, b, hkv, G, lq, lk, causal, npairs, band=band)
+        assert set(reads) == set(slots), "the dQ kernel's reads differ from the main kernel's writes"
+        assert all(lo <= qb <= hi for _, qb, _ in items)
+        all_items += items
+    one_pass = []
+    main_kernel_slots(state, b, hkv, G, lq, lk, causal, items=one_pass)
+    assert len(all_items) == len(set(all_items)), "an item walked in two bands"
+    assert set(all_items) == set(one_pass), "the bands walk other items than the one pass"
+
+
+@pytest.mark.parametrize("b,lq,lk,G,hkv,causal", CASES[:-1])
+def test_min_workspace_matches_the_library(b, lq, lk, G, hkv, causal):
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    L = ctypes.CDLL(LIB)
+    f = L.dma_attn_bwd_workspace_size_min
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int]
+    for d in (64, 128):
+        want = ws_min_size(b, lq, lk, G * hkv, hkv, d, causal)
+        assert f(b, lq, lk, G * hkv, hkv, d, causal) == want
+        assert want <= ws_size(b, lq, lk, G * hkv, hkv, d, causal) + 2 * b * lk * hkv * d * 4 + 256
+    assert f(0, lq, lk, G * hkv, hkv, 64, causal) == 0
