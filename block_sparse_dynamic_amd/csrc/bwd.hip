@@ -349,9 +349,10 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   const int kb0 = 2 * KB;
   const bool has_kb1 = kb0 + 1 < p.nkb;
   const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
-  // Query blocks this workgroup walks, [q_lo, q_hi]: all of them, or one half of the pair's live
-  // blocks (the first live one is the smallest qb with KB < live_pairs(qb), which only grows with qb)
-  int q_lo = 0, q_hi = p.nqb - 1;
+  // Query blocks this workgroup walks, [q_lo, q_hi]: all those of the launch's range, or one half
+  // of the pair's live blocks in it (the first live one is the smallest qb with KB < live_pairs(qb),
+  // which only grows with qb)
+  int q_lo = p.band_lo, q_hi = p.band_hi;
   if (p.splits > 1) {
     int lo = 0, hi = p.nqb;  // first live query block, found by bisection
     while (lo < hi) {
@@ -359,12 +360,11 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
       if (KB < live_pairs(mid, p.lq, p.lk, p.causal)) hi = mid;
       else lo = mid + 1;
     }
-    const int upper = lo + (p.nqb - lo) / 2;  // segment 0: [upper, nqb), segment 1: [lo, upper)
+    lo = max(lo, p.band_lo);
+    const int upper = lo + (p.band_hi + 1 - lo) / 2;  // segment 0: [upper, band_hi], segment 1: [lo, upper)
     q_lo = seg == 0 ? upper : lo;
-    q_hi = seg == 0 ? p.nqb - 1 : upper - 1;
+    q_hi = seg == 0 ? p.band_hi : upper - 1;
   }
-  q_lo = max(q_lo, p.band_lo);
-  q_hi = min(q_hi, p.band_hi);
   // wave and the block states below are uniform across a wave; readfirstlane tells the compiler
   // so, which keeps the loop control and the buffer resources in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -1159,7 +1159,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   p.nkb = nkb;
   p.nkb2 = nkb2;
   const bool banded = a.band_pairs > 0;
-  p.splits = a.dkv_acc != nullptr && !banded ? bwd_splits(a.b, a.hkv, a.lq, a.lk, a.causal) : 1;
+  p.splits = a.dkv_acc != nullptr && !banded ? bwd_splits(a.b, a.hkv, a.lq, a.lk, a.causal) : 1;  // banded: per band below
   p.scale = a.scale;
   p.causal = a.causal;
   const int MK = a.rstart != nullptr ? kMaskRanges : a.mbits != nullptr ? kMaskBits : kMaskDense;
@@ -1175,6 +1175,10 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
     p.pb_lo = pb_lo;
     p.npairs = npairs;
     p.wg_pairs = (int)live_pairs(hi, a.lq, a.lk, a.causal);
+    // bands: the first band's dK/dV sums start at zero, so its pairs may split as the one pass's
+    // do (two partial sums onto zero, the same bits in either order); later bands add onto
+    // earlier sums and keep one workgroup per pair
+    if (banded) p.splits = (lo == 0 && a.causal && a.b * a.hkv * p.wg_pairs <= 256 && hi + 1 >= 8) ? 2 : 1;
     p.total_wg = (int)(a.b * a.hkv * p.wg_pairs * p.splits);
     const int64_t grid = p.total_wg + (a.dbias != nullptr ? a.b * a.hkv * (int64_t)(hi - lo + 1) : 0);
     if (grid == 0) return hipSuccess;

@@ -59,13 +59,15 @@ def ws_size(b, lq, lk, hq, hkv, d, causal):
         up(b * hq * npairs * 64 * 128 * 2) + up(b * hq * npairs * 2 * 8 * 8) + dkv
 
 
-def segments(KB, nqb, lq, lk, causal, splits):
-    """Query-block ranges [lo, hi] of the workgroups of key pair KB."""
+def segments(KB, nqb, lq, lk, causal, splits, band=None):
+    """Query-block ranges [lo, hi] of the workgroups of key pair KB, inside the launch's band."""
+    band_lo, band_hi = band if band is not None else (0, nqb - 1)
     if splits == 1:
-        return [(0, nqb - 1)]
+        return [(band_lo, band_hi)]
     lo = next(qb for qb in range(nqb + 1) if qb == nqb or KB < live_pairs(qb, lq, lk, causal))
-    upper = lo + (nqb - lo) // 2
-    return [(upper, nqb - 1), (lo, upper - 1)]
+    lo = max(lo, band_lo)
+    upper = lo + (band_hi + 1 - lo) // 2
+    return [(upper, band_hi), (lo, upper - 1)]
 
 
 def bands(nqb, lq, lk, causal, max_pairs):
@@ -96,7 +98,10 @@ def main_kernel_slots(state, b, hkv, G, lq, lk, causal, band=None, items=None):
     pb_lo = int(pair_base[lo_b])
     npairs = int(pair_base[hi_b + 1]) - pb_lo
     wg_pairs = live_pairs(hi_b, lq, lk, causal)  # the grid's pairs
-    splits = bwd_splits(b, hkv, lq, lk, causal) if band is None else 1
+    if band is None:
+        splits = bwd_splits(b, hkv, lq, lk, causal)
+    else:  # the first band may split its pairs (its fp32 sums start at zero), later bands do not
+        splits = 2 if lo_b == 0 and causal and b * hkv * wg_pairs <= 256 and hi_b + 1 >= 8 else 1
     hpi = 2 if G % 2 == 0 else 1
     slots = []
     for plane in range(b * hkv):
@@ -117,8 +122,7 @@ def main_kernel_slots(state, b, hkv, G, lq, lk, causal, band=None, items=None):
                             st[hf, j] = state[bb, g, qb, kb0 + hf]
                 return lo, st
 
-            for q_lo, q_hi in segments(KB, nqb, lq, lk, causal, splits):
-                q_lo, q_hi = max(q_lo, lo_b), min(q_hi, hi_b)
+            for q_lo, q_hi in segments(KB, nqb, lq, lk, causal, splits, (lo_b, hi_b)):
                 cache_lo = nqb  # each workgroup starts with an empty cache
                 qb = q_hi
                 while qb >= q_lo:
