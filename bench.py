@@ -291,8 +291,9 @@ def band_count(c, ws_bytes: int) -> int:
 
     fixed = up(2 * c.b * c.hq * c.lq * 4) + up((nqb + 1) * 8) + up(c.b * c.hkv * c.d * nkb2 * 128 * 2)
     total = sum(live(qb) for qb in range(nqb))
+    split = c.causal and c.b * c.hkv * nkb2 <= 256 and nqb >= 8
     if ws_bytes >= fixed + up(c.b * c.hq * total * 16384) + up(c.b * c.hq * total * 128) + \
-            (up(2 * c.b * c.lk * c.hkv * c.d * 4) if c.causal and c.b * c.hkv * nkb2 <= 256 and nqb >= 8 else 0):
+            (up(2 * c.b * c.lk * c.hkv * c.d * 4) if split else 0) + up(2 * c.b * c.hkv * nkb2 * (2 if split else 1) * 4):
         return 1
     fixed += up(2 * c.b * c.lk * c.hkv * c.d * 4)
     np_ = min(total, (ws_bytes - fixed) // (c.b * c.hq * 16512))

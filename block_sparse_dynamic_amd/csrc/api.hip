@@ -206,8 +206,10 @@ namespace {
 //   dsmap      u64  [b, hkv, np, G, 2, 8]          which 16-byte chunks of each slot are stored
 //   dkv        fp32 2 x [b, lk, hkv, d]            dK, dV sums of split key pairs or of a banded
 //                                                  backward (only then)
+//   order      int32 2 x [b * hkv * nkb2 * splits] the main kernel's workgroup order and the work
+//                                                  counts it is sorted by (one pass only)
 struct WsLayout {
-  size_t rows, pair_base, kt, ds, dsmap, dkv, total;
+  size_t rows, pair_base, kt, ds, dsmap, dkv, order, total;
   int64_t npairs;
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -217,8 +219,9 @@ int64_t all_live_pairs(int64_t lq, int64_t lk, int causal) {
   for (int64_t qb = 0, nqb = (lq + 63) / 64; qb < nqb; ++qb) np += dma::live_pairs(qb, lq, lk, causal);
   return np;
 }
-// Slots for np pairs per plane; the fp32 dK/dV sums when acc.
-WsLayout ws_layout_n(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int64_t np, bool acc) {
+// Slots for np pairs per plane; the fp32 dK/dV sums when acc; order_tasks entries of workgroup order.
+WsLayout ws_layout_n(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int64_t np, bool acc,
+                     int64_t order_tasks = 0) {
   WsLayout w = {};
   const int64_t nqb = (lq + 63) / 64, nkb2 = ((lk + 63) / 64 + 1) / 2;
   w.npairs = np;
@@ -228,13 +231,15 @@ WsLayout ws_layout_n(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv,
   w.ds = w.kt + up256((size_t)b * hkv * d * nkb2 * 128 * sizeof(uint16_t));
   w.dsmap = w.ds + up256((size_t)b * hq * np * 2 * 32 * 128 * sizeof(uint16_t));
   w.dkv = w.dsmap + up256((size_t)b * hq * np * 2 * 8 * sizeof(uint64_t));
-  w.total = w.dkv + up256(acc ? (size_t)2 * b * lk * hkv * d * sizeof(float) : 0);
+  w.order = w.dkv + up256(acc ? (size_t)2 * b * lk * hkv * d * sizeof(float) : 0);
+  w.total = w.order + up256((size_t)2 * order_tasks * sizeof(int32_t));
   return w;
 }
 // One pass over all query blocks (the fastest backward).
 WsLayout ws_layout(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int causal) {
-  return ws_layout_n(b, lq, lk, hq, hkv, d, all_live_pairs(lq, lk, causal),
-                     dma::bwd_splits(b, hkv, lq, lk, causal) > 1);
+  const int splits = dma::bwd_splits(b, hkv, lq, lk, causal);
+  const int64_t nkb2 = ((lk + 63) / 64 + 1) / 2;
+  return ws_layout_n(b, lq, lk, hq, hkv, d, all_live_pairs(lq, lk, causal), splits > 1, b * hkv * nkb2 * splits);
 }
 // Bands of single query blocks: the smallest workspace the backward runs in.
 WsLayout ws_layout_min(int64_t b, int64_t lq, int64_t lk, int64_t hq, int64_t hkv, int64_t d, int causal) {
@@ -320,6 +325,11 @@ int attn_bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   a.dsmap = reinterpret_cast<uint64_t*>(ws + wl.dsmap);
   a.npairs = wl.npairs;
   a.band_pairs = band_pairs;
+  if (band_pairs == 0) {  // one pass: the workgroup order and its counts, T entries each
+    const int64_t tasks = b * hkv * (((lk + 63) / 64 + 1) / 2) * dma::bwd_splits(b, hkv, lq, lk, is_causal);
+    a.order = reinterpret_cast<int32_t*>(ws + wl.order);
+    a.pair_counts = a.order + tasks;
+  }
   a.dkv_acc = (band_pairs > 0 || dma::bwd_splits(b, hkv, lq, lk, is_causal) > 1) ? reinterpret_cast<float*>(ws + wl.dkv)
                                                                                   : nullptr;
   a.b = b;

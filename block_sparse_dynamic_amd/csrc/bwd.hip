@@ -151,6 +151,124 @@ __global__ __launch_bounds__(1024) void pair_base_kernel(int64_t* __restrict__ p
   }
 }
 
+// Query blocks [q_lo, q_hi] that the workgroup of key pair KB and segment seg walks inside the
+// launch's range [band_lo, band_hi]: all of them, or (splits = 2) one half of the pair's live
+// blocks there (the first live one is the smallest qb with KB < live_pairs(qb), which only grows
+// with qb).  Shared by the main kernel and the count of each workgroup's work.
+__device__ inline void walk_range(int KB, int seg, int splits, int nqb, int64_t lq, int64_t lk, int causal,
+                                  int band_lo, int band_hi, int& q_lo, int& q_hi) {
+  q_lo = band_lo;
+  q_hi = band_hi;
+  if (splits > 1) {
+    int lo = 0, hi = nqb;  // first live query block, found by bisection
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (KB < live_pairs(mid, lq, lk, causal)) hi = mid;
+      else lo = mid + 1;
+    }
+    lo = max(lo, band_lo);
+    const int upper = lo + (band_hi + 1 - lo) / 2;  // segment 0: [upper, band_hi], segment 1: [lo, upper)
+    q_lo = seg == 0 ? upper : lo;
+    q_hi = seg == 0 ? band_hi : upper - 1;
+  }
+}
+
+// Work of each main-kernel workgroup of a one-pass backward: the query blocks its walk visits
+// (those where one of its pair's two key blocks is not SKIP and causality leaves the pair live),
+// written to counts[(plane * nkb2 + KB) * splits + seg].  One wave per (plane, pair): lanes take 64
+// query blocks at a time, a ballot and its population count per segment.
+__global__ __launch_bounds__(256) void pair_count_kernel(const uint8_t* __restrict__ state, int32_t* __restrict__ counts,
+                                                         int64_t planes, int nqb, int nkb, int nkb2, int splits,
+                                                         int64_t lq, int64_t lk, int causal) {
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wv >= planes * nkb2) return;  // whole waves
+  const int KB = (int)(wv % nkb2);
+  const int64_t plane = wv / nkb2;
+  int q_lo = 0, q_hi = nqb - 1;
+  if (splits > 1) walk_range(KB, 0, splits, nqb, lq, lk, causal, 0, nqb - 1, q_lo, q_hi);  // segment 0: [q_lo, nqb)
+  int n0 = 0, n1 = 0;
+  for (int base = 0; base < nqb; base += 64) {
+    const int qb = base + lane;
+    bool live = false;
+    if (qb < nqb && KB < live_pairs(qb, lq, lk, causal)) {
+      const uint8_t* row = state + (plane * nqb + qb) * nkb + 2 * KB;
+      live = row[0] != kSkip || (2 * KB + 1 < nkb && row[1] != kSkip);
+    }
+    const uint64_t b = __ballot(live);
+    const uint64_t upper = __ballot(live && qb >= q_lo);
+    n0 += __popcll(upper);
+    n1 += __popcll(b) - __popcll(upper);
+  }
+  if (lane == 0) {
+    counts[(plane * nkb2 + KB) * splits] = n0;
+    if (splits > 1) counts[(plane * nkb2 + KB) * splits + 1] = n1;
+  }
+}
+
+// The main kernel's workgroup order: order[w] = the task (plane * nkb2 + KB) * splits + seg that
+// workgroup w runs.  Workgroup w runs on XCD w % 8 as the w / 8-th of that XCD, and each CU holds
+// one main-kernel workgroup at a time.  Where every plane's work falls with the key pair (the
+// causal triangle with a uniform mask) the XCD-aware contiguous order (xcd_task) already pairs
+// long and short walks and keeps a plane's rows in one XCD's L2.  Otherwise (document masks and
+// other irregular ones) the tasks are sorted longest first and dealt to the XCDs in serpentine
+// order (ranks 8k .. 8k+7 to XCDs 0..7 for even k, 7..0 for odd k), so that each CU starts the
+// longest task left when it frees: a long walk no longer waits behind another on the same CU.
+// One workgroup; a bitonic sort of up to kMaxOrder tasks in LDS (more tasks keep xcd_task).
+constexpr int kMaxOrder = 16384;
+__global__ __launch_bounds__(1024) void pair_order_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
+                                                          int T, int planes, int nkb2, int splits) {
+  __shared__ uint32_t keys[kMaxOrder];
+  const int tid = threadIdx.x;
+  const int per_plane = nkb2 * splits;
+  // does each plane's work fall (weakly) with the pair?
+  int rising = 0;
+  for (int i = tid; i < T; i += 1024) {
+    const int KB = (i % per_plane) / splits, seg = i % splits;
+    if (seg == 0 && KB + 1 < nkb2) {
+      int a = 0, b = 0;
+      for (int s2 = 0; s2 < splits; ++s2) {
+        a += counts[i + s2];
+        b += counts[i + splits + s2];
+      }
+      rising |= b > a;
+    }
+  }
+  const bool irregular = __syncthreads_or(rising) != 0;
+  if (!irregular || T > kMaxOrder) {
+    for (int w = tid; w < T; w += 1024) order[w] = xcd_task(w, T, planes);
+    return;
+  }
+  int n2 = 1;
+  while (n2 < T) n2 *= 2;
+  // key: (most work first) then the task index; counts are at most 2^18 query blocks
+  for (int i = tid; i < n2; i += 1024)
+    keys[i] = i < T ? (((uint32_t)((1 << 18) - 1 - counts[i]) << 14) | (uint32_t)i) : 0xFFFFFFFFu;
+  __syncthreads();
+  for (int k = 2; k <= n2; k *= 2) {
+    for (int j = k / 2; j > 0; j /= 2) {
+      for (int i = tid; i < n2; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t x = keys[i], y = keys[l];
+          const bool up = (i & k) == 0;
+          if (up ? x > y : x < y) {
+            keys[i] = y;
+            keys[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = tid; r < T; r += 1024) {
+    const int k = r / 8, j = r % 8;
+    const bool full_group = 8 * k + 8 <= T;
+    const int x = (full_group && (k & 1)) ? 7 - j : j;  // a last, partial group keeps its order
+    order[8 * k + x] = (int32_t)(keys[r] & 0x3FFFu);
+  }
+}
+
 // ---------------------------------------------------------------------------
 struct BwdParams {
   const uint16_t* q;
@@ -173,6 +291,7 @@ struct BwdParams {
   uint16_t* dv;
   uint16_t* dbias;
   float* dkv_acc;  // fp32 dK, dV sums when the pairs are split (splits > 1) or the query blocks banded
+  const int32_t* order;  // workgroup w runs task order[w] (pair_order_kernel), or null: xcd_task
   int64_t lq, lk, hq, hkv;
   // This launch covers query blocks [band_lo, band_hi] (all of them unless the backward runs in
   // bands); the dS slots hold that range's pairs only, the first of which is pair_base[band_lo] = pb_lo.
@@ -343,28 +462,15 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   }
   const int w = blockIdx.x;
   const int per_plane = p.wg_pairs * p.splits;
-  const int t = xcd_task(w, p.total_wg, p.total_wg / per_plane);  // units: planes
+  const int t = p.order != nullptr ? p.order[w] : xcd_task(w, p.total_wg, p.total_wg / per_plane);  // units: planes
   // low key blocks (most query blocks under causality) first; a split pair's halves next to each other
   const int plane = t / per_plane, KB = (t % per_plane) / p.splits, seg = (t % per_plane) % p.splits;
   const int kb0 = 2 * KB;
   const bool has_kb1 = kb0 + 1 < p.nkb;
   const int64_t bidx = plane / p.hkv, g = plane % p.hkv;
-  // Query blocks this workgroup walks, [q_lo, q_hi]: all those of the launch's range, or one half
-  // of the pair's live blocks in it (the first live one is the smallest qb with KB < live_pairs(qb),
-  // which only grows with qb)
-  int q_lo = p.band_lo, q_hi = p.band_hi;
-  if (p.splits > 1) {
-    int lo = 0, hi = p.nqb;  // first live query block, found by bisection
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2;
-      if (KB < live_pairs(mid, p.lq, p.lk, p.causal)) hi = mid;
-      else lo = mid + 1;
-    }
-    lo = max(lo, p.band_lo);
-    const int upper = lo + (p.band_hi + 1 - lo) / 2;  // segment 0: [upper, band_hi], segment 1: [lo, upper)
-    q_lo = seg == 0 ? upper : lo;
-    q_hi = seg == 0 ? p.band_hi : upper - 1;
-  }
+  // query blocks this workgroup walks
+  int q_lo, q_hi;
+  walk_range(KB, seg, p.splits, p.nqb, p.lq, p.lk, p.causal, p.band_lo, p.band_hi, q_lo, q_hi);
   // wave and the block states below are uniform across a wave; readfirstlane tells the compiler
   // so, which keeps the loop control and the buffer resources in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -1126,6 +1232,15 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
       const int64_t n4 = 2 * a.b * a.lk * a.hkv * a.d / 4;
       hipLaunchKernelGGL(dkv_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a.dkv_acc, n4);
     }
+    if (a.order != nullptr) {  // one pass: the main kernel's workgroup order from the bitmap
+      const int splits = a.dkv_acc != nullptr ? bwd_splits(a.b, a.hkv, a.lq, a.lk, a.causal) : 1;
+      const int64_t T = a.b * a.hkv * nkb2 * splits;
+      const int64_t waves = a.b * a.hkv * nkb2;  // one per (plane, pair)
+      hipLaunchKernelGGL(pair_count_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a.state,
+                         a.pair_counts, a.b * a.hkv, nqb, nkb, nkb2, splits, a.lq, a.lk, a.causal);
+      hipLaunchKernelGGL(pair_order_kernel, dim3(1), dim3(1024), 0, stream, a.pair_counts, a.order, (int)T,
+                         (int)(a.b * a.hkv), nkb2, splits);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1150,6 +1265,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream, int parts) {
   p.dv = a.dv;
   p.dbias = a.dbias;
   p.dkv_acc = a.dkv_acc;
+  p.order = a.band_pairs > 0 ? nullptr : a.order;
   p.lq = a.lq;
   p.lk = a.lk;
   p.hq = a.hq;

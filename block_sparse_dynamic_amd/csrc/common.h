@@ -210,6 +210,8 @@ struct AttnArgs {
   int64_t npairs;     // live key-block pairs of one plane (pair_base[nqb])
   float* dkv_acc;     // fp32 [2][b, lk, hkv, d]: dK, dV sums of split pairs (bwd_splits > 1) or of
                       // a backward in bands, else null
+  int32_t* order;       // one-pass backward: main-kernel workgroup order [b * hkv * nkb2 * splits]
+  int32_t* pair_counts; // its work counts, same size (null with bands)
   int64_t band_pairs; // backward in bands of query blocks whose live pairs fit this many dS slot
                       // pairs per plane (bwd_band_end); 0: one pass over all query blocks
   int64_t b, lq, lk, hq, hkv, d;

@@ -168,13 +168,15 @@ def test_workspace_size(lib, b, lq, lk, hq, hkv, d, causal):
     # regions: row terms (2 fp32 per row), pair offsets (int64), K^T (bf16, keys padded to 128), dS tile
     # slots (bf16, 64 x 128 per live pair and query head), their chunk masks (8 u64 per 32-row half of a
     # slot), and when the backward splits its key pairs (causal, at most 256 of them over all planes,
-    # at least 8 query blocks) fp32 dK and dV sums; each rounded up to 256 bytes
+    # at least 8 query blocks) fp32 dK and dV sums, then the main kernel's workgroup order and its
+    # work counts (an int32 per workgroup each); each rounded up to 256 bytes
     up = lambda x: (x + 255) // 256 * 256
     nqb, nkb2 = (lq + 63) // 64, ((lk + 63) // 64 + 1) // 2
     npairs = sum(live_pairs(qb, lq, lk, causal) for qb in range(nqb))
     split = causal and b * hkv * nkb2 <= 256 and nqb >= 8
+    tasks = b * hkv * nkb2 * (2 if split else 1)
     want = up(2 * b * hq * lq * 4) + up((nqb + 1) * 8) + up(b * hkv * d * nkb2 * 128 * 2) + up(b * hq * npairs * 64 * 128 * 2) \
-        + up(b * hq * npairs * 2 * 8 * 8) + (up(2 * b * lk * hkv * d * 4) if split else 0)
+        + up(b * hq * npairs * 2 * 8 * 8) + (up(2 * b * lk * hkv * d * 4) if split else 0) + up(2 * tasks * 4)
     assert lib.dma_attn_bwd_workspace_size(b, lq, lk, hq, hkv, d, causal) == want
 
 

@@ -54,9 +54,11 @@ def ws_size(b, lq, lk, hq, hkv, d, causal):
     up = lambda x: (x + 255) // 256 * 256
     nqb, nkb2 = (lq + 63) // 64, ((lk + 63) // 64 + 1) // 2
     npairs = sum(live_pairs(qb, lq, lk, causal) for qb in range(nqb))
-    dkv = up(2 * b * lk * hkv * d * 4) if bwd_splits(b, hkv, lq, lk, causal) > 1 else 0
+    splits = bwd_splits(b, hkv, lq, lk, causal)
+    dkv = up(2 * b * lk * hkv * d * 4) if splits > 1 else 0
+    order = up(2 * b * hkv * nkb2 * splits * 4)  # the main kernel's workgroup order and work counts
     return up(2 * b * hq * lq * 4) + up((nqb + 1) * 8) + up(b * hkv * d * nkb2 * 128 * 2) + \
-        up(b * hq * npairs * 64 * 128 * 2) + up(b * hq * npairs * 2 * 8 * 8) + dkv
+        up(b * hq * npairs * 64 * 128 * 2) + up(b * hq * npairs * 2 * 8 * 8) + dkv + order
 
 
 def segments(KB, nqb, lq, lk, causal, splits, band=None):
