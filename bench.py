@@ -83,8 +83,10 @@ def parse():
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "headline_traffic.json")
 KERNEL_SOURCES = ["classify.hip", "fwd.hip", "bwd.hip", "common.h"]
 # kernels of each measured unit, matched by substring of the demangled name
-CALL_KERNELS = {"fwd": ["fwd_kernel"], "bwd_main": ["bwd_main_kernel"], "bwd_dq": ["dq_kernel"],
-                "bwd_prepare": ["bwd_pre_kernel", "kt_kernel", "pair_base_kernel"], "classify": ["classify_kernel"]}
+CALL_KERNELS = {"fwd": ["fwd_kernel"], "bwd_main": ["bwd_main_kernel", "dkv_finalize_kernel"], "bwd_dq": ["dq_kernel"],
+                "bwd_prepare": ["bwd_pre_kernel", "kt_kernel", "pair_base_kernel", "pair_count_kernel",
+                                "pair_order_kernel", "dkv_zero_kernel"],
+                "classify": ["classify_kernel"]}
 
 
 def kernel_source_hash() -> str:

@@ -7,10 +7,11 @@ slots: every output against the fp64 oracle (whole tensors, the tolerances of gp
 and dBias equal to the one-pass backward's bit for bit (the same items, the same sums); dK and dV
 through the oracle (they differ from the one pass by the fp32 rounding of the band sums); two
 runs bit-identical.  Cases: causal and not, ragged sizes, lq > lk (leading query blocks without a
-live pair, whose bands launch only dBias zero-fill), head dims 64 and 128, group sizes 1..8, the
-dense, bit-packed and column-range mask inputs.  At full size the Long workload (b=1, L=65536,
-Hq=8, Hkv=1, d=128, top-k 2048) runs in a workspace of one mask plane (b*hkv*L*L bf16, a quarter
-of its one-pass workspace) and is checked on sampled query blocks.
+live pair, whose bands launch only dBias zero-fill), head dims 64 and 128, group sizes 1..8, no
+mask and no bias, no dBias output, the dense, bit-packed and column-range mask inputs.  At full
+size the Long workload (b=1, L=65536, Hq=8, Hkv=1, d=128, top-k 2048) runs in a workspace of one
+mask plane (b*hkv*L*L bf16, a quarter of its one-pass workspace) and is checked on sampled query
+blocks.
 """
 import numpy as np
 import pytest
@@ -28,6 +29,7 @@ CASES = [
     Case("bands_lq_gt_lk", 73, 1, 456, 200, 4, 1, 128, True, "topk", 40),
     Case("bands_doc_g8", 74, 1, 1000, 1000, 8, 1, 64, True, "doc", doc_min=64, doc_max=300, bias_std=0.5,
          fill="lowest"),
+    Case("bands_no_mask_no_bias", 76, 1, 328, 328, 4, 2, 64, True, "none", bias=False),
 ]
 
 
@@ -72,6 +74,26 @@ def test_banded_backward(c, which):
     assert np.array_equal(first[3], one[3]), "dBias differs from the one-pass backward"
     H.compare_with_oracle(f"{c.name} (bands, {which})", c, dc.q_h, dc.k_h, dc.v_h, dc.mask_h, dc.bias_h, dc.do_h,
                           dc.o, dc.lse, dc.dq, dc.dk, dc.dv, dc.dbias)
+
+
+def test_banded_backward_without_dbias():
+    """No dBias output: the bands still give the one-pass dQ bit for bit and dK, dV against the oracle."""
+    import gpu_harness as H
+
+    c = CASES[0]
+    ws = workspace_bytes(c, "min")
+    print(f"case {c} workspace {ws} bytes (min), no dBias", flush=True)
+    dc = H.DeviceCase(c)
+    dc.classify()
+    dc.forward()
+    dc.backward(want_dbias=False)
+    torch.cuda.synchronize()
+    one_dq = H.bits(dc.dq)
+    dc.backward(want_dbias=False, ws_bytes=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.bits(dc.dq), one_dq), "dQ differs from the one-pass backward"
+    H.compare_with_oracle(f"{c.name} (bands, no dBias)", c, dc.q_h, dc.k_h, dc.v_h, dc.mask_h, dc.bias_h, dc.do_h,
+                          dc.o, dc.lse, dc.dq, dc.dk, dc.dv, None)
 
 
 def test_banded_bits_and_ranges_backward():
