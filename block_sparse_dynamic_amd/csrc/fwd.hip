@@ -580,6 +580,9 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
     }
     prev_ok = compute;
     // ---- stage the next block's K, bias and V; load the one after -----------------------------
+    // (range input: the next block's column ranges were written after this iteration's barrier by
+    // the first wave; one more barrier orders them before the staging reads them)
+    if constexpr (MK == kMaskRanges) lds_barrier();
     if (kbn < p.nkb) {
       const int vnext = vcur == 2 ? 0 : vcur + 1;  // the buffer of the block two back, read by no one now
       stage_kb(buf ^ 1, kbn, stn);
