@@ -95,11 +95,11 @@ int dma_block_classify(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq,
  *
  *   q           bf16 [b, lq, hq, d]
  *   k, v        bf16 [b, lk, hkv, d]; v enters the P V product in fp16,
- *               scaled by a power of two per group of 8 keys so that the
- *               group's largest magnitude lands in [2^14, 2^15): every finite
- *               bf16 value within 2^29 of its group's largest is taken exactly
- *               (smaller ones move by at most 2^-39 of it); the weights P enter
- *               in fp16 too (relative rounding 2^-11)
+ *               scaled by a power of two (a multiple of 8) per group of 8 keys
+ *               so that the group's largest magnitude lands in [2^7, 2^15):
+ *               every finite bf16 value within 2^22 of its group's largest is
+ *               taken exactly (smaller ones move by at most 2^-32 of it); the
+ *               weights P enter in fp16 too (relative rounding 2^-11)
  *   mask, bias  bf16 [b, hkv, lq, lk]; either may be NULL (no mask: every key
  *               attends; no bias: zero).  bias entries at masked positions
  *               are never read into the result (they may hold NaN or inf).
