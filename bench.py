@@ -28,10 +28,11 @@ Beside it:
   as a fraction of the bound that applies (bf16 MFMA, or HBM for the document
   workload);
 * ``measured_peaks``: a 4 GiB device copy's read + write bandwidth beside the
-  spec HBM peak;
+  spec HBM peak, and a bf16 8192^3 library GEMM's rate beside the spec MFMA peak;
 * ``cpu_baseline``: the fp64 oracle on sampled query blocks of the workload;
 * ``next_rows`` (unless --no-next): GPU top-k mask construction, the step with the
-  bit-packed PARTIAL-block mask, the other classification path.
+  bit-packed PARTIAL-block mask, and (with the Long workload measured) the
+  backward in bands of query blocks at three workspace sizes.
 """
 from __future__ import annotations
 
@@ -457,6 +458,25 @@ def measured_copy_gbs(torch, mib=4096):
     return round(2.0 * mib * (1 << 20) / (ms * 1e-3) / 1e9, 1)
 
 
+def measured_gemm_tflops(torch, n=8192):
+    """bf16 n x n x n products through the vendor BLAS (torch.matmul): the matrix-core rate a plain
+    library GEMM reaches on this device, beside the dense bf16 spec peak."""
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del a, b, c
+    torch.cuda.empty_cache()
+    return round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+
+
 def summarize_counters(counter_dir: str, out_md: str):
     """Per-kernel SQ counters (mean over dispatches, summed over the GPU) and derived ratios."""
     import csv
@@ -621,6 +641,7 @@ def main():
             line["next_rows"]["topk_mask"] = time_topk(c, dma, torch, st.stream)
     if args.calibrate_copy_mib == 0:
         line["measured_peaks"] = {"hbm_copy_gbs": measured_copy_gbs(torch), "hbm_spec_gbs": PEAK_HBM_GBS,
+                                  "bf16_gemm_tflops": measured_gemm_tflops(torch),
                                   "mfma_bf16_spec_tflops": PEAK_BF16_TFLOPS}
     head_method = None
     if not args.no_workloads and args.calibrate_copy_mib == 0:
