@@ -127,24 +127,23 @@ __global__ __launch_bounds__(256) void kt_kernel(const uint16_t* __restrict__ k,
 // plane); pair_base[nqb] = all of them.  One workgroup.
 __global__ __launch_bounds__(1024) void pair_base_kernel(int64_t* __restrict__ pair_base, int64_t nqb, int64_t lq,
                                                          int64_t lk, int causal) {
-  __shared__ int64_t part[1024];
+  __shared__ int64_t wave_sum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t per = (nqb + 1023) / 1024;
-  const int64_t lo = min(nqb, (int64_t)threadIdx.x * per), hi = min(nqb, lo + per);
+  const int64_t lo = min(nqb, (int64_t)tid * per), hi = min(nqb, lo + per);
   int64_t sum = 0;
   for (int64_t qb = lo; qb < hi; ++qb) sum += live_pairs(qb, lq, lk, causal);
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int64_t x = part[i];
-      part[i] = run;
-      run += x;
-    }
-    pair_base[nqb] = run;
+  // exclusive scan of the 1024 thread sums: inside each wave, then over the 16 wave totals
+  int64_t incl = sum;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
   }
+  if (lane == 63) wave_sum[wave] = incl;
   __syncthreads();
-  int64_t run = part[threadIdx.x];
+  int64_t run = incl - sum;
+  for (int w2 = 0; w2 < wave; ++w2) run += wave_sum[w2];
+  if (tid == 1023) pair_base[nqb] = run + sum;
   for (int64_t qb = lo; qb < hi; ++qb) {
     pair_base[qb] = run;
     run += live_pairs(qb, lq, lk, causal);

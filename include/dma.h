@@ -348,7 +348,7 @@ int dma_attn_bwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
  * taken for the pages' unsorted top-k), so the result is fully determined.
  * Errors: DMA_ERR_INVALID_ARGUMENT (NULL or misaligned pointers, rows, lk or
  * k < 1, lk % 8 != 0, mask_out aliasing an input), DMA_ERR_UNSUPPORTED
- * (lk > 65536: a row is held in LDS; rows > 2^31 - 1).
+ * (lk > 65536: a row is held in the registers of one workgroup; rows > 2^31 - 1).
  */
 int dma_topk_mask(const uint16_t* bias, int64_t rows, int64_t lk, int64_t k, uint16_t* mask_out, uint16_t* bias_out,
                   void* stream);

@@ -78,6 +78,41 @@ def test_special_values(lk, k):
     check(bits, k)
 
 
+# (k-th value, fill below it, fill above it): rows whose k-th largest value is each kind of number
+THRESHOLDS = [
+    (0x0000, 0x8001, 0x0001),  # +0, tied with -0; subnormals on both sides
+    (0x0001, 0x8000, 0x0002),  # the smallest subnormal
+    (0x0080, 0x007F, 0x0081),  # the smallest normal, beside the largest subnormal
+    (0x8080, 0x8081, 0x807F),  # the negative of it
+    (0x7F80, 0x7F7F, 0x7F80),  # +inf
+    (0xFF80, 0x7FC0, 0xFF7F),  # -inf, NaN below it
+    (0xFF7F, 0xFF80, 0xFF7E),  # the smallest bf16
+    (0x7FC0, 0xFFC1, 0x3F80),  # NaN: fewer numbers than k
+    (0xBF80, 0xC000, 0x3F80),  # -1
+]
+
+
+@pytest.mark.parametrize("t,lo,hi", THRESHOLDS, ids=[f"{t:04x}" for t, _, _ in THRESHOLDS])
+@pytest.mark.parametrize("lk,k", [(1000, 301), (4104, 1003), (16384, 5003)])
+def test_threshold_values(t, lo, hi, lk, k):
+    """The k-th value is t and several keys hold it (the kept ties cut inside a 16-byte chunk, and
+    at 16384 keys in a later row of 256 chunks), with values below and above it scattered."""
+    rng = np.random.default_rng(5000 + lk + t)
+    n = 8
+    bits = np.empty((n, lk), np.uint16)
+    for i in range(n):
+        n_hi = k - 1 - i * 37 % 200  # keys above t
+        n_eq = 1 + (i * 997 + 3 * k) % (lk - n_hi - 1)  # keys equal to t, at least k - n_hi
+        n_eq = max(n_eq, k - n_hi)
+        row = np.full(lk, lo, np.uint16)
+        row[:n_hi] = hi
+        row[n_hi:n_hi + n_eq] = t
+        if t == 0x0000:
+            row[n_hi:n_hi + n_eq:2] = 0x8000  # -0 and +0 tie
+        bits[i] = rng.permutation(row)
+    check(bits, k)
+
+
 def test_in_place():
     rng = np.random.default_rng(3000)
     check(rows_with_ties(rng, 16, 2048), 300, in_place=True)
