@@ -267,15 +267,23 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       *reinterpret_cast<u32x4*>(&sm.k[buf][tile_off<D>(kr[n], kc[n] * 8)]) = pk[n];  // rows past lk are zeros
     const bool full = (st == kFull);
     bool any_v = false, all_v = true;  // fused classification: this thread's positions of the block
+    // a block inside the matrix whose every key is causal for its first row: no position is cut
+    // by the ragged edge or by causality (uniform across the workgroup)
+    const int64_t kend = (int64_t)kb * kBlock + kBlock;
+    const bool inner = q_rows == kBlock && kend <= p.lk && (!p.causal || kend - 1 <= (int64_t)qb * kBlock + shift);
+    auto stage_bias = [&](auto inner_c) {
 #pragma unroll
     for (int n = 0; n < BN; ++n) {
       const int task = tid + n * NT;
       const int r = task >> 3, c = task & 7;
       const int64_t i = (int64_t)qb * kBlock + r, j0 = (int64_t)kb * kBlock + c * 8;
       // columns j0 + e of this chunk are inside the matrix and causal for e <= emax
-      int64_t lim = p.lk - 1 - j0;
-      if (p.causal) lim = min(lim, i + shift - j0);
-      const int emax = (i < p.lq) ? (int)max((int64_t)-1, min(lim, (int64_t)7)) : -1;
+      int emax = 7;
+      if constexpr (!decltype(inner_c)::value) {
+        int64_t lim = p.lk - 1 - j0;
+        if (p.causal) lim = min(lim, i + shift - j0);
+        emax = (i < p.lq) ? (int)max((int64_t)-1, min(lim, (int64_t)7)) : -1;
+      }
       const u32x4 bw = pb[n];  // zeros without a bias
       u32x4 mw = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
       if (!full) {
@@ -322,6 +330,9 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
       *reinterpret_cast<f32x4*>(&sm.b[buf][r * BR + c * 8]) = y0;
       *reinterpret_cast<f32x4*>(&sm.b[buf][r * BR + c * 8 + 4]) = y1;
     }
+    };
+    if (inner) stage_bias(std::true_type{});
+    else stage_bias(std::false_type{});
     if constexpr (kCls) {
       // the block is SKIP without a valid position, FULL when all 4096 are valid (rows past lq
       // and keys past lk count as invalid), PARTIAL otherwise; every thread holds 8 positions
@@ -529,9 +540,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) {
           const float pw = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], as_l2e, -mb));
           sacc[kt][i] = pw;
-          rs += pw;
         }
-      l_part += rs;
       // the block's V exponents (uniform): the reference moves up to the largest, the output
       // accumulators follow exactly; then the weights in units of 2^e_ref.  A lane's 8 weights
       // of k-step (kt, hh) are keys kt*32 + hh*16 + 4 hi + {0..3} (group kt*4 + hh*2) and
@@ -560,9 +569,18 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              pf[kt][hh][e] = pack_f16x2(sacc[kt][hh * 8 + 2 * e], sacc[kt][hh * 8 + 2 * e + 1]);
+            for (int e = 0; e < 4; ++e) {
+              // the row sum takes the fp16 weights the P V products take, two per dot instruction
+              // (from the pair as built: a bit cast of an element of pf compiled to element 0)
+              const f16x2 h = {(_Float16)sacc[kt][hh * 8 + 2 * e], (_Float16)sacc[kt][hh * 8 + 2 * e + 1]};
+              pf[kt][hh][e] = __builtin_bit_cast(uint32_t, h);
+              rs = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.f, (_Float16)1.f}, rs, false);
+            }
       } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) rs += sacc[kt][i];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -576,6 +594,7 @@ __global__ __launch_bounds__(HC * 128) void fwd_kernel(FwdParams p) {
           }
         }
       }
+      l_part += rs;
       if (!defer) pv_products(vcur);
     }
     prev_ok = compute;
