@@ -20,7 +20,7 @@ Beside it:
 * ``roofline`` for the dominant kernel, the backward main kernel: its algorithmic
   FLOPs (S, dP, dV, dK products: 8*d per block element per query head) over its
   mean duration from HIP events around it in the K timed steps;
-* ``method``: the measurement of every workload by the survey's method: 2 warm-up
+* ``method``: every workload measured the same way, with cold caches: 2 warm-up
   iterations, then 10 timed ones, each preceded by an untimed 512 MiB write (larger
   than the last-level caches, so mask and bias come from HBM), with HIP events
   around every call; the mean of the first 3 and the median of 10 per phase,
@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload method measurements")
     ap.add_argument("--workloads", default="mid,headline,docpacked,long",
-                    help="workloads measured by the survey's method (comma separated)")
+                    help="workloads measured in the method block, caches flushed before each call (comma separated)")
     ap.add_argument("--cpu-blocks", type=int, default=16, help="query-row blocks the oracle times")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps, so that a hardware counter "
@@ -241,7 +241,7 @@ class Step:
 
 
 def method_measure(st, np, torch, flush, n_warm=2, n_iter=10, bound="mfma"):
-    """The survey's method: warm-ups, then n_iter iterations each after an untimed flush write;
+    """Cold-cache measurement: warm-ups, then n_iter iterations each after an untimed flush write;
     per phase the mean of the first 3 and the median of all, and rates against the bound."""
     c = st.c
     for _ in range(n_warm):
