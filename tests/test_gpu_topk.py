@@ -2,8 +2,9 @@
 
 Rows mix heavy ties at the k-th value (values drawn from a few bf16 numbers), the special
 values (+-0, +-inf, NaN with several payloads, the smallest bf16, subnormals), k = 1, k = lk - 1,
-k >= lk, lengths that are not a multiple of the workgroup width, in-place output, and N(0,1)
-rows at the sizes of the pages' workloads (L = 16384, k = 1024; L = 65536, k = 2048).
+k >= lk, lengths that are not a multiple of the workgroup width, every register layout of a row
+(1 to 32 chunks per thread), in-place output, rows whose k-th value is each kind of number, and
+N(0,1) rows at the sizes of the pages' workloads (L = 16384, k = 1024; L = 65536, k = 2048).
 """
 import numpy as np
 import pytest
@@ -110,6 +111,17 @@ def test_threshold_values(t, lo, hi, lk, k):
         if t == 0x0000:
             row[n_hi:n_hi + n_eq:2] = 0x8000  # -0 and +0 tie
         bits[i] = rng.permutation(row)
+    check(bits, k)
+
+
+@pytest.mark.parametrize("lk,k", [(24584, 20001), (40000, 7), (65528, 65000)])
+def test_long_rows_with_ties(lk, k):
+    """Rows of 16 and 32 chunks per thread with a partial last row of chunks: heavy ties and special
+    values, the kept ties cut early in the row (k = 7) and in its last chunk row."""
+    rng = np.random.default_rng(6000 + lk)
+    bits = rows_with_ties(rng, 4, lk)
+    pos = rng.random(bits.shape) < 0.05
+    bits[pos] = rng.choice(SPECIAL, size=int(pos.sum()))
     check(bits, k)
 
 
