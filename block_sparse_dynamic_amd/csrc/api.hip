@@ -375,6 +375,9 @@ int dma_attn_bwd_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       float scale, int is_causal, uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbias,
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!mask_bits || !aligned16(mask_bits)) return DMA_ERR_INVALID_ARGUMENT;
+  // the main kernel addresses one plane's bits through a single buffer range
+  if (lq > 0 && lk > 0 && ((lq + dma::kBlock - 1) / dma::kBlock) * ((lk + dma::kBlock - 1) / dma::kBlock) * 512 > (int64_t)1 << 31)
+    return DMA_ERR_UNSUPPORTED;
   return attn_bwd_impl(q, k, v, nullptr, nullptr, nullptr, mask_bits, bias, block_state, o, dout, lse, b, lq, lk, hq,
                        hkv, d, scale, is_causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream, false,
                        dma::kBwdAll, /*allow_bands=*/true);

@@ -597,6 +597,12 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
   const uint16_t* mask_plane = p.mask + plane_off + (int64_t)kb0 * kBlock;
   const uint32_t qrow_bytes = (uint32_t)(p.hq * D * 2);
   const uint32_t krange = (uint32_t)min((int64_t)kKeys, p.lk - (int64_t)kb0 * kBlock) * 2u;
+  // bit input: this plane's bits from the workgroup's first key block on (at most 2^31 bytes: the
+  // host checks nqb * nkb * 512 per plane)
+  u32x4 mb_rsrc = {0u, 0u, 0u, 0u};
+  if constexpr (MK == kMaskBits)
+    mb_rsrc = rsrc_words(p.mbits + ((int64_t)plane * p.nqb * p.nkb + kb0) * kBitsPerBlock,
+                         (uint32_t)(((int64_t)p.nqb * p.nkb - kb0) * kBitsPerBlock));
 
   // LDS byte addresses of the load destinations (buffer B of a tile is B tiles above buffer 0):
   // plain integers, so no generic-to-LDS pointer conversion is redone on every item
@@ -632,12 +638,12 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdParams p) {
       if constexpr (MK == kMaskBits) {
         // rows rh*32 .. +31 of a PARTIAL key block are 256 contiguous bytes of its bits: wave
         // 4 + hf fetches those of block hf, one dword per lane, to bytes hf*256 .. of the tile
+        // (one buffer range over the plane's bits, set up once; the item picks its bytes by offset)
         const int hf = wave - 4;
         if (hf >= 0 && hf < 2 && (hf ? s1 : s0) == kPartial) {
-          const uint8_t* src =
-              p.mbits + (((int64_t)plane * p.nqb + qb) * p.nkb + kb0 + hf) * kBitsPerBlock + rh * (kRows * 8);
-          dma_x1(rsrc_words(src, kRows * 8), lds_m + (uint32_t)B * kBTileBytes + (uint32_t)hf * 256u,
-                 (uint32_t)lane * 4u);
+          const uint32_t off = ((uint32_t)qb * (uint32_t)p.nkb + (uint32_t)hf) * (uint32_t)kBitsPerBlock +
+                               (uint32_t)(rh * (kRows * 8)) + (uint32_t)lane * 4u;
+          dma_x1(mb_rsrc, lds_m + (uint32_t)B * kBTileBytes + (uint32_t)hf * 256u, off);
         }
       }
     }

@@ -316,7 +316,9 @@ int dma_attn_bwd_ranges(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * points take mask, with the block_state written together with those bits (the
  * bits of any other PARTIAL block are undefined).  Other arguments, layouts,
  * workspace and errors are those of dma_attn_fwd / dma_attn_bwd (NULL or
- * misaligned mask_bits: DMA_ERR_INVALID_ARGUMENT).
+ * misaligned mask_bits: DMA_ERR_INVALID_ARGUMENT; dma_attn_bwd_bits also
+ * returns DMA_ERR_UNSUPPORTED when one plane's bits, nqb * nkb * 512 bytes,
+ * exceed 2^31, i.e. above lq * lk = 2^34, L = 131072).
  */
 size_t dma_mask_bits_size(int64_t b, int64_t hkv, int64_t lq, int64_t lk);
 int dma_block_classify_bits(const uint16_t* mask, int64_t b, int64_t hkv, int64_t lq, int64_t lk, int is_causal,

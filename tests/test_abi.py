@@ -273,6 +273,8 @@ def test_bits_reject(lib):
     assert g(*bargs[:3], None, *bargs[4:]) == INVALID
     assert g(*bargs[:14], 80, *bargs[15:]) == UNSUPPORTED
     assert g(*bargs[:15], 0.0, *bargs[16:]) == INVALID
+    big = 131072 + 64  # one plane's bits past 2^31 bytes
+    assert g(*bargs[:10], big, big, *bargs[12:]) == UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw", [dict(lk=(1 << 24) + 64), dict(lq=(1 << 24) + 64)])
