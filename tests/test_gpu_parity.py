@@ -42,6 +42,11 @@ SMALL = [
     # over two workgroups that add their dK, dV in fp32 (ragged rows and keys)
     Case("split_pairs", 25, 1, 600, 600, 8, 2, 128, True, "blocks"),
     Case("split_pairs_d64_g1", 26, 2, 520, 544, 2, 2, 64, True, "topk", 96),
+    # the smallest shapes: one query row over one 8-key chunk, a few decode-like rows over a ragged
+    # key range, and one whole 64x64 block
+    Case("one_row_one_chunk", 27, 1, 1, 8, 2, 1, 64, True, "ones"),
+    Case("few_rows_ragged_keys", 28, 2, 3, 520, 4, 2, 128, True, "topk", 40),
+    Case("single_block", 29, 1, 64, 64, 4, 4, 128, False, "blocks"),
 ]
 
 
