@@ -3,7 +3,8 @@
 Mid is checked whole (its 64 query blocks are all sampled); Headline, Doc-packed and
 Long on 64 seeded 64-row query blocks, with the whole block bitmap bit-exact.  The head
 dimension 64 kernels, which no workload uses, run once at a comparable size (b=2, L=8192,
-Hq=16, Hkv=2, d=64, causal top-k 512, and a non-causal ragged one).
+Hq=16, Hkv=2, d=64, causal top-k 512, and a non-causal ragged one), and so do group sizes 16
+and 1 (L=4096).
 """
 from synth import Case
 import pytest
@@ -43,8 +44,10 @@ def test_headline_fused_classify_sampled_parity():
 @pytest.mark.parametrize("c", [
     Case("d64_large_topk", 90, 2, 8192, 8192, 16, 2, 64, True, "topk", 512),
     Case("d64_large_blocks_noncausal", 91, 1, 4130, 3000, 8, 4, 64, False, "blocks"),
-], ids=["d64_topk_causal", "d64_blocks_noncausal_ragged"])
-def test_d64_at_scale(c):
+    Case("g16_scale", 92, 1, 4096, 4096, 32, 2, 128, True, "topk", 256),
+    Case("g1_scale", 93, 1, 4096, 4096, 8, 8, 128, True, "topk", 256),
+], ids=["d64_topk_causal", "d64_blocks_noncausal_ragged", "g16_topk_causal", "g1_topk_causal"])
+def test_other_shapes_at_scale(c):
     import gpu_harness as H
 
     print(f"case {c}", flush=True)
